@@ -1,0 +1,240 @@
+"""Parity of the HIP path (called through the C ABI) with the fp64 oracle.
+
+Acceptance: max |x - ref| / max |ref| per output tensor (o and the final
+state) within 1e-4 for fp32 q/k/v and 2e-2 for bf16 q/k/v (fp32 state).
+Small cases compare every element; the named full-size workloads compare
+every output of sampled (b, h) pairs, which the oracle computes head by head.
+"""
+import numpy as np
+import pytest
+
+from _gpu import TOL, compare_heads, dev, io_dtype, oracle_heads, random_state, run_gpu
+from oracle import seq
+from oracle.errors import max_rel_err
+from synth.gen import WORKLOADS, Workload, generate, generate_decode
+
+pytestmark = pytest.mark.gpu
+
+
+def _wl(io="bf16", decay="diag", dk=64, B=2, H=3, T=200, chunk=64, content=False, seed=21):
+    return Workload("case", B, H, T, dk, dk, chunk, io, decay, content, seed,
+                    decay_scale=0.1 if decay == "diag" else 0.05)
+
+
+# ------------------------------------------------------------ named workloads
+def test_tiny_full():
+    """Oracle-check workload (B=1, H=1, T=256, d=32, L=16, fp32), every output."""
+    x = generate(WORKLOADS["tiny"])
+    o, S = run_gpu(x)
+    compare_heads(o, S, oracle_heads(x), TOL["f32"], "tiny")
+
+
+def test_small_full():
+    """Small layer (B=4, H=8, T=2048, d=64, L=64, bf16), every output."""
+    x = generate(WORKLOADS["small"])
+    o, S = run_gpu(x)
+    compare_heads(o, S, oracle_heads(x), TOL["bf16"], "small")
+
+
+def test_layer_sampled():
+    """1.3B-scale mixer layer (B=8, H=16, T=4096, d=128, L=64, bf16): full-size run,
+    every output of sampled heads (corners and interior, both value tiles)."""
+    x = generate(WORKLOADS["layer"])
+    o, S = run_gpu(x)
+    assert np.all(np.isfinite(o)) and np.all(np.isfinite(S))
+    heads = [(0, 0), (3, 7), (5, 10), (7, 15)]
+    compare_heads(o, S, oracle_heads(x, heads), TOL["bf16"], "layer")
+
+
+def test_rot_sampled():
+    """Rotation variant (B=4, H=16, T=8192, d=128, L=64, bf16): sampled heads."""
+    x = generate(WORKLOADS["rot"])
+    o, S = run_gpu(x)
+    assert np.all(np.isfinite(o)) and np.all(np.isfinite(S))
+    compare_heads(o, S, oracle_heads(x, [(0, 0), (2, 9), (3, 15)]), TOL["bf16"], "rot")
+
+
+def test_long_content_sampled():
+    """Long context + content-aware erase (B=1, H=16, T=32768, d=128, L=128)."""
+    x = generate(WORKLOADS["long"])
+    o, S = run_gpu(x)
+    assert np.all(np.isfinite(o)) and np.all(np.isfinite(S))
+    compare_heads(o, S, oracle_heads(x, [(0, 0), (0, 11)]), TOL["bf16"], "long")
+
+
+def test_decode_full():
+    """Decode: one token on 256 x 16 states of 128 x 128 (rotation variant)."""
+    import torch
+    import recurrent_state_memory_amd as gdr
+    d = generate_decode()
+    io = io_dtype(d.io)
+    S = dev(d.S)
+    o = gdr.gdr_step_decode(S, dev(d.q, io), dev(d.k, io), dev(d.v, io), dev(d.alpha),
+                            dev(d.beta), dev(d.w), theta=dev(d.theta))
+    torch.cuda.synchronize()
+    S_r, o_r = seq.decode_step(d.S, d.q, d.k, d.v, d.beta, d.w, d.alpha, d.theta, d.decay)
+    eo = max_rel_err(o.float().cpu().numpy(), o_r)
+    es = max_rel_err(S.cpu().numpy(), S_r)
+    print(f"decode: err(o) = {eo:.3e} err(S) = {es:.3e}")
+    assert eo <= TOL["bf16"] and es <= TOL["bf16"]
+
+
+# ------------------------------------------------------------ sweeps and edges
+@pytest.mark.parametrize("io", ["f32", "bf16"])
+@pytest.mark.parametrize("decay", ["diag", "rot2"])
+@pytest.mark.parametrize("dk", [32, 64, 128])
+@pytest.mark.parametrize("chunk", [16, 32, 64, 128])
+def test_sweep_ragged(io, decay, dk, chunk):
+    """Several chunks plus a ragged tail, non-zero S0, every supported block size."""
+    T = 3 * chunk + 5
+    x = generate(_wl(io, decay, dk, T=T, chunk=chunk, seed=100 + dk + chunk))
+    S0 = random_state(2, 3, dk, dk, 7)
+    o, S = run_gpu(x, S0=S0)
+    compare_heads(o, S, oracle_heads(x, S0=S0), TOL[io], f"{io}/{decay}/d{dk}/L{chunk}")
+
+
+@pytest.mark.parametrize("io", ["f32", "bf16"])
+def test_single_token_and_short(io):
+    for T in (1, 2, 15, 17):
+        x = generate(_wl(io, "diag", 64, T=T, chunk=16, seed=T))
+        S0 = random_state(2, 3, 64, 64, T)
+        o, S = run_gpu(x, S0=S0)
+        compare_heads(o, S, oracle_heads(x, S0=S0), TOL[io], f"T={T}")
+
+
+def test_many_heads_grid_padding():
+    """B*H not a multiple of 8 exercises the padded workgroup grid."""
+    x = generate(_wl("bf16", "diag", 128, B=3, H=5, T=130, chunk=64, seed=5))
+    o, S = run_gpu(x)
+    compare_heads(o, S, oracle_heads(x), TOL["bf16"], "B3H5")
+
+
+def test_state_in_place_alias():
+    x = generate(_wl("bf16", "rot2", 128, T=150, chunk=64, seed=9))
+    S0 = random_state(2, 3, 128, 128, 9)
+    o1, S1 = run_gpu(x, S0=S0)
+    o2, S2 = run_gpu(x, S0=S0, alias=True)
+    np.testing.assert_array_equal(o1, o2)
+    np.testing.assert_array_equal(S1, S2)
+
+
+def test_zero_state_same_as_null():
+    x = generate(_wl("bf16", "diag", 64, T=100, chunk=32, seed=3))
+    o1, S1 = run_gpu(x)
+    o2, S2 = run_gpu(x, S0=np.zeros((2, 3, 64, 64), np.float32))
+    np.testing.assert_array_equal(o1, o2)
+    np.testing.assert_array_equal(S1, S2)
+
+
+def test_deterministic_rerun():
+    x = generate(_wl("bf16", "diag", 128, B=2, H=4, T=300, chunk=64, seed=4))
+    o1, S1 = run_gpu(x)
+    o2, S2 = run_gpu(x)
+    assert np.array_equal(o1, o2) and np.array_equal(S1, S2)
+
+
+@pytest.mark.parametrize("io", ["f32", "bf16"])
+def test_resume_matches_whole(io):
+    """fwd(T1) then fwd(T2, S0 = S_T1) equals fwd(T1 + T2) (exact affine transfer)."""
+    x = generate(_wl(io, "rot2", 64, T=300, chunk=64, seed=12))
+    o, S = run_gpu(x)
+    a, b = _split(x, 137)
+    o1, S1 = run_gpu(a)
+    o2, S2 = run_gpu(b, S0=S1)
+    tol = TOL[io]
+    assert max_rel_err(np.concatenate([o1, o2], axis=1), o) <= tol
+    assert max_rel_err(S2, S) <= tol
+
+
+def _split(x, t1):
+    import dataclasses
+
+    def cut(arr, sl):
+        return None if arr is None else arr[:, sl]
+    parts = []
+    for sl, T in ((slice(0, t1), t1), (slice(t1, None), x.wl.T - t1)):
+        parts.append(dataclasses.replace(
+            x, wl=x.wl.replace(T=T), q=cut(x.q, sl), k=cut(x.k, sl), v=cut(x.v, sl),
+            beta=cut(x.beta, sl), w=cut(x.w, sl), alpha=cut(x.alpha, sl),
+            theta=cut(x.theta, sl), beta_logit=cut(x.beta_logit, sl)))
+    return parts
+
+
+# ------------------------------------------------------------ content-aware erase
+@pytest.mark.parametrize("io", ["f32", "bf16"])
+@pytest.mark.parametrize("dk", [64, 128])
+@pytest.mark.parametrize("chunk", [16, 64, 128])
+def test_content_aware_stress(io, dk, chunk):
+    """Projection std 1.0 so the content signal moves beta visibly; T spans 4 windows
+    plus a partial one."""
+    wl = _wl(io, "diag", dk, B=2, H=2, T=4 * chunk + 7, chunk=chunk, content=True, seed=31)
+    x = generate(wl, ub_std=1.0)
+    o, S = run_gpu(x)
+    compare_heads(o, S, oracle_heads(x), TOL[io], f"content {io}/d{dk}/L{chunk}")
+    # the signal matters: the plain-beta result differs beyond tolerance
+    import dataclasses
+    ref0 = oracle_heads(dataclasses.replace(x, ub_down=0 * x.ub_down))
+    o0 = np.stack([ref0[k][0] for k in ref0])
+    og = np.stack([o[b, :, h] for (b, h) in ref0])
+    assert max_rel_err(og, o0) > 0.1
+
+
+@pytest.mark.parametrize("io", ["f32", "bf16"])
+def test_content_aware_resume_with_carry(io):
+    wl = _wl(io, "diag", 64, B=2, H=2, T=256, chunk=64, content=True, seed=32)
+    x = generate(wl, ub_std=1.0)
+    o, S = run_gpu(x)
+    a, b = _split(x, 128)
+    o1, S1, m1 = run_gpu(a, return_m=True)
+    ref = oracle_heads(a, return_m=True)
+    m_r = np.stack([ref[k][2] for k in ref])
+    m_g = np.stack([m1[bb, hh] for (bb, hh) in ref])
+    assert max_rel_err(m_g, m_r) <= TOL[io]
+    o2, S2 = run_gpu(b, S0=S1, m_carry=m1)
+    tol = TOL[io]
+    assert max_rel_err(np.concatenate([o1, o2], axis=1), o) <= tol
+    assert max_rel_err(S2, S) <= tol
+
+
+# ------------------------------------------------------------ decode
+@pytest.mark.parametrize("io", ["f32", "bf16"])
+@pytest.mark.parametrize("decay", ["diag", "rot2"])
+@pytest.mark.parametrize("dk", [32, 64, 128])
+def test_decode_variants(io, decay, dk):
+    import torch
+    import recurrent_state_memory_amd as gdr
+    wl = _wl(io, decay, dk)
+    d = generate_decode(wl, N=7, rng=np.random.default_rng(dk))
+    iot = io_dtype(io)
+    S = dev(d.S)
+    o = gdr.gdr_step_decode(S, dev(d.q, iot), dev(d.k, iot), dev(d.v, iot), dev(d.alpha),
+                            dev(d.beta), dev(d.w), theta=dev(d.theta))
+    torch.cuda.synchronize()
+    S_r, o_r = seq.decode_step(d.S, d.q, d.k, d.v, d.beta, d.w, d.alpha, d.theta, decay)
+    assert max_rel_err(o.float().cpu().numpy(), o_r) <= TOL[io]
+    assert max_rel_err(S.cpu().numpy(), S_r) <= TOL[io]
+
+
+@pytest.mark.parametrize("io", ["f32", "bf16"])
+@pytest.mark.parametrize("decay", ["diag", "rot2"])
+def test_decode_chain_equals_chunk_fwd(io, decay):
+    """T decode steps from S0 reproduce the chunked forward (o and final S)."""
+    import torch
+    import recurrent_state_memory_amd as gdr
+    x = generate(_wl(io, decay, 128, B=2, H=2, T=40, chunk=16, seed=41))
+    S0 = random_state(2, 2, 128, 128, 41)
+    o_c, S_c = run_gpu(x, S0=S0)
+    iot = io_dtype(io)
+    S = dev(S0)
+    outs = []
+    for t in range(x.wl.T):
+        sl = (slice(None), t)
+        o = gdr.gdr_step_decode(
+            S, dev(x.q[sl], iot), dev(x.k[sl], iot), dev(x.v[sl], iot), dev(x.alpha[sl]),
+            dev(x.beta[sl]), dev(x.w[sl]), theta=None if x.theta is None else dev(x.theta[sl]))
+        outs.append(o.float())
+    torch.cuda.synchronize()
+    o_d = torch.stack(outs, dim=1).cpu().numpy()
+    tol = TOL[io]
+    assert max_rel_err(o_d, o_c) <= tol
+    assert max_rel_err(S.cpu().numpy(), S_c) <= tol
