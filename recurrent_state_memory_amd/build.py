@@ -21,7 +21,7 @@ ROOT = os.path.dirname(HERE)
 BUILD = os.path.join(ROOT, "_build")
 LIB = os.path.join(HERE, "libgdr.so")
 
-SOURCES = ["gdr_api.cpp", "gdr_fwd.hip", "gdr_step.hip"]
+SOURCES = ["gdr_api.cpp", "gdr_fwd.hip", "gdr_fwd_pipe.hip", "gdr_step.hip"]
 
 HIPCC = os.environ.get("HIPCC", shutil.which("hipcc") or "/opt/rocm/bin/hipcc")
 ARCH = "gfx950"

@@ -76,6 +76,77 @@ __device__ inline void store4<float>(float* p, const float (&x)[4]) {
   *(f32x4*)p = v;
 }
 
+
+// Raw (unconverted) inputs of one chunk for one thread, loaded without
+// branches (token indices are clamped; invalid tokens are masked on use).
+template <typename T>
+struct RawPair;
+template <>
+struct RawPair<__bf16> {
+  using type = uint32_t;
+  static __device__ inline uint32_t load(const __bf16* p) { return *(const uint32_t*)p; }
+  static __device__ inline f32x2 cvt(uint32_t u) {
+    return f32x2{__uint_as_float(u << 16), __uint_as_float(u & 0xffff0000u)};
+  }
+};
+template <>
+struct RawPair<float> {
+  using type = f32x2;
+  static __device__ inline f32x2 load(const float* p) { return *(const f32x2*)p; }
+  static __device__ inline f32x2 cvt(f32x2 u) { return u; }
+};
+
+template <typename T, int TPS, int NVL>
+struct RawChunk {
+  typename RawPair<T>::type k[TPS], q[TPS];
+  f32x2 a[TPS];   // per-channel decay: the alpha pair; rotation: (gamma, theta)
+  uint4 v[NVL];   // 16-byte pieces of the value tile
+  float bt, wt;   // erase strength (or its logit) and write gate of token tid
+};
+
+template <typename T, int DK, int L, int TV, int DECAY, bool CONTENT, typename Raw>
+__device__ inline void load_raw(Raw& R, const FwdParams& p, int c0, int pp, int seg, int tid,
+                                int b, int h, int v0) {
+  constexpr int NP = DK / 2, NT = TV / 16 * 64;
+  constexpr int NSEG0 = NT / NP;
+  constexpr int NSEG = NSEG0 < L / 4 ? NSEG0 : L / 4;
+  constexpr int TPS = L / NSEG;
+  constexpr int VEC = 16 / sizeof(T), VPR = TV / VEC;
+  const int Tn = p.T, H = p.H, DV = p.DV;
+  const T* gk = (const T*)p.k;
+  const T* gq = (const T*)p.q;
+  const T* gv = (const T*)p.v;
+#pragma unroll
+  for (int r = 0; r < TPS; ++r) {
+    int t = c0 + seg * TPS + r;
+    t = t < Tn ? t : Tn - 1;
+    const size_t base = (size_t)(b * Tn + t) * H + h;
+    R.k[r] = RawPair<T>::load(gk + base * DK + 2 * pp);
+    R.q[r] = RawPair<T>::load(gq + base * DK + 2 * pp);
+    if constexpr (DECAY == 0) {
+      R.a[r] = *(const f32x2*)(p.alpha + base * DK + 2 * pp);
+    } else {
+      R.a[r] = f32x2{p.alpha[base * NP + pp], p.theta[base * NP + pp]};
+    }
+  }
+#pragma unroll
+  for (int i = 0; i < (int)(sizeof(R.v) / sizeof(R.v[0])); ++i) {
+    int idx = tid + i * NT;
+    idx = idx < L * VPR ? idx : 0;
+    const int r = idx / VPR, cc = idx % VPR;
+    int t = c0 + r;
+    t = t < Tn ? t : Tn - 1;
+    R.v[i] = *(const uint4*)(gv + ((size_t)(b * Tn + t) * H + h) * DV + v0 + cc * VEC);
+  }
+  {
+    int t = c0 + (tid < L ? tid : L - 1);
+    t = t < Tn ? t : Tn - 1;
+    const size_t gi = (size_t)(b * Tn + t) * H + h;
+    R.bt = CONTENT ? p.beta_logit[gi] : p.beta[gi];
+    R.wt = p.w[gi];
+  }
+}
+
 template <typename T, int DK, int L, int TV, int DECAY, bool CONTENT>
 struct FwdCfg {
   static constexpr int NW = TV / 16;             // waves; wave w owns value block w
@@ -93,6 +164,8 @@ struct FwdCfg {
   static constexpr int NKC = DK / 32;            // 32-wide steps over key channels
   static constexpr int NKT = (NB + 1) / 2;       // 32-wide steps over tokens
   static constexpr int NCW = NCT / NW;           // W channel tiles per wave
+  static constexpr int NVL0 = (L * (int)sizeof(T) + 63) / 64;
+  static constexpr int NVL = NVL0 < 1 ? 1 : NVL0;  // 16-byte value loads per thread
   static_assert(TV % 16 == 0 && NCT % NW == 0, "tile split");
   static_assert(NSEG >= 1 && TPS % 4 == 0, "prep split");
   static constexpr size_t LDS =
@@ -164,13 +237,12 @@ __global__ __launch_bounds__(TV / 16 * 64) void gdr_fwd_kernel(FwdParams p) {
   f32x4 Sacc[NCT];
   {
     const size_t srow = ((size_t)(b * H + h) * DV + v0 + 16 * wv + n) * DK;
+    if (p.S0) {
 #pragma unroll
-    for (int ct = 0; ct < NCT; ++ct) {
-      if (p.S0) {
-        Sacc[ct] = *(const f32x4*)(p.S0 + srow + 16 * ct + 4 * g);
-      } else {
-        Sacc[ct] = f32x4{0.f, 0.f, 0.f, 0.f};
-      }
+      for (int ct = 0; ct < NCT; ++ct) Sacc[ct] = *(const f32x4*)(p.S0 + srow + 16 * ct + 4 * g);
+    } else {
+#pragma unroll
+      for (int ct = 0; ct < NCT; ++ct) Sacc[ct] = f32x4{0.f, 0.f, 0.f, 0.f};
     }
   }
 
@@ -196,72 +268,58 @@ __global__ __launch_bounds__(TV / 16 * 64) void gdr_fwd_kernel(FwdParams p) {
   }
 
   const bool prep = tid < NP * NSEG;
-  const int pp = tid % NP, seg = tid / NP;
+  // threads outside the prep split load a valid (unused) address instead of branching
+  const int pp = tid % NP, seg = (tid / NP) % NSEG;
   const int nchunks = (Tn + L - 1) / L;
+
+  using RP = RawPair<T>;
+  using Raw = RawChunk<T, TPS, C::NVL>;
+  Raw R;
+  load_raw<T, DK, L, TV, DECAY, CONTENT>(R, p, 0, pp, seg, tid, b, h, v0);
 
   for (int c = 0; c < nchunks; ++c) {
     const int c0 = c * L;
 
     // ------------------------------------------------------------ stage P1
-    f32x2 cum[TPS], k2[TPS], q2[TPS];
+    f32x2 cum[TPS];
     if (prep) {
       f32x2 run = {1.f, DECAY == 0 ? 1.f : 0.f};
 #pragma unroll
       for (int r = 0; r < TPS; ++r) {
-        const int t = c0 + seg * TPS + r;
-        const bool ok = t < Tn;
-        const size_t base = (size_t)(b * Tn + (ok ? t : 0)) * H + h;
-        f32x2 kv = {0.f, 0.f}, qv = {0.f, 0.f};
-        if (ok) {
-          kv = Pair<T>::load(gk + base * DK + 2 * pp);
-          qv = Pair<T>::load(gq + base * DK + 2 * pp);
-        }
+        const bool ok = c0 + seg * TPS + r < Tn;
         if constexpr (DECAY == 0) {
-          f32x2 a = {1.f, 1.f};
-          if (ok) a = *(const f32x2*)(p.alpha + base * DK + 2 * pp);
+          const f32x2 a = ok ? R.a[r] : f32x2{1.f, 1.f};
           run.x *= a.x;
           run.y *= a.y;
         } else {
-          float gm = 1.f, th = 0.f;
-          if (ok) {
-            gm = p.alpha[base * NP + pp];
-            th = p.theta[base * NP + pp];
-          }
+          const float gm = ok ? R.a[r].x : 1.f;
+          const float th = ok ? R.a[r].y : 0.f;
           float sn, cs;
           __sincosf(th, &sn, &cs);
-          f32x2 z = {gm * cs, gm * sn};
-          run = cmul(run, z);
+          run = cmul(run, f32x2{gm * cs, gm * sn});
         }
         cum[r] = run;
-        k2[r] = kv;
-        q2[r] = qv;
       }
       sSeg[seg * NP + pp] = run;
     }
     if (tid < L) {
-      const int t = c0 + tid;
-      float bt = 0.f, wt = 0.f;
-      if (t < Tn) {
-        const size_t gi = (size_t)(b * Tn + t) * H + h;
-        if constexpr (CONTENT) {
-          const float x = p.beta_logit[gi] + sS[0];
-          bt = 1.f / (1.f + __expf(-x));
-        } else {
-          bt = p.beta[gi];
-        }
-        wt = p.w[gi];
-      }
+      const bool ok = c0 + tid < Tn;
+      float bt = R.bt;
+      if constexpr (CONTENT) bt = 1.f / (1.f + __expf(-(bt + sS[0])));
+      bt = ok ? bt : 0.f;
       sBeta[tid] = bt;
-      sBW[tid] = bt * wt;
+      sBW[tid] = ok ? bt * R.wt : 0.f;
     }
     {
       constexpr int VEC = 16 / sizeof(T), VPR = TV / VEC;
-      for (int idx = tid; idx < L * VPR; idx += NT) {
-        const int r = idx / VPR, cc = idx % VPR;
-        const int t = c0 + r;
-        uint4 val = {0u, 0u, 0u, 0u};
-        if (t < Tn) val = *(const uint4*)(gv + ((size_t)(b * Tn + t) * H + h) * DV + v0 + cc * VEC);
-        *(uint4*)(sV + r * RSV + cc * VEC) = val;
+#pragma unroll
+      for (int i = 0; i < C::NVL; ++i) {
+        const int idx = tid + i * NT;
+        if (idx < L * VPR) {
+          const int r = idx / VPR, cc = idx % VPR;
+          const uint4 zero = {0u, 0u, 0u, 0u};
+          *(uint4*)(sV + r * RSV + cc * VEC) = (c0 + r < Tn) ? R.v[i] : zero;
+        }
       }
     }
     __syncthreads();
@@ -293,21 +351,24 @@ __global__ __launch_bounds__(TV / 16 * 64) void gdr_fwd_kernel(FwdParams p) {
         for (int u = 0; u < 4; ++u) {
           const int r = r4 + u;
           const int row = seg * TPS + r;
+          const bool ok = c0 + row < Tn;
+          f32x2 k2 = RP::cvt(R.k[r]), q2 = RP::cvt(R.q[r]);
+          if (!ok) k2 = q2 = f32x2{0.f, 0.f};
           f32x2 kp, kh, qp, km;
           if constexpr (DECAY == 0) {
             const f32x2 gc = {pre.x * cum[r].x, pre.y * cum[r].y};
-            const f32x2 inv = {1.f / gc.x, 1.f / gc.y};
-            kp = f32x2{k2[r].x * gc.x, k2[r].y * gc.y};
-            kh = f32x2{k2[r].x * inv.x, k2[r].y * inv.y};
-            qp = f32x2{q2[r].x * gc.x, q2[r].y * gc.y};
-            km = f32x2{k2[r].x * (tot.x * inv.x), k2[r].y * (tot.y * inv.y)};
+            const f32x2 inv = {__builtin_amdgcn_rcpf(gc.x), __builtin_amdgcn_rcpf(gc.y)};
+            kp = f32x2{k2.x * gc.x, k2.y * gc.y};
+            kh = f32x2{k2.x * inv.x, k2.y * inv.y};
+            qp = f32x2{q2.x * gc.x, q2.y * gc.y};
+            km = f32x2{k2.x * (tot.x * inv.x), k2.y * (tot.y * inv.y)};
           } else {
             const f32x2 z = cmul(pre, cum[r]);
-            const float nz = 1.f / (z.x * z.x + z.y * z.y);
+            const float nz = __builtin_amdgcn_rcpf(z.x * z.x + z.y * z.y);
             const f32x2 zi = {z.x * nz, z.y * nz};          // Gamma^{-T} block
-            kp = cmul(z, k2[r]);
-            kh = cmul(zi, k2[r]);
-            qp = cmul(z, q2[r]);
+            kp = cmul(z, k2);
+            kh = cmul(zi, k2);
+            qp = cmul(z, q2);
             km = cmul(f32x2{tot.x, -tot.y}, kh);          // Gamma_L^T Kh
           }
           Pair<T>::store(sKp + row * RSK + 2 * pp, kp);
@@ -321,6 +382,9 @@ __global__ __launch_bounds__(TV / 16 * 64) void gdr_fwd_kernel(FwdParams p) {
         store4<T>(sKmT + (2 * pp + 1) * RSL + col, km1);
       }
     }
+    // prefetch the next chunk's inputs; they land while this chunk computes
+    if (c + 1 < nchunks)
+      load_raw<T, DK, L, TV, DECAY, CONTENT>(R, p, c0 + L, pp, seg, tid, b, h, v0);
     __syncthreads();
 
     // ------------------------------------------------------------ stage G
@@ -589,6 +653,7 @@ static hipError_t pick_variant(const FwdParams& p, hipStream_t s) {
 }
 
 hipError_t launch_fwd(const FwdParams& p, hipStream_t stream) {
+  if (fwd_pipe_supported(p)) return launch_fwd_pipe(p, stream);
   if (p.io_bf16) return pick_variant<__bf16>(p, stream);
   return pick_variant<float>(p, stream);
 }

@@ -47,6 +47,9 @@ struct StepParams {
 };
 
 hipError_t launch_fwd(const FwdParams& p, hipStream_t stream);
+// pipelined bf16 forward (gdr_fwd_pipe.hip) for the plain erase, d_k = d_v in {64, 128}
+bool fwd_pipe_supported(const FwdParams& p);
+hipError_t launch_fwd_pipe(const FwdParams& p, hipStream_t stream);
 hipError_t launch_step(const StepParams& p, hipStream_t stream);
 int fwd_block_len(int dk, int chunk, bool io_bf16);
 
