@@ -256,7 +256,7 @@ __global__ __launch_bounds__(TV / 16 * 64) void gdr_fwd_kernel(FwdParams p) {
       sU[vv] = acc;
       sMean[vv] = p.m_carry ? p.m_carry[(size_t)(b * H + h) * DV + v0 + vv] : 0.f;
     }
-    __syncthreads();
+    lds_barrier();
     if (wv == 0) {
       float acc = 0.f;
       for (int vv = l; vv < TV; vv += 64) acc += sU[vv] * sMean[vv];
@@ -264,7 +264,7 @@ __global__ __launch_bounds__(TV / 16 * 64) void gdr_fwd_kernel(FwdParams p) {
       for (int off = 32; off > 0; off >>= 1) acc += __shfl_xor(acc, off);
       if (l == 0) sS[0] = acc;
     }
-    __syncthreads();
+    lds_barrier();
   }
 
   const bool prep = tid < NP * NSEG;
@@ -317,12 +317,17 @@ __global__ __launch_bounds__(TV / 16 * 64) void gdr_fwd_kernel(FwdParams p) {
         const int idx = tid + i * NT;
         if (idx < L * VPR) {
           const int r = idx / VPR, cc = idx % VPR;
-          const uint4 zero = {0u, 0u, 0u, 0u};
-          *(uint4*)(sV + r * RSV + cc * VEC) = (c0 + r < Tn) ? R.v[i] : zero;
+          const bool ok = c0 + r < Tn;
+          uint4 val;
+          val.x = ok ? R.v[i].x : 0u;
+          val.y = ok ? R.v[i].y : 0u;
+          val.z = ok ? R.v[i].z : 0u;
+          val.w = ok ? R.v[i].w : 0u;
+          *(uint4*)(sV + r * RSV + cc * VEC) = val;
         }
       }
     }
-    __syncthreads();
+    lds_barrier();
 
     // ------------------------------------------------------------ stage P2
     if (prep) {
@@ -385,7 +390,7 @@ __global__ __launch_bounds__(TV / 16 * 64) void gdr_fwd_kernel(FwdParams p) {
     // prefetch the next chunk's inputs; they land while this chunk computes
     if (c + 1 < nchunks)
       load_raw<T, DK, L, TV, DECAY, CONTENT>(R, p, c0 + L, pp, seg, tid, b, h, v0);
-    __syncthreads();
+    lds_barrier();
 
     // ------------------------------------------------------------ stage G
     {
@@ -415,7 +420,7 @@ __global__ __launch_bounds__(TV / 16 * 64) void gdr_fwd_kernel(FwdParams p) {
         }
       }
     }
-    __syncthreads();
+    lds_barrier();
 
     // ------------------------------------------------------------ stage D
     if (tid < L) {
@@ -431,7 +436,7 @@ __global__ __launch_bounds__(TV / 16 * 64) void gdr_fwd_kernel(FwdParams p) {
 #pragma unroll
       for (int i = 0; i < 16; ++i) sTd[(bb * 16 + i) * RST + cc] = (T)tcol[i];
     }
-    __syncthreads();
+    lds_barrier();
 
     // ------------------------------------------------------------ stage WU
     f32x4 Uacc[NB];
@@ -489,7 +494,7 @@ __global__ __launch_bounds__(TV / 16 * 64) void gdr_fwd_kernel(FwdParams p) {
             sW[(16 * bb + 4 * g + j) * RSK + 16 * cb + n] = (T)Wacc[cw][bb][j];
       }
     }
-    __syncthreads();
+    lds_barrier();
 
     // ------------------------------------------------------------ stage S
     {
@@ -570,10 +575,10 @@ __global__ __launch_bounds__(TV / 16 * 64) void gdr_fwd_kernel(FwdParams p) {
         s += __shfl_xor(s, 32);
         const int wstart = (cend - 1) / p.window * p.window;
         const int wlen = (cend < Tn ? cend : Tn) - wstart;
-        __syncthreads();   // everyone is done reading sS for this window
+        lds_barrier();   // everyone is done reading sS for this window
         if (g == 0) sMean[16 * wv + n] = s / (float)wlen;
         colsum = 0.f;
-        __syncthreads();
+        lds_barrier();
         if (wv == 0) {
           float acc = 0.f;
           for (int vv = l; vv < TV; vv += 64) acc += sU[vv] * sMean[vv];
@@ -583,7 +588,7 @@ __global__ __launch_bounds__(TV / 16 * 64) void gdr_fwd_kernel(FwdParams p) {
         }
       }
     }
-    __syncthreads();
+    lds_barrier();
   }
 
   if (p.S_out) {

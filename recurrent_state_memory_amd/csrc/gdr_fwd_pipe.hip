@@ -2,29 +2,26 @@
 //
 // Same computation as gdr_fwd.hip (chunk-WY algebra of the CARVE technical
 // summary, section 1.3, and the SFDA constructive chunk-WY theorem / exact
-// affine chunk transfer), organised so that the state-independent work of
-// chunk c+1 overlaps the state-dependent work of chunk c inside one
-// workgroup:
+// affine chunk transfer), as a three-stage pipeline inside one workgroup with
+// a single workgroup barrier per 32-token step:
 //
-//   producer waves (4): load chunk c+1 (issued one chunk ahead), running
-//     products of the key-axis transitions, decayed forms K+, Q+, Kh, K-^T,
-//     Gram tiles A = strict_lower(diag(beta) K+ Kh^T), M = lower_incl(Q+ Kh^T),
-//     and the two 16x16 diagonal blocks T00, T11 of (I + A)^{-1};
-//   consumer waves (one per 16 value channels): for chunk c,
+//   prep waves (4), chunk i+2: load the chunk (issued one chunk ahead),
+//     running products of the key-axis transitions (forward and backward,
+//     scanned across token segments inside each wave), decayed forms
+//     K+ = g_r k, Q+ = g_r q, K- = h_r^T k, Kh = Gamma_L^{-T} K-.
+//   solve waves (4), chunk i+1: Gram tiles A = strict_lower(diag(beta) K+ Kh^T)
+//     and M = lower_incl(Q+ Kh^T), and the two 16x16 diagonal blocks T00, T11
+//     of (I + A)^{-1} as the nilpotent product (I - N)(I + N^2)(I + N^4)(I + N^8)
+//     on the matrix cores.
+//   consumer waves (one per 16 value channels), chunk i:
 //     R  = diag(beta w) V - diag(beta) K+ S^T
 //     Dl = (I + A)^{-1} R by blocks: Dl0 = T00 R0, Dl1 = T11 (R1 - A10 Dl0)
 //     O  = Q+ S^T + M Dl,   S <- S Gamma_L + Dl^T K-.
 //
-// The chunk length is 32 tokens (two 16-token blocks).  The consumer-side
-// buffers are double-buffered in LDS; one workgroup-wide barrier separates
-// each of the three phases of an iteration, and both roles pass the same
-// number of barriers.
-//
-// Running products without reciprocals: with g_r = prod_{s<=r} D_s (forward)
-// and h_r = prod_{s>r} D_s (backward) inside the chunk, K+ = g_r k,
-// Q+ = g_r q, K- = h_r^T k, and Kh = Gamma_r^{-T} k = Gamma_L^{-T} K-, so only
-// one reciprocal per key channel (of Gamma_L) is needed per chunk.  For 2x2
-// rotation-decay blocks the same holds with complex products per channel pair.
+// g_r = prod_{s<=r} D_s and h_r = prod_{s>r} D_s inside the chunk, so only one
+// reciprocal per key channel (of Gamma_L) is needed; for 2x2 rotation-decay
+// blocks the same holds with complex products per channel pair.  Prep outputs
+// are triple-buffered and solve outputs double-buffered in LDS.
 #include "gdr_kernels.h"
 #include "gdr_mfma.h"
 
@@ -49,18 +46,19 @@ __device__ inline uint32_t f2_to_bf2(f32x2 x) {
 }
 
 constexpr int L = 32;      // tokens per chunk
-constexpr int NWP = 4;     // producer waves
+constexpr int NWP = 4;     // prep waves
+constexpr int NWS = 4;     // solve waves
 constexpr int RSL = L + 4; // row stride of [.][L] arrays
 constexpr int RS16 = 20;   // row stride of 16x16 blocks
 
 template <int DK, int TV>
 struct Cfg {
   static constexpr int NWC = TV / 16;            // consumer waves
-  static constexpr int NT = (NWP + NWC) * 64;
+  static constexpr int NT = (NWP + NWS + NWC) * 64;
   static constexpr int NP = DK / 2;              // channel pairs
-  static constexpr int NSEG0 = NWP * 64 / NP;
-  static constexpr int NSEG = NSEG0 < L / 4 ? NSEG0 : L / 4;
-  static constexpr int TPS = L / NSEG;           // tokens per producer thread
+  static constexpr int PPW = NP / NWP;           // channel pairs per prep wave
+  static constexpr int NSEG = 64 / PPW;          // token segments per prep wave
+  static constexpr int TPS = L / NSEG;           // tokens per prep lane
   static constexpr int RSK = DK + 8;
   static constexpr int RSV = TV + 8;
   static constexpr int NCT = DK / 16;
@@ -70,29 +68,33 @@ struct Cfg {
   static_assert(L * VPR <= NWP * 64, "value tile load split");
 };
 
-// Consumer-side buffers of one chunk (double-buffered).
+// Prep outputs of one chunk (3 slots: written for i+2, read for i+1 and i).
 template <int DK, int TV>
-struct Buf {
+struct SlotA {
   using C = Cfg<DK, TV>;
   bf Kp[L * C::RSK];
   bf Qp[L * C::RSK];
   bf KmT[DK * RSL];
-  bf M[L * RSL];
-  bf A10[16 * RS16];
-  bf Td[2 * 16 * RS16];
   bf V[L * C::RSV];
   float beta[L];
   float bw[L];
   f32x2 GL[C::NP];
 };
 
+// Solve outputs of one chunk (2 slots).
+struct SlotS {
+  bf M[L * RSL];
+  bf A10[16 * RS16];
+  bf Td[2 * 16 * RS16];
+};
+
 template <int DK, int TV>
 struct Shared {
   using C = Cfg<DK, TV>;
-  Buf<DK, TV> buf[2];
-  bf Kh[L * C::RSK];
-  float Ad[2 * 16 * 17];
-  f32x2 segF[C::NSEG * C::NP];
+  SlotA<DK, TV> a[3];
+  bf Kh[2][L * C::RSK];
+  SlotS s[2];
+  f32x2 segT[NWP][64];
 };
 
 template <int TPS>
@@ -103,50 +105,86 @@ struct Raw {
   float bt, wt;
 };
 
+// Buffer resources over one (b, h): element (t, c) of a [B,T,H,X] tensor sits at
+// byte (t * H * X + c) * size from the resource base, and the resource ends
+// after token T-1, so loads past the sequence return zero without a branch.
+using rsrc_t = __amdgpu_buffer_rsrc_t;
+__device__ inline rsrc_t make_rsrc(const void* base, size_t bytes) {
+  return __builtin_amdgcn_make_buffer_rsrc(const_cast<void*>(base), (short)0,
+                                           (int)(uint32_t)bytes, 0x00020000);
+}
+
+struct Rsrc {
+  rsrc_t k, q, a, th, v, beta, w;
+  int sk, sa, sv, sb;   // per-token byte strides
+};
+
 template <int DK, int TV, int DECAY>
-__device__ inline void load_raw(Raw<Cfg<DK, TV>::TPS>& R, const FwdParams& p, int c0, int pp,
-                                int seg, int ptid, int b, int h, int v0) {
+__device__ inline Rsrc make_rsrcs(const FwdParams& p, int b, int h, int v0) {
+  const int Tn = p.T, H = p.H, DV = p.DV;
+  const size_t bh = (size_t)b * Tn * H + h;
+  const size_t rows = (size_t)(Tn - 1) * H + 1;   // token rows up to token T-1 of head h
+  Rsrc r;
+  r.sk = H * DK * 2;
+  r.k = make_rsrc((const bf*)p.k + bh * DK, rows * DK * 2);
+  r.q = make_rsrc((const bf*)p.q + bh * DK, rows * DK * 2);
+  if constexpr (DECAY == 0) {
+    r.sa = H * DK * 4;
+    r.a = make_rsrc(p.alpha + bh * DK, rows * DK * 4);
+    r.th = r.a;
+  } else {
+    r.sa = H * (DK / 2) * 4;
+    r.a = make_rsrc(p.alpha + bh * (DK / 2), rows * (DK / 2) * 4);
+    r.th = make_rsrc(p.theta + bh * (DK / 2), rows * (DK / 2) * 4);
+  }
+  r.sv = H * DV * 2;
+  r.v = make_rsrc((const bf*)p.v + bh * DV + v0, rows * DV * 2 - (size_t)v0 * 2);
+  r.sb = H * 4;
+  r.beta = make_rsrc(p.beta + bh, rows * 4);
+  r.w = make_rsrc(p.w + bh, rows * 4);
+  return r;
+}
+
+template <int DK, int TV, int DECAY>
+__device__ inline void load_raw(Raw<Cfg<DK, TV>::TPS>& R, const Rsrc& rs, int c0, int pp, int seg,
+                                int ptid) {
   using C = Cfg<DK, TV>;
-  const int Tn = p.T, H = p.H;
-  const bf* gk = (const bf*)p.k;
-  const bf* gq = (const bf*)p.q;
-  const bf* gv = (const bf*)p.v;
+  const int t0 = c0 + seg * C::TPS;
+  const int ko = t0 * rs.sk + 4 * pp;                       // byte offsets of token t0
+  const int ao = t0 * rs.sa + (DECAY == 0 ? 8 : 4) * pp;
 #pragma unroll
   for (int r = 0; r < C::TPS; ++r) {
-    int t = c0 + seg * C::TPS + r;
-    t = t < Tn ? t : Tn - 1;
-    const size_t base = (size_t)(b * Tn + t) * H + h;
-    R.k[r] = *(const uint32_t*)(gk + base * DK + 2 * pp);
-    R.q[r] = *(const uint32_t*)(gq + base * DK + 2 * pp);
+    const int kr = ko + r * rs.sk, ar = ao + r * rs.sa;     // r * stride is uniform
+    R.k[r] = __builtin_amdgcn_raw_buffer_load_b32(rs.k, kr, 0, 0);
+    R.q[r] = __builtin_amdgcn_raw_buffer_load_b32(rs.q, kr, 0, 0);
     if constexpr (DECAY == 0) {
-      R.a[r] = *(const f32x2*)(p.alpha + base * DK + 2 * pp);
+      const auto x = __builtin_amdgcn_raw_buffer_load_b64(rs.a, ar, 0, 0);
+      R.a[r] = f32x2{__uint_as_float(x[0]), __uint_as_float(x[1])};
     } else {
-      R.a[r] = f32x2{p.alpha[base * C::NP + pp], p.theta[base * C::NP + pp]};
+      R.a[r] = f32x2{__uint_as_float(__builtin_amdgcn_raw_buffer_load_b32(rs.a, ar, 0, 0)),
+                     __uint_as_float(__builtin_amdgcn_raw_buffer_load_b32(rs.th, ar, 0, 0))};
     }
   }
   {
     const int idx = ptid < L * C::VPR ? ptid : 0;
     const int r = idx / C::VPR, cc = idx % C::VPR;
-    int t = c0 + r;
-    t = t < Tn ? t : Tn - 1;
-    R.v = *(const uint4*)(gv + ((size_t)(b * Tn + t) * H + h) * p.DV + v0 + cc * 8);
+    const auto x = __builtin_amdgcn_raw_buffer_load_b128(rs.v, (c0 + r) * rs.sv + cc * 16, 0, 0);
+    R.v = uint4{x[0], x[1], x[2], x[3]};
   }
   {
-    int t = c0 + (ptid < L ? ptid : L - 1);
-    t = t < Tn ? t : Tn - 1;
-    const size_t gi = (size_t)(b * Tn + t) * H + h;
-    R.bt = p.beta[gi];
-    R.wt = p.w[gi];
+    const int t = c0 + (ptid < L ? ptid : L - 1);
+    R.bt = __uint_as_float(__builtin_amdgcn_raw_buffer_load_b32(rs.beta, t * rs.sb, 0, 0));
+    R.wt = __uint_as_float(__builtin_amdgcn_raw_buffer_load_b32(rs.w, t * rs.sb, 0, 0));
   }
 }
 
 template <int DK, int TV, int DECAY>
-__global__ __launch_bounds__((NWP + TV / 16) * 64) void gdr_fwd_pipe_kernel(FwdParams p) {
+__global__ __launch_bounds__((NWP + NWS + TV / 16) * 64) void gdr_fwd_pipe_kernel(FwdParams p) {
   using C = Cfg<DK, TV>;
   using O = Op<bf>;
   using frag = O::frag;
-  constexpr int NP = C::NP, NSEG = C::NSEG, TPS = C::TPS, RSK = C::RSK, RSV = C::RSV,
-                NCT = C::NCT, NKC = C::NKC, VPR = C::VPR;
+  constexpr int NP = C::NP, PPW = C::PPW, NSEG = C::NSEG, TPS = C::TPS, RSK = C::RSK,
+                RSV = C::RSV, NCT = C::NCT, NKC = C::NKC, VPR = C::VPR;
   __shared__ __attribute__((aligned(16))) Shared<DK, TV> sh;
 
   const int tid = threadIdx.x;
@@ -163,25 +201,26 @@ __global__ __launch_bounds__((NWP + TV / 16) * 64) void gdr_fwd_pipe_kernel(FwdP
   const int v0 = vt * TV;
   const int Tn = p.T, H = p.H, DV = p.DV;
   const int nchunks = (Tn + L - 1) / L;
+  const int nsteps = nchunks + 2;
 
   if (wv < NWP) {
-    // =============================================================== producer
+    // ================================================================ prep
+    const int pw = wv;
+    const int pl = l % PPW, seg = l / PPW, pp = pw * PPW + pl;
     const int ptid = tid;                       // 0 .. NWP*64-1
-    const bool prep = ptid < NP * NSEG;
-    const int pp = ptid % NP, seg = (ptid / NP) % NSEG;
+    const Rsrc rs = make_rsrcs<DK, TV, DECAY>(p, b, h, v0);
     Raw<TPS> R;
-    load_raw<DK, TV, DECAY>(R, p, 0, pp, seg, ptid, b, h, v0);
-
-    auto produce = [&](int j) {
-      Buf<DK, TV>& B = sh.buf[j & 1];
-      const int c0 = j * L;
-      // ---- phase 1: running products inside this thread's segment
-      f32x2 cf[TPS], cb[TPS];
-      if (prep) {
-        f32x2 d[TPS];
+    load_raw<DK, TV, DECAY>(R, rs, 0, pp, seg, ptid);
+    for (int it = 0; it < nsteps; ++it) {
+      if (it < nchunks) {
+        SlotA<DK, TV>& A = sh.a[it % 3];
+        bf* Kh = sh.Kh[it & 1];
+        const int c0 = it * L;
+        // running products inside this lane's token segment
+        f32x2 d[TPS], cf[TPS], cb[TPS];
 #pragma unroll
         for (int r = 0; r < TPS; ++r) {
-          const bool ok = c0 + seg * TPS + r < Tn;
+          const bool ok = c0 + seg * TPS + r < Tn;   // identity transition past the end
           if constexpr (DECAY == 0) {
             d[r] = ok ? R.a[r] : f32x2{1.f, 1.f};
           } else {
@@ -194,55 +233,44 @@ __global__ __launch_bounds__((NWP + TV / 16) * 64) void gdr_fwd_pipe_kernel(FwdP
         f32x2 run = {1.f, DECAY == 0 ? 1.f : 0.f};
 #pragma unroll
         for (int r = 0; r < TPS; ++r) {
-          if constexpr (DECAY == 0) {
-            run = f32x2{run.x * d[r].x, run.y * d[r].y};
-          } else {
-            run = cmul(run, d[r]);
-          }
+          run = (DECAY == 0) ? f32x2{run.x * d[r].x, run.y * d[r].y} : cmul(run, d[r]);
           cf[r] = run;
         }
         f32x2 bk = {1.f, DECAY == 0 ? 1.f : 0.f};
 #pragma unroll
         for (int r = TPS - 1; r >= 0; --r) {
-          cb[r] = bk;   // product over later tokens of the segment
-          if constexpr (DECAY == 0) {
-            bk = f32x2{bk.x * d[r].x, bk.y * d[r].y};
-          } else {
-            bk = cmul(bk, d[r]);
-          }
+          cb[r] = bk;   // product over the later tokens of the segment
+          bk = (DECAY == 0) ? f32x2{bk.x * d[r].x, bk.y * d[r].y} : cmul(bk, d[r]);
         }
-        sh.segF[seg * NP + pp] = run;
-      }
-      if (ptid < L) {
-        const bool ok = c0 + ptid < Tn;
-        B.beta[ptid] = ok ? R.bt : 0.f;
-        B.bw[ptid] = ok ? R.bt * R.wt : 0.f;
-      }
-      if (ptid < L * VPR) {
-        const int r = ptid / VPR, cc = ptid % VPR;
-        const uint4 zero = {0u, 0u, 0u, 0u};
-        *(uint4*)(B.V + r * RSV + cc * 8) = (c0 + r < Tn) ? R.v : zero;
-      }
-      __syncthreads();
-      // ---- phase 2: decayed forms
-      if (prep) {
+        sh.segT[pw][l] = run;
+        if (ptid < L) {   // loads past the sequence returned zero
+          A.beta[ptid] = R.bt;
+          A.bw[ptid] = R.bt * R.wt;
+        }
+        if (ptid < L * VPR) {
+          const int r = ptid / VPR, cc = ptid % VPR;
+          *(uint4*)(A.V + r * RSV + cc * 8) = R.v;
+        }
+        // segment products of this wave's channel pairs (same wave: no workgroup barrier)
+        __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront", "local");
+        __builtin_amdgcn_wave_barrier();
+        __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront", "local");
         f32x2 pre = {1.f, DECAY == 0 ? 1.f : 0.f}, post = pre, tot = pre;
 #pragma unroll
-        for (int s = 0; s < NSEG; ++s) {
-          const f32x2 x = sh.segF[s * NP + pp];
+        for (int s2 = 0; s2 < NSEG; ++s2) {
+          const f32x2 x = sh.segT[pw][pl + PPW * s2];
           if constexpr (DECAY == 0) {
-            if (s < seg) pre = f32x2{pre.x * x.x, pre.y * x.y};
-            if (s > seg) post = f32x2{post.x * x.x, post.y * x.y};
+            if (s2 < seg) pre = f32x2{pre.x * x.x, pre.y * x.y};
+            if (s2 > seg) post = f32x2{post.x * x.x, post.y * x.y};
             tot = f32x2{tot.x * x.x, tot.y * x.y};
           } else {
-            if (s < seg) pre = cmul(pre, x);
-            if (s > seg) post = cmul(post, x);
+            if (s2 < seg) pre = cmul(pre, x);
+            if (s2 > seg) post = cmul(post, x);
             tot = cmul(tot, x);
           }
         }
-        if (seg == 0) B.GL[pp] = tot;
-        // Kh = Gamma_L^{-T} K-: per-channel 1/G (diag) or z_L/|z_L|^2 (rotation)
-        f32x2 ig;
+        if (seg == 0) A.GL[pp] = tot;
+        f32x2 ig;   // Gamma_L^{-T} per channel (pair)
         if constexpr (DECAY == 0) {
           ig = f32x2{__builtin_amdgcn_rcpf(tot.x), __builtin_amdgcn_rcpf(tot.y)};
         } else {
@@ -256,9 +284,7 @@ __global__ __launch_bounds__((NWP + TV / 16) * 64) void gdr_fwd_pipe_kernel(FwdP
           for (int u = 0; u < 4; ++u) {
             const int r = r4 + u;
             const int row = seg * TPS + r;
-            const bool ok = c0 + row < Tn;
-            f32x2 kx = bf2_to_f2(R.k[r]), qx = bf2_to_f2(R.q[r]);
-            if (!ok) kx = qx = f32x2{0.f, 0.f};
+            const f32x2 kx = bf2_to_f2(R.k[r]), qx = bf2_to_f2(R.q[r]);
             f32x2 kp, qp, km, kh;
             if constexpr (DECAY == 0) {
               const f32x2 gf = {pre.x * cf[r].x, pre.y * cf[r].y};
@@ -275,97 +301,102 @@ __global__ __launch_bounds__((NWP + TV / 16) * 64) void gdr_fwd_pipe_kernel(FwdP
               km = cmul(conj(zb), kx);
               kh = cmul(ig, km);
             }
-            *(uint32_t*)(B.Kp + row * RSK + 2 * pp) = f2_to_bf2(kp);
-            *(uint32_t*)(B.Qp + row * RSK + 2 * pp) = f2_to_bf2(qp);
-            *(uint32_t*)(sh.Kh + row * RSK + 2 * pp) = f2_to_bf2(kh);
+            *(uint32_t*)(A.Kp + row * RSK + 2 * pp) = f2_to_bf2(kp);
+            *(uint32_t*)(A.Qp + row * RSK + 2 * pp) = f2_to_bf2(qp);
+            *(uint32_t*)(Kh + row * RSK + 2 * pp) = f2_to_bf2(kh);
             km0[u] = km.x;
             km1[u] = km.y;
           }
           const int col = seg * TPS + r4;
-          bf16x4 v0v, v1v;
+          bf16x4 m0, m1;
 #pragma unroll
           for (int u = 0; u < 4; ++u) {
-            v0v[u] = (bf)km0[u];
-            v1v[u] = (bf)km1[u];
+            m0[u] = (bf)km0[u];
+            m1[u] = (bf)km1[u];
           }
-          *(bf16x4*)(B.KmT + (2 * pp) * RSL + col) = v0v;
-          *(bf16x4*)(B.KmT + (2 * pp + 1) * RSL + col) = v1v;
+          *(bf16x4*)(A.KmT + (2 * pp) * RSL + col) = m0;
+          *(bf16x4*)(A.KmT + (2 * pp + 1) * RSL + col) = m1;
         }
+        if (it + 1 < nchunks) load_raw<DK, TV, DECAY>(R, rs, c0 + L, pp, seg, ptid);
       }
-      if (j + 1 < nchunks) load_raw<DK, TV, DECAY>(R, p, c0 + L, pp, seg, ptid, b, h, v0);
-      __syncthreads();
-      // ---- phase 3: Gram tiles and the diagonal inverse blocks
-      if (wv == 0) {
+      lds_barrier();
+    }
+  } else if (wv < NWP + NWS) {
+    // ================================================================ solve
+    const int sw = wv - NWP;
+    for (int it = 0; it < nsteps; ++it) {
+      const int j = it - 1;
+      if (j >= 0 && j < nchunks) {
+        const SlotA<DK, TV>& A = sh.a[j % 3];
+        const bf* Kh = sh.Kh[j & 1];
+        SlotS& S = sh.s[j & 1];
+        if (sw < 2) {
+          // diagonal block bb: N and N^T as accumulator tiles, then
+          // T_bb = (I + N)^{-1} = (I - N)(I + N^2)(I + N^4)(I + N^8).
+          // mul(Q, Y) = C(Q^T Y): a tile feeds the left operand as its transpose.
+          const int bb = sw;
+          f32x4 g0 = {0.f, 0.f, 0.f, 0.f}, g1 = {0.f, 0.f, 0.f, 0.f};
 #pragma unroll
-        for (int bb = 0; bb < 2; ++bb) {
-          f32x4 acc = {0.f, 0.f, 0.f, 0.f};
-#pragma unroll
-          for (int kk = 0; kk < NKC; ++kk)
-            O::mma(acc, load_plain<bf>(B.Kp, RSK, 16 * bb, 32 * kk),
-                   load_plain<bf>(sh.Kh, RSK, 16 * bb, 32 * kk));
+          for (int kk = 0; kk < NKC; ++kk) {
+            const frag kp = load_plain<bf>(A.Kp, RSK, 16 * bb, 32 * kk);
+            const frag kh = load_plain<bf>(Kh, RSK, 16 * bb, 32 * kk);
+            O::mma(g0, kp, kh);   // (K+ Kh^T)[4g+j][n]
+            O::mma(g1, kh, kp);   // (K+ Kh^T)[n][4g+j]
+          }
+          f32x4 Nc, Nt, Pt;
+          const float bn = A.beta[16 * bb + n];
 #pragma unroll
           for (int jj = 0; jj < 4; ++jj) {
             const int rr = 4 * g + jj;
-            sh.Ad[(bb * 16 + rr) * 17 + n] = (n < rr) ? B.beta[16 * bb + rr] * acc[jj] : 0.f;
+            Nc[jj] = (n < rr) ? A.beta[16 * bb + rr] * g0[jj] : 0.f;   // N[rr][n]
+            Nt[jj] = (rr < n) ? bn * g1[jj] : 0.f;                     // N[n][rr]
+            Pt[jj] = ((rr == n) ? 1.f : 0.f) - Nt[jj];                  // (I - N)^T
           }
-        }
-        __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
-        __builtin_amdgcn_wave_barrier();
-        __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
-        if (l < 32) {
-          const int bb = l >> 4, cc = l & 15;
-          const float* Ab = sh.Ad + bb * 16 * 17;
-          float tcol[16];
+          auto mul = [](const f32x4& Q, const f32x4& Y) {
+            f32x4 z = {0.f, 0.f, 0.f, 0.f};
+            O::mma(z, O::from_acc_half(Q), O::from_acc_half(Y));
+            return z;
+          };
+          const f32x4 N2 = mul(Nt, Nc), N2t = mul(Nc, Nt);
+          const f32x4 N4 = mul(N2t, N2), N4t = mul(N2, N2t);
+          const f32x4 N8 = mul(N4t, N4);
+          Pt += mul(N2, Pt);
+          Pt += mul(N4, Pt);
+          Pt += mul(N8, Pt);   // T^T: lane holds T[n][4g..4g+3]
+          bf16x4 tv;
 #pragma unroll
-          for (int i = 0; i < 16; ++i) {
-            float acc = (i == cc) ? 1.f : 0.f;
+          for (int jj = 0; jj < 4; ++jj) tv[jj] = (bf)Pt[jj];
+          *(bf16x4*)(S.Td + (bb * 16 + n) * RS16 + 4 * g) = tv;
+        } else {
+          // wave 2: A10 and M00; wave 3: M10 and M11
 #pragma unroll
-            for (int jj = 0; jj < i; ++jj) acc -= Ab[i * 17 + jj] * tcol[jj];
-            tcol[i] = acc;
-          }
+          for (int ti = 0; ti < 2; ++ti) {
+            const bool isA = (sw == 2 && ti == 0);
+            const int rb = (sw == 2) ? (ti == 0 ? 1 : 0) : 1;
+            const int cbk = (sw == 3) ? ti : 0;
+            const bf* src = isA ? A.Kp : A.Qp;
+            f32x4 acc = {0.f, 0.f, 0.f, 0.f};
 #pragma unroll
-          for (int i = 0; i < 16; ++i) B.Td[(bb * 16 + i) * RS16 + cc] = (bf)tcol[i];
-        }
-      } else {
-        // wave 1: A10 and M00; wave 2: M10; wave 3: M11
-        const int ntile = (wv == 1) ? 2 : 1;
-        for (int ti = 0; ti < ntile; ++ti) {
-          const int kind = (wv == 1 && ti == 0) ? 0 : 1;          // 0: A10, 1: an M tile
-          const int rb = (wv == 1) ? (ti == 0 ? 1 : 0) : 1;
-          const int cbk = (wv == 3) ? 1 : 0;
-          const bf* src = kind == 0 ? B.Kp : B.Qp;
-          f32x4 acc = {0.f, 0.f, 0.f, 0.f};
+            for (int kk = 0; kk < NKC; ++kk)
+              O::mma(acc, load_plain<bf>(src, RSK, 16 * rb, 32 * kk),
+                     load_plain<bf>(Kh, RSK, 16 * cbk, 32 * kk));
 #pragma unroll
-          for (int kk = 0; kk < NKC; ++kk)
-            O::mma(acc, load_plain<bf>(src, RSK, 16 * rb, 32 * kk),
-                   load_plain<bf>(sh.Kh, RSK, 16 * cbk, 32 * kk));
-#pragma unroll
-          for (int jj = 0; jj < 4; ++jj) {
-            const int rr = 16 * rb + 4 * g + jj, cc = 16 * cbk + n;
-            if (kind == 0) {
-              B.A10[(4 * g + jj) * RS16 + n] = (bf)(B.beta[rr] * acc[jj]);
-            } else {
-              B.M[rr * RSL + cc] = (bf)((cc <= rr) ? acc[jj] : 0.f);
+            for (int jj = 0; jj < 4; ++jj) {
+              const int rr = 16 * rb + 4 * g + jj, cc = 16 * cbk + n;
+              if (isA) {
+                S.A10[(4 * g + jj) * RS16 + n] = (bf)(A.beta[rr] * acc[jj]);
+              } else {
+                S.M[rr * RSL + cc] = (bf)((cc <= rr) ? acc[jj] : 0.f);
+              }
             }
           }
         }
       }
-      __syncthreads();
-    };
-
-    produce(0);
-    for (int i = 0; i < nchunks; ++i) {
-      if (i + 1 < nchunks) {
-        produce(i + 1);
-      } else {
-        __syncthreads();
-        __syncthreads();
-        __syncthreads();
-      }
+      lds_barrier();
     }
   } else {
-    // =============================================================== consumer
-    const int cw = wv - NWP;                    // value block of 16 channels
+    // ============================================================ consumer
+    const int cw = wv - NWP - NWS;              // value block of 16 channels
     f32x4 Sacc[NCT];
     const size_t srow = ((size_t)(b * H + h) * DV + v0 + 16 * cw + n) * DK;
     if (p.S0) {
@@ -375,70 +406,79 @@ __global__ __launch_bounds__((NWP + TV / 16) * 64) void gdr_fwd_pipe_kernel(FwdP
 #pragma unroll
       for (int ct = 0; ct < NCT; ++ct) Sacc[ct] = f32x4{0.f, 0.f, 0.f, 0.f};
     }
-    bf* go = (bf*)p.o;
-    __syncthreads();   // prologue: chunk 0 is being prepared
-    __syncthreads();
-    __syncthreads();
-    for (int i = 0; i < nchunks; ++i) {
-      const Buf<DK, TV>& B = sh.buf[i & 1];
-      const int c0 = i * L;
-      // ---- phase 1: R = diag(bw) V - diag(beta) K+ S^T, Qs = Q+ S^T
-      frag Sf[NKC];
+    // o through a buffer resource over this wave's 16 value channels of (b, h):
+    // stores past token T-1 fall outside the resource and are dropped.
+    const size_t obh = (size_t)b * Tn * H + h;
+    const size_t orows = (size_t)(Tn - 1) * H + 1;
+    const int ocol = v0 + 16 * cw;
+    const rsrc_t ro = make_rsrc((bf*)p.o + obh * DV + ocol, orows * DV * 2 - (size_t)ocol * 2);
+    const int so = H * DV * 2;                     // bytes per token row
+    const int olane = (4 * g) * so + 2 * n;
+    for (int it = 0; it < nsteps; ++it) {
+      const int i = it - 2;
+      if (i >= 0) {
+        const SlotA<DK, TV>& A = sh.a[i % 3];
+        const SlotS& S = sh.s[i & 1];
+        const int c0 = i * L;
+        // R = diag(bw) V - diag(beta) K+ S^T, Qs = Q+ S^T
+        frag Sf[NKC];
 #pragma unroll
-      for (int kk = 0; kk < NKC; ++kk) Sf[kk] = O::from_acc(Sacc[2 * kk], Sacc[2 * kk + 1]);
-      f32x4 Rt[2], Qs[2];
+        for (int kk = 0; kk < NKC; ++kk) Sf[kk] = O::from_acc(Sacc[2 * kk], Sacc[2 * kk + 1]);
+        f32x4 Rt[2], Qs[2];
 #pragma unroll
-      for (int t = 0; t < 2; ++t) {
-        f32x4 P = {0.f, 0.f, 0.f, 0.f}, Q = {0.f, 0.f, 0.f, 0.f};
+        for (int t = 0; t < 2; ++t) {
+          f32x4 P = {0.f, 0.f, 0.f, 0.f}, Q = {0.f, 0.f, 0.f, 0.f};
 #pragma unroll
-        for (int kk = 0; kk < NKC; ++kk) {
-          O::mma(P, load_cb<bf>(B.Kp, RSK, 16 * t, 32 * kk), Sf[kk]);
-          O::mma(Q, load_cb<bf>(B.Qp, RSK, 16 * t, 32 * kk), Sf[kk]);
+          for (int kk = 0; kk < NKC; ++kk) {
+            O::mma(P, load_cb<bf>(A.Kp, RSK, 16 * t, 32 * kk), Sf[kk]);
+            O::mma(Q, load_cb<bf>(A.Qp, RSK, 16 * t, 32 * kk), Sf[kk]);
+          }
+#pragma unroll
+          for (int jj = 0; jj < 4; ++jj) {
+            const int r = 16 * t + 4 * g + jj;
+            Rt[t][jj] = A.bw[r] * (float)A.V[r * RSV + 16 * cw + n] - A.beta[r] * P[jj];
+          }
+          Qs[t] = Q;
         }
+        // Dl by blocks, O = Qs + M Dl
+        f32x4 D0 = {0.f, 0.f, 0.f, 0.f}, D1 = {0.f, 0.f, 0.f, 0.f};
+        O::mma(D0, load_cb_half<bf>(S.Td, RS16, 0, 0), O::from_acc_half(Rt[0]));
+        f32x4 Y = Rt[1];
+        O::mma(Y, O::neg(load_cb_half<bf>(S.A10, RS16, 0, 0)), O::from_acc_half(D0));
+        O::mma(D1, load_cb_half<bf>(S.Td + 16 * RS16, RS16, 0, 0), O::from_acc_half(Y));
+        const frag Df = O::from_acc(D0, D1);
+        f32x4 O0 = Qs[0], O1 = Qs[1];
+        O::mma(O0, load_cb_half<bf>(S.M, RSL, 0, 0), O::from_acc_half(D0));
+        O::mma(O1, load_cb<bf>(S.M, RSL, 16, 0), Df);
+        {
+          const int ob = olane + c0 * so;
 #pragma unroll
-        for (int jj = 0; jj < 4; ++jj) {
-          const int r = 16 * t + 4 * g + jj;
-          Rt[t][jj] = B.bw[r] * (float)B.V[r * RSV + 16 * cw + n] - B.beta[r] * P[jj];
-        }
-        Qs[t] = Q;
-      }
-      __syncthreads();
-      // ---- phase 2: Dl by blocks, O = Qs + M Dl, store o
-      f32x4 D0 = {0.f, 0.f, 0.f, 0.f}, D1 = {0.f, 0.f, 0.f, 0.f};
-      O::mma(D0, load_cb_half<bf>(B.Td, RS16, 0, 0), O::from_acc_half(Rt[0]));
-      f32x4 Y = Rt[1];
-      O::mma(Y, O::neg(load_cb_half<bf>(B.A10, RS16, 0, 0)), O::from_acc_half(D0));
-      O::mma(D1, load_cb_half<bf>(B.Td + 16 * RS16, RS16, 0, 0), O::from_acc_half(Y));
-      const frag Df = O::from_acc(D0, D1);
-      f32x4 O0 = Qs[0], O1 = Qs[1];
-      O::mma(O0, load_cb_half<bf>(B.M, RSL, 0, 0), O::from_acc_half(D0));
-      O::mma(O1, load_cb<bf>(B.M, RSL, 16, 0), Df);
-#pragma unroll
-      for (int jj = 0; jj < 4; ++jj) {
-        const int t0 = c0 + 4 * g + jj, t1 = t0 + 16;
-        const int col = v0 + 16 * cw + n;
-        if (t0 < Tn) go[((size_t)(b * Tn + t0) * H + h) * DV + col] = (bf)O0[jj];
-        if (t1 < Tn) go[((size_t)(b * Tn + t1) * H + h) * DV + col] = (bf)O1[jj];
-      }
-      __syncthreads();
-      // ---- phase 3: S <- S Gamma_L + Dl^T K-
-#pragma unroll
-      for (int ct = 0; ct < NCT; ++ct) {
-#pragma unroll
-        for (int jj = 0; jj < 4; jj += 2) {
-          const f32x2 z = B.GL[(16 * ct + 4 * g + jj) >> 1];
-          const float x0 = Sacc[ct][jj], x1 = Sacc[ct][jj + 1];
-          if constexpr (DECAY == 0) {
-            Sacc[ct][jj] = x0 * z.x;
-            Sacc[ct][jj + 1] = x1 * z.y;
-          } else {
-            Sacc[ct][jj] = z.x * x0 + z.y * x1;
-            Sacc[ct][jj + 1] = -z.y * x0 + z.x * x1;
+          for (int jj = 0; jj < 4; ++jj) {
+            const bf x0 = (bf)O0[jj], x1 = (bf)O1[jj];
+            __builtin_amdgcn_raw_buffer_store_b16(*(const unsigned short*)&x0, ro, ob + jj * so, 0, 0);
+            __builtin_amdgcn_raw_buffer_store_b16(*(const unsigned short*)&x1, ro,
+                                                  ob + (16 + jj) * so, 0, 0);
           }
         }
-        O::mma(Sacc[ct], load_cb<bf>(B.KmT, RSL, 16 * ct, 0), Df);
+        // S <- S Gamma_L + Dl^T K-
+#pragma unroll
+        for (int ct = 0; ct < NCT; ++ct) {
+#pragma unroll
+          for (int jj = 0; jj < 4; jj += 2) {
+            const f32x2 z = A.GL[(16 * ct + 4 * g + jj) >> 1];
+            const float x0 = Sacc[ct][jj], x1 = Sacc[ct][jj + 1];
+            if constexpr (DECAY == 0) {
+              Sacc[ct][jj] = x0 * z.x;
+              Sacc[ct][jj + 1] = x1 * z.y;
+            } else {
+              Sacc[ct][jj] = z.x * x0 + z.y * x1;
+              Sacc[ct][jj + 1] = -z.y * x0 + z.x * x1;
+            }
+          }
+          O::mma(Sacc[ct], load_cb<bf>(A.KmT, RSL, 16 * ct, 0), Df);
+        }
       }
-      __syncthreads();
+      lds_barrier();
     }
     if (p.S_out) {
 #pragma unroll

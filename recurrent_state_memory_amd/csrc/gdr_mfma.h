@@ -32,6 +32,15 @@ typedef __attribute__((ext_vector_type(2))) __bf16 bf16x2;
 
 __device__ inline int lane_id() { return threadIdx.x & 63; }
 
+// Workgroup barrier that orders LDS only.  All cross-wave communication in the
+// kernels goes through LDS, so global loads (prefetches) and global stores
+// (outputs) stay in flight across it; __syncthreads() would wait for them.
+__device__ inline void lds_barrier() {
+  __builtin_amdgcn_fence(__ATOMIC_RELEASE, "workgroup", "local");
+  __builtin_amdgcn_s_barrier();
+  __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "workgroup", "local");
+}
+
 template <typename T>
 struct Op;
 
