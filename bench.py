@@ -33,8 +33,9 @@ METRIC = "tokens/sec gated-delta chunk fwd (H=16,d=128,T=4096) + % MFMA/HBM roof
 HBM_PEAK_GBS = 8000.0          # MI355X HBM3E
 MFMA_BF16_PEAK_TFS = 2500.0    # dense bf16 matrix peak
 MFMA_F32_PEAK_TFS = 157.3
-TRAFFIC_FILE = os.path.join(ROOT, "profiles", "gdr_fwd_kernel_layer_traffic.txt")
-KERNEL_SRC = os.path.join(ROOT, "recurrent_state_memory_amd", "csrc", "gdr_fwd.hip")
+TRAFFIC_FILE = os.path.join(ROOT, "profiles", "gdr_fwd_pipe_kernel_layer_traffic.txt")
+KERNEL_SRCS = [os.path.join(ROOT, "recurrent_state_memory_amd", "csrc", f)
+               for f in ("gdr_fwd_pipe.hip", "gdr_mfma.h", "gdr_kernels.h")]
 
 
 def algorithmic_bytes(wl, s0: bool = False) -> int:
@@ -56,13 +57,17 @@ def algorithmic_flops(wl, L: int) -> float:
 
 
 def _kernel_hash() -> str:
-    with open(KERNEL_SRC, "rb") as f:
-        return hashlib.sha256(f.read()).hexdigest()[:16]
+    h = hashlib.sha256()
+    for path in KERNEL_SRCS:
+        with open(path, "rb") as f:
+            h.update(f.read())
+    return h.hexdigest()[:16]
 
 
 def _traffic():
-    """Per-launch HBM bytes from the committed rocprofv3 counter summary, if it
-    was taken on the current kernel source (else None)."""
+    """Per-launch HBM bytes (FETCH_SIZE + WRITE_SIZE, each scaled by what the
+    counter reads for a copy of known size) from the committed rocprofv3
+    summary, if it was taken on the current kernel source (else None)."""
     try:
         vals = {}
         for ln in open(TRAFFIC_FILE):

@@ -501,7 +501,10 @@ hipError_t launch(const FwdParams& p0, hipStream_t s) {
 }  // namespace pipe
 
 bool fwd_pipe_supported(const FwdParams& p) {
-  return p.io_bf16 && p.beta_logit == nullptr && (p.DK == 64 || p.DK == 128) && p.DV == p.DK;
+  // buffer resources address one (b, h) with 32-bit byte offsets
+  const bool fits = (unsigned long long)p.T * p.H * p.DK * 4ull < (1ull << 31);
+  return p.io_bf16 && p.beta_logit == nullptr && (p.DK == 64 || p.DK == 128) && p.DV == p.DK &&
+         fits;
 }
 
 hipError_t launch_fwd_pipe(const FwdParams& p, hipStream_t s) {
