@@ -45,6 +45,15 @@ __device__ inline uint32_t f2_to_bf2(f32x2 x) {
   return *(uint32_t*)&v;
 }
 
+// K+, Q+ and Kh rows store the key channels of each 32-channel block in the
+// order of the "cb" slot map (gdr_mfma.h): position 8g + s holds channel
+// 4g + s (s < 4) or 16 + 4g + s - 4 (s >= 4).  A plain 16-byte fragment read
+// then pairs with a fragment built from two stacked accumulator tiles, and a
+// contraction of two rows stored this way is unchanged.
+__device__ constexpr int cb_pos(int c) {
+  return (c & ~31) + 8 * ((c & 15) >> 2) + (((c & 31) >> 4) << 2) + (c & 3);
+}
+
 constexpr int L = 32;      // tokens per chunk
 constexpr int NWP = 4;     // prep waves
 constexpr int NWS = 4;     // solve waves
@@ -80,6 +89,16 @@ struct SlotA {
   float bw[L];
   f32x2 GL[C::NP];
 };
+
+// 16-byte LDS reads of beta, bw and GL rely on these offsets
+template <int DK, int TV>
+constexpr bool slot_aligned() {
+  using S = SlotA<DK, TV>;
+  return offsetof(S, beta) % 16 == 0 && offsetof(S, bw) % 16 == 0 && offsetof(S, GL) % 16 == 0 &&
+         sizeof(S) % 16 == 0;
+}
+static_assert(slot_aligned<128, 64>() && slot_aligned<128, 32>() && slot_aligned<64, 32>(),
+              "SlotA alignment");
 
 // Solve outputs of one chunk (2 slots).
 struct SlotS {
@@ -145,36 +164,222 @@ __device__ inline Rsrc make_rsrcs(const FwdParams& p, int b, int h, int v0) {
   return r;
 }
 
+// Byte offsets: the per-lane part goes in voffset, the per-token part (uniform)
+// in soffset.  Both count in the range check of a raw buffer (no stride), so
+// tokens at or past T still read as zero.
+// PART 0: value tile, beta, w; 1: key-axis transitions; 2: keys; 3: queries.
+template <int DK, int TV, int DECAY, int PART>
+__device__ inline void load_part(Raw<Cfg<DK, TV>::TPS>& R, const Rsrc& rs, int c0, int pp, int seg,
+                                 int ptid) {
+  using C = Cfg<DK, TV>;
+  if constexpr (PART == 0) {
+    {
+      const int idx = ptid < L * C::VPR ? ptid : 0;
+      const int r = idx / C::VPR, cc = idx % C::VPR;
+      const auto x = __builtin_amdgcn_raw_buffer_load_b128(rs.v, r * rs.sv + cc * 16, c0 * rs.sv, 0);
+      R.v = uint4{x[0], x[1], x[2], x[3]};
+    }
+    const int t = ptid < L ? ptid : L - 1;
+    R.bt = __uint_as_float(__builtin_amdgcn_raw_buffer_load_b32(rs.beta, t * rs.sb, c0 * rs.sb, 0));
+    R.wt = __uint_as_float(__builtin_amdgcn_raw_buffer_load_b32(rs.w, t * rs.sb, c0 * rs.sb, 0));
+  } else if constexpr (PART == 1) {
+    const int al = seg * C::TPS * rs.sa + (DECAY == 0 ? 8 : 4) * pp;
+#pragma unroll
+    for (int r = 0; r < C::TPS; ++r) {
+      const int as = (c0 + r) * rs.sa;   // uniform
+      if constexpr (DECAY == 0) {
+        const auto x = __builtin_amdgcn_raw_buffer_load_b64(rs.a, al, as, 0);
+        R.a[r] = f32x2{__uint_as_float(x[0]), __uint_as_float(x[1])};
+      } else {
+        R.a[r] = f32x2{__uint_as_float(__builtin_amdgcn_raw_buffer_load_b32(rs.a, al, as, 0)),
+                       __uint_as_float(__builtin_amdgcn_raw_buffer_load_b32(rs.th, al, as, 0))};
+      }
+    }
+  } else {
+    const int kl = seg * C::TPS * rs.sk + 4 * pp;
+#pragma unroll
+    for (int r = 0; r < C::TPS; ++r) {
+      const int ks = (c0 + r) * rs.sk;   // uniform
+      if constexpr (PART == 2) R.k[r] = __builtin_amdgcn_raw_buffer_load_b32(rs.k, kl, ks, 0);
+      else R.q[r] = __builtin_amdgcn_raw_buffer_load_b32(rs.q, kl, ks, 0);
+    }
+  }
+}
+
 template <int DK, int TV, int DECAY>
 __device__ inline void load_raw(Raw<Cfg<DK, TV>::TPS>& R, const Rsrc& rs, int c0, int pp, int seg,
                                 int ptid) {
+  load_part<DK, TV, DECAY, 0>(R, rs, c0, pp, seg, ptid);
+  load_part<DK, TV, DECAY, 1>(R, rs, c0, pp, seg, ptid);
+  load_part<DK, TV, DECAY, 2>(R, rs, c0, pp, seg, ptid);
+  load_part<DK, TV, DECAY, 3>(R, rs, c0, pp, seg, ptid);
+}
+
+// One prep step: decayed key/query forms of chunk `it` (raw loads in R) into
+// prep slot it % 3 and the Kh buffer it % 2.  With NEXT, the raw loads of the
+// chunk at token cn go into Rn, spread over the step in four groups so that
+// the prep waves do not all stall on a full memory-instruction queue at the
+// start of every step.
+template <int DK, int TV, int DECAY, bool NEXT>
+__device__ __forceinline__ void prep_chunk(Shared<DK, TV>& sh, const Raw<Cfg<DK, TV>::TPS>& R,
+                                           Raw<Cfg<DK, TV>::TPS>& Rn, const Rsrc& rs, int cn,
+                                           int it, int Tn, int pw, int l, int pl, int seg,
+                                           int pp, int ptid) {
   using C = Cfg<DK, TV>;
-  const int t0 = c0 + seg * C::TPS;
-  const int ko = t0 * rs.sk + 4 * pp;                       // byte offsets of token t0
-  const int ao = t0 * rs.sa + (DECAY == 0 ? 8 : 4) * pp;
+  constexpr int PPW = C::PPW, NSEG = C::NSEG, TPS = C::TPS, RSK = C::RSK, RSV = C::RSV,
+                VPR = C::VPR;
+  SlotA<DK, TV>& A = sh.a[it % 3];
+  bf* Kh = sh.Kh[it & 1];
+  const int c0 = it * L;
+  if constexpr (NEXT) load_part<DK, TV, DECAY, 0>(Rn, rs, cn, pp, seg, ptid);
+  // transitions of this lane's token segment (identity past the end)
+  f32x2 d[TPS];
+  if (c0 + L <= Tn) {
 #pragma unroll
-  for (int r = 0; r < C::TPS; ++r) {
-    const int kr = ko + r * rs.sk, ar = ao + r * rs.sa;     // r * stride is uniform
-    R.k[r] = __builtin_amdgcn_raw_buffer_load_b32(rs.k, kr, 0, 0);
-    R.q[r] = __builtin_amdgcn_raw_buffer_load_b32(rs.q, kr, 0, 0);
-    if constexpr (DECAY == 0) {
-      const auto x = __builtin_amdgcn_raw_buffer_load_b64(rs.a, ar, 0, 0);
-      R.a[r] = f32x2{__uint_as_float(x[0]), __uint_as_float(x[1])};
-    } else {
-      R.a[r] = f32x2{__uint_as_float(__builtin_amdgcn_raw_buffer_load_b32(rs.a, ar, 0, 0)),
-                     __uint_as_float(__builtin_amdgcn_raw_buffer_load_b32(rs.th, ar, 0, 0))};
+    for (int r = 0; r < TPS; ++r) d[r] = R.a[r];
+  } else {
+#pragma unroll
+    for (int r = 0; r < TPS; ++r) {
+      const bool ok = c0 + seg * TPS + r < Tn;
+      d[r].x = ok ? R.a[r].x : 1.f;
+      d[r].y = ok ? R.a[r].y : (DECAY == 0 ? 1.f : 0.f);
     }
   }
-  {
-    const int idx = ptid < L * C::VPR ? ptid : 0;
-    const int r = idx / C::VPR, cc = idx % C::VPR;
-    const auto x = __builtin_amdgcn_raw_buffer_load_b128(rs.v, (c0 + r) * rs.sv + cc * 16, 0, 0);
-    R.v = uint4{x[0], x[1], x[2], x[3]};
+  if constexpr (DECAY != 0) {
+#pragma unroll
+    for (int r = 0; r < TPS; ++r) {   // (gamma, theta) -> gamma e^{i theta}
+      float sn, cs;
+      __sincosf(d[r].y, &sn, &cs);
+      d[r] = f32x2{d[r].x * cs, d[r].x * sn};
+    }
   }
+  auto mulz = [](f32x2 u, f32x2 v) {
+    return (DECAY == 0) ? f32x2{u.x * v.x, u.y * v.y} : cmul(u, v);
+  };
+  const f32x2 one = {1.f, DECAY == 0 ? 1.f : 0.f};
+  if constexpr (NEXT) {
+    __builtin_amdgcn_sched_barrier(0);
+    load_part<DK, TV, DECAY, 1>(Rn, rs, cn, pp, seg, ptid);
+  }
+  f32x2 run = d[0];
+#pragma unroll
+  for (int r = 1; r < TPS; ++r) run = mulz(run, d[r]);
+  sh.segT[pw][l] = run;   // product over this segment
+  if (ptid < L) {   // loads past the sequence returned zero
+    A.beta[ptid] = R.bt;
+    A.bw[ptid] = R.bt * R.wt;
+  }
+  if (ptid < L * VPR) {
+    const int r = ptid / VPR, cc = ptid % VPR;
+    *(uint4*)(A.V + r * RSV + cc * 8) = R.v;
+  }
+  // products over the earlier (pre) and later (post) segments of this
+  // wave's channel pairs; same wave, so no workgroup barrier is needed
+  __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront", "local");
+  __builtin_amdgcn_wave_barrier();
+  __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront", "local");
+  f32x2 pre, post, tot;
+  if constexpr (NSEG == 4) {
+    const f32x2 x0 = sh.segT[pw][pl], x1 = sh.segT[pw][pl + PPW],
+                x2 = sh.segT[pw][pl + 2 * PPW], x3 = sh.segT[pw][pl + 3 * PPW];
+    const f32x2 p2 = mulz(x0, x1), s2 = mulz(x2, x3);
+    pre = seg == 0 ? one : seg == 1 ? x0 : seg == 2 ? p2 : mulz(p2, x2);
+    post = seg == 3 ? one : seg == 2 ? x3 : seg == 1 ? s2 : mulz(x1, s2);
+    tot = mulz(p2, s2);
+  } else {
+    pre = post = tot = one;
+#pragma unroll
+    for (int s2 = 0; s2 < NSEG; ++s2) {
+      const f32x2 x = sh.segT[pw][pl + PPW * s2];
+      if (s2 < seg) pre = mulz(pre, x);
+      if (s2 > seg) post = mulz(post, x);
+      tot = mulz(tot, x);
+    }
+  }
+  if (seg == 0) A.GL[pp] = tot;
+  if constexpr (NEXT) {
+    __builtin_amdgcn_sched_barrier(0);
+    load_part<DK, TV, DECAY, 2>(Rn, rs, cn, pp, seg, ptid);
+  }
+  // running products from the chunk start (gf = Gamma_r) and to its end (gb)
+  f32x2 gfv[TPS], gbv[TPS];
   {
-    const int t = c0 + (ptid < L ? ptid : L - 1);
-    R.bt = __uint_as_float(__builtin_amdgcn_raw_buffer_load_b32(rs.beta, t * rs.sb, 0, 0));
-    R.wt = __uint_as_float(__builtin_amdgcn_raw_buffer_load_b32(rs.w, t * rs.sb, 0, 0));
+    f32x2 rf = pre;
+#pragma unroll
+    for (int r = 0; r < TPS; ++r) {
+      rf = mulz(rf, d[r]);
+      gfv[r] = rf;
+    }
+    f32x2 rb = post;
+#pragma unroll
+    for (int r = TPS - 1; r >= 0; --r) {
+      gbv[r] = rb;
+      rb = mulz(rb, d[r]);
+    }
+  }
+  f32x2 ig;   // Gamma_L^{-T} per channel (pair)
+  if constexpr (DECAY == 0) {
+    ig = f32x2{__builtin_amdgcn_rcpf(tot.x), __builtin_amdgcn_rcpf(tot.y)};
+  } else {
+    const float nz = __builtin_amdgcn_rcpf(tot.x * tot.x + tot.y * tot.y);
+    ig = f32x2{tot.x * nz, tot.y * nz};
+  }
+  const int pc = cb_pos(2 * pp);   // stored position of this channel pair
+  float km0[TPS], km1[TPS];
+#pragma unroll
+  for (int r4 = 0; r4 < TPS; r4 += 4) {
+    if (NEXT && r4 == (TPS > 4 ? 4 : 0)) {
+      __builtin_amdgcn_sched_barrier(0);
+      load_part<DK, TV, DECAY, 3>(Rn, rs, cn, pp, seg, ptid);
+    }
+#pragma unroll
+    for (int u = 0; u < 4; ++u) {
+      const int r = r4 + u;
+      const int row = seg * TPS + r;
+      const f32x2 kx = bf2_to_f2(R.k[r]), qx = bf2_to_f2(R.q[r]);
+      f32x2 kp, qp, km, kh;
+      const f32x2 gf = gfv[r], gb = gbv[r];
+      if constexpr (DECAY == 0) {
+        kp = f32x2{kx.x * gf.x, kx.y * gf.y};
+        qp = f32x2{qx.x * gf.x, qx.y * gf.y};
+        km = f32x2{kx.x * gb.x, kx.y * gb.y};
+        kh = f32x2{km.x * ig.x, km.y * ig.y};
+      } else {
+        kp = cmul(gf, kx);
+        qp = cmul(gf, qx);
+        km = cmul(conj(gb), kx);
+        kh = cmul(ig, km);
+      }
+      *(uint32_t*)(A.Kp + row * RSK + pc) = f2_to_bf2(kp);
+      *(uint32_t*)(A.Qp + row * RSK + pc) = f2_to_bf2(qp);
+      *(uint32_t*)(Kh + row * RSK + pc) = f2_to_bf2(kh);
+      km0[r] = km.x;
+      km1[r] = km.y;
+    }
+  }
+  // K- transposed: one 16-byte store per channel for 8-token segments
+  // (conflict-free at the 18-dword row stride), 8-byte stores otherwise
+  if constexpr (TPS == 8) {
+    bf16x8 m0, m1;
+#pragma unroll
+    for (int u = 0; u < 8; ++u) {
+      m0[u] = (bf)km0[u];
+      m1[u] = (bf)km1[u];
+    }
+    *(bf16x8*)(A.KmT + (2 * pp) * RSL + seg * TPS) = m0;
+    *(bf16x8*)(A.KmT + (2 * pp + 1) * RSL + seg * TPS) = m1;
+  } else {
+#pragma unroll
+    for (int r4 = 0; r4 < TPS; r4 += 4) {
+      bf16x4 m0, m1;
+#pragma unroll
+      for (int u = 0; u < 4; ++u) {
+        m0[u] = (bf)km0[r4 + u];
+        m1[u] = (bf)km1[r4 + u];
+      }
+      *(bf16x4*)(A.KmT + (2 * pp) * RSL + seg * TPS + r4) = m0;
+      *(bf16x4*)(A.KmT + (2 * pp + 1) * RSL + seg * TPS + r4) = m1;
+    }
   }
 }
 
@@ -205,122 +410,32 @@ __global__ __launch_bounds__((NWP + NWS + TV / 16) * 64) void gdr_fwd_pipe_kerne
 
   if (wv < NWP) {
     // ================================================================ prep
+    // Raw loads run one chunk ahead (issued during the step before their use),
+    // in two register sets with the loop unrolled by two.  They are
+    // unconditional (the last chunk is loaded again at the end) so that the
+    // outstanding-load count at every use is known statically.
     const int pw = wv;
     const int pl = l % PPW, seg = l / PPW, pp = pw * PPW + pl;
     const int ptid = tid;                       // 0 .. NWP*64-1
     const Rsrc rs = make_rsrcs<DK, TV, DECAY>(p, b, h, v0);
-    Raw<TPS> R;
-    load_raw<DK, TV, DECAY>(R, rs, 0, pp, seg, ptid);
-    for (int it = 0; it < nsteps; ++it) {
-      if (it < nchunks) {
-        SlotA<DK, TV>& A = sh.a[it % 3];
-        bf* Kh = sh.Kh[it & 1];
-        const int c0 = it * L;
-        // running products inside this lane's token segment
-        f32x2 d[TPS], cf[TPS], cb[TPS];
-#pragma unroll
-        for (int r = 0; r < TPS; ++r) {
-          const bool ok = c0 + seg * TPS + r < Tn;   // identity transition past the end
-          if constexpr (DECAY == 0) {
-            d[r] = ok ? R.a[r] : f32x2{1.f, 1.f};
-          } else {
-            float sn, cs;
-            __sincosf(ok ? R.a[r].y : 0.f, &sn, &cs);
-            const float gm = ok ? R.a[r].x : 1.f;
-            d[r] = f32x2{gm * cs, gm * sn};
-          }
-        }
-        f32x2 run = {1.f, DECAY == 0 ? 1.f : 0.f};
-#pragma unroll
-        for (int r = 0; r < TPS; ++r) {
-          run = (DECAY == 0) ? f32x2{run.x * d[r].x, run.y * d[r].y} : cmul(run, d[r]);
-          cf[r] = run;
-        }
-        f32x2 bk = {1.f, DECAY == 0 ? 1.f : 0.f};
-#pragma unroll
-        for (int r = TPS - 1; r >= 0; --r) {
-          cb[r] = bk;   // product over the later tokens of the segment
-          bk = (DECAY == 0) ? f32x2{bk.x * d[r].x, bk.y * d[r].y} : cmul(bk, d[r]);
-        }
-        sh.segT[pw][l] = run;
-        if (ptid < L) {   // loads past the sequence returned zero
-          A.beta[ptid] = R.bt;
-          A.bw[ptid] = R.bt * R.wt;
-        }
-        if (ptid < L * VPR) {
-          const int r = ptid / VPR, cc = ptid % VPR;
-          *(uint4*)(A.V + r * RSV + cc * 8) = R.v;
-        }
-        // segment products of this wave's channel pairs (same wave: no workgroup barrier)
-        __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront", "local");
-        __builtin_amdgcn_wave_barrier();
-        __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront", "local");
-        f32x2 pre = {1.f, DECAY == 0 ? 1.f : 0.f}, post = pre, tot = pre;
-#pragma unroll
-        for (int s2 = 0; s2 < NSEG; ++s2) {
-          const f32x2 x = sh.segT[pw][pl + PPW * s2];
-          if constexpr (DECAY == 0) {
-            if (s2 < seg) pre = f32x2{pre.x * x.x, pre.y * x.y};
-            if (s2 > seg) post = f32x2{post.x * x.x, post.y * x.y};
-            tot = f32x2{tot.x * x.x, tot.y * x.y};
-          } else {
-            if (s2 < seg) pre = cmul(pre, x);
-            if (s2 > seg) post = cmul(post, x);
-            tot = cmul(tot, x);
-          }
-        }
-        if (seg == 0) A.GL[pp] = tot;
-        f32x2 ig;   // Gamma_L^{-T} per channel (pair)
-        if constexpr (DECAY == 0) {
-          ig = f32x2{__builtin_amdgcn_rcpf(tot.x), __builtin_amdgcn_rcpf(tot.y)};
-        } else {
-          const float nz = __builtin_amdgcn_rcpf(tot.x * tot.x + tot.y * tot.y);
-          ig = f32x2{tot.x * nz, tot.y * nz};
-        }
-#pragma unroll
-        for (int r4 = 0; r4 < TPS; r4 += 4) {
-          float km0[4], km1[4];
-#pragma unroll
-          for (int u = 0; u < 4; ++u) {
-            const int r = r4 + u;
-            const int row = seg * TPS + r;
-            const f32x2 kx = bf2_to_f2(R.k[r]), qx = bf2_to_f2(R.q[r]);
-            f32x2 kp, qp, km, kh;
-            if constexpr (DECAY == 0) {
-              const f32x2 gf = {pre.x * cf[r].x, pre.y * cf[r].y};
-              const f32x2 gb = {cb[r].x * post.x, cb[r].y * post.y};
-              kp = f32x2{kx.x * gf.x, kx.y * gf.y};
-              qp = f32x2{qx.x * gf.x, qx.y * gf.y};
-              km = f32x2{kx.x * gb.x, kx.y * gb.y};
-              kh = f32x2{km.x * ig.x, km.y * ig.y};
-            } else {
-              const f32x2 zf = cmul(pre, cf[r]);
-              const f32x2 zb = cmul(cb[r], post);
-              kp = cmul(zf, kx);
-              qp = cmul(zf, qx);
-              km = cmul(conj(zb), kx);
-              kh = cmul(ig, km);
-            }
-            *(uint32_t*)(A.Kp + row * RSK + 2 * pp) = f2_to_bf2(kp);
-            *(uint32_t*)(A.Qp + row * RSK + 2 * pp) = f2_to_bf2(qp);
-            *(uint32_t*)(Kh + row * RSK + 2 * pp) = f2_to_bf2(kh);
-            km0[u] = km.x;
-            km1[u] = km.y;
-          }
-          const int col = seg * TPS + r4;
-          bf16x4 m0, m1;
-#pragma unroll
-          for (int u = 0; u < 4; ++u) {
-            m0[u] = (bf)km0[u];
-            m1[u] = (bf)km1[u];
-          }
-          *(bf16x4*)(A.KmT + (2 * pp) * RSL + col) = m0;
-          *(bf16x4*)(A.KmT + (2 * pp + 1) * RSL + col) = m1;
-        }
-        if (it + 1 < nchunks) load_raw<DK, TV, DECAY>(R, rs, c0 + L, pp, seg, ptid);
-      }
+    const int clast = (nchunks - 1) * L;
+    Raw<TPS> R0, R1;
+    load_raw<DK, TV, DECAY>(R0, rs, 0, pp, seg, ptid);
+    int it = 0;
+    for (; it + 1 < nchunks; it += 2) {
+      prep_chunk<DK, TV, DECAY, true>(sh, R0, R1, rs, (it + 1) * L, it, Tn, pw, l, pl, seg, pp,
+                                      ptid);
+      lds_barrier();
+      prep_chunk<DK, TV, DECAY, true>(sh, R1, R0, rs, min((it + 2) * L, clast), it + 1, Tn, pw, l,
+                                      pl, seg, pp, ptid);
       lds_barrier();
     }
+    if (it < nchunks) {   // odd chunk count: the last chunk is in R0
+      prep_chunk<DK, TV, DECAY, false>(sh, R0, R1, rs, 0, it, Tn, pw, l, pl, seg, pp, ptid);
+      lds_barrier();
+      ++it;
+    }
+    for (; it < nsteps; ++it) lds_barrier();
   } else if (wv < NWP + NWS) {
     // ================================================================ solve
     const int sw = wv - NWP;
@@ -406,6 +521,9 @@ __global__ __launch_bounds__((NWP + NWS + TV / 16) * 64) void gdr_fwd_pipe_kerne
 #pragma unroll
       for (int ct = 0; ct < NCT; ++ct) Sacc[ct] = f32x4{0.f, 0.f, 0.f, 0.f};
     }
+    // drain the state load here, so that inside the loop only the loop's own
+    // output stores are outstanding and no wait on them is needed
+    __builtin_amdgcn_s_waitcnt(0x0F70);   // vmcnt(0)
     // o through a buffer resource over this wave's 16 value channels of (b, h):
     // stores past token T-1 fall outside the resource and are dropped.
     const size_t obh = (size_t)b * Tn * H + h;
@@ -413,14 +531,15 @@ __global__ __launch_bounds__((NWP + NWS + TV / 16) * 64) void gdr_fwd_pipe_kerne
     const int ocol = v0 + 16 * cw;
     const rsrc_t ro = make_rsrc((bf*)p.o + obh * DV + ocol, orows * DV * 2 - (size_t)ocol * 2);
     const int so = H * DV * 2;                     // bytes per token row
-    const int olane = (4 * g) * so + 2 * n;
+    const int olane = n * so + 8 * g;              // token n, value channels 4g..4g+3
     for (int it = 0; it < nsteps; ++it) {
       const int i = it - 2;
       if (i >= 0) {
         const SlotA<DK, TV>& A = sh.a[i % 3];
         const SlotS& S = sh.s[i & 1];
         const int c0 = i * L;
-        // R = diag(bw) V - diag(beta) K+ S^T, Qs = Q+ S^T
+        // R = diag(bw) V - diag(beta) K+ S^T;  Qs^T = (Q+ S^T)^T, kept transposed
+        // (lane holds one token and four value channels) for 8-byte o stores
         frag Sf[NKC];
 #pragma unroll
         for (int kk = 0; kk < NKC; ++kk) Sf[kk] = O::from_acc(Sacc[2 * kk], Sacc[2 * kk + 1]);
@@ -430,13 +549,15 @@ __global__ __launch_bounds__((NWP + NWS + TV / 16) * 64) void gdr_fwd_pipe_kerne
           f32x4 P = {0.f, 0.f, 0.f, 0.f}, Q = {0.f, 0.f, 0.f, 0.f};
 #pragma unroll
           for (int kk = 0; kk < NKC; ++kk) {
-            O::mma(P, load_cb<bf>(A.Kp, RSK, 16 * t, 32 * kk), Sf[kk]);
-            O::mma(Q, load_cb<bf>(A.Qp, RSK, 16 * t, 32 * kk), Sf[kk]);
+            O::mma(P, load_plain<bf>(A.Kp, RSK, 16 * t, 32 * kk), Sf[kk]);
+            O::mma(Q, Sf[kk], load_plain<bf>(A.Qp, RSK, 16 * t, 32 * kk));
           }
+          const f32x4 bw4 = *(const f32x4*)(A.bw + 16 * t + 4 * g);
+          const f32x4 bt4 = *(const f32x4*)(A.beta + 16 * t + 4 * g);
 #pragma unroll
           for (int jj = 0; jj < 4; ++jj) {
             const int r = 16 * t + 4 * g + jj;
-            Rt[t][jj] = A.bw[r] * (float)A.V[r * RSV + 16 * cw + n] - A.beta[r] * P[jj];
+            Rt[t][jj] = bw4[jj] * (float)A.V[r * RSV + 16 * cw + n] - bt4[jj] * P[jj];
           }
           Qs[t] = Q;
         }
@@ -447,25 +568,24 @@ __global__ __launch_bounds__((NWP + NWS + TV / 16) * 64) void gdr_fwd_pipe_kerne
         O::mma(Y, O::neg(load_cb_half<bf>(S.A10, RS16, 0, 0)), O::from_acc_half(D0));
         O::mma(D1, load_cb_half<bf>(S.Td + 16 * RS16, RS16, 0, 0), O::from_acc_half(Y));
         const frag Df = O::from_acc(D0, D1);
+        // O^T = Qs^T + (M Dl)^T = Qs^T + Dl^T M^T
         f32x4 O0 = Qs[0], O1 = Qs[1];
-        O::mma(O0, load_cb_half<bf>(S.M, RSL, 0, 0), O::from_acc_half(D0));
-        O::mma(O1, load_cb<bf>(S.M, RSL, 16, 0), Df);
+        O::mma(O0, O::from_acc_half(D0), load_cb_half<bf>(S.M, RSL, 0, 0));
+        O::mma(O1, Df, load_cb<bf>(S.M, RSL, 16, 0));
         {
-          const int ob = olane + c0 * so;
-#pragma unroll
-          for (int jj = 0; jj < 4; ++jj) {
-            const bf x0 = (bf)O0[jj], x1 = (bf)O1[jj];
-            __builtin_amdgcn_raw_buffer_store_b16(*(const unsigned short*)&x0, ro, ob + jj * so, 0, 0);
-            __builtin_amdgcn_raw_buffer_store_b16(*(const unsigned short*)&x1, ro,
-                                                  ob + (16 + jj) * so, 0, 0);
-          }
+          const bf16x4 x0 = {(bf)O0[0], (bf)O0[1], (bf)O0[2], (bf)O0[3]};
+          const bf16x4 x1 = {(bf)O1[0], (bf)O1[1], (bf)O1[2], (bf)O1[3]};
+          typedef __attribute__((ext_vector_type(2))) unsigned u32x2;
+          __builtin_amdgcn_raw_buffer_store_b64(*(const u32x2*)&x0, ro, olane, c0 * so, 0);
+          __builtin_amdgcn_raw_buffer_store_b64(*(const u32x2*)&x1, ro, olane, (c0 + 16) * so, 0);
         }
         // S <- S Gamma_L + Dl^T K-
 #pragma unroll
         for (int ct = 0; ct < NCT; ++ct) {
+          const f32x4 z4 = *(const f32x4*)(A.GL + 8 * ct + 2 * g);   // channels 16ct+4g..+3
 #pragma unroll
           for (int jj = 0; jj < 4; jj += 2) {
-            const f32x2 z = A.GL[(16 * ct + 4 * g + jj) >> 1];
+            const f32x2 z = {z4[jj], z4[jj + 1]};
             const float x0 = Sacc[ct][jj], x1 = Sacc[ct][jj + 1];
             if constexpr (DECAY == 0) {
               Sacc[ct][jj] = x0 * z.x;
