@@ -113,7 +113,6 @@ struct Shared {
   SlotA<DK, TV> a[3];
   bf Kh[2][L * C::RSK];
   SlotS s[2];
-  f32x2 segT[NWP][64];
 };
 
 template <int TPS>
@@ -121,7 +120,6 @@ struct Raw {
   uint32_t k[TPS], q[TPS];
   f32x2 a[TPS];
   uint4 v;
-  float bt, wt;
 };
 
 // Buffer resources over one (b, h): element (t, c) of a [B,T,H,X] tensor sits at
@@ -167,7 +165,7 @@ __device__ inline Rsrc make_rsrcs(const FwdParams& p, int b, int h, int v0) {
 // Byte offsets: the per-lane part goes in voffset, the per-token part (uniform)
 // in soffset.  Both count in the range check of a raw buffer (no stride), so
 // tokens at or past T still read as zero.
-// PART 0: value tile, beta, w; 1: key-axis transitions; 2: keys; 3: queries.
+// PART 0: value tile; 1: key-axis transitions; 2: keys; 3: queries.
 template <int DK, int TV, int DECAY, int PART>
 __device__ inline void load_part(Raw<Cfg<DK, TV>::TPS>& R, const Rsrc& rs, int c0, int pp, int seg,
                                  int ptid) {
@@ -179,9 +177,6 @@ __device__ inline void load_part(Raw<Cfg<DK, TV>::TPS>& R, const Rsrc& rs, int c
       const auto x = __builtin_amdgcn_raw_buffer_load_b128(rs.v, r * rs.sv + cc * 16, c0 * rs.sv, 0);
       R.v = uint4{x[0], x[1], x[2], x[3]};
     }
-    const int t = ptid < L ? ptid : L - 1;
-    R.bt = __uint_as_float(__builtin_amdgcn_raw_buffer_load_b32(rs.beta, t * rs.sb, c0 * rs.sb, 0));
-    R.wt = __uint_as_float(__builtin_amdgcn_raw_buffer_load_b32(rs.w, t * rs.sb, c0 * rs.sb, 0));
   } else if constexpr (PART == 1) {
     const int al = seg * C::TPS * rs.sa + (DECAY == 0 ? 8 : 4) * pp;
 #pragma unroll
@@ -215,11 +210,30 @@ __device__ inline void load_raw(Raw<Cfg<DK, TV>::TPS>& R, const Rsrc& rs, int c0
   load_part<DK, TV, DECAY, 3>(R, rs, c0, pp, seg, ptid);
 }
 
+// Value held by lane l ^ (PPW * d) (d = 1, 2, 4; PPW * d in {8, 16, 32}):
+// a row rotation by 8 within rows of 16 lanes, or the gfx950 lane swaps, which
+// return rows (v0, v0, v2, v2) and (v1, v1, v3, v3) for 16 and
+// (v0, v1, v0, v1) and (v2, v3, v2, v3) for 32.
+template <int PPW>
+__device__ inline float xor_lanes(float v, int d, int l) {
+  const int dist = PPW * d;
+  const unsigned u = __float_as_uint(v);
+  if (dist == 8) {
+    return __uint_as_float(__builtin_amdgcn_mov_dpp(u, 0x128, 0xf, 0xf, false));   // row_ror:8
+  } else if (dist == 16) {
+    const auto e = __builtin_amdgcn_permlane16_swap(u, u, false, false);
+    return __uint_as_float((l & 16) ? e[0] : e[1]);
+  } else {
+    const auto e = __builtin_amdgcn_permlane32_swap(u, u, false, false);
+    return __uint_as_float((l & 32) ? e[0] : e[1]);
+  }
+}
+
 // One prep step: decayed key/query forms of chunk `it` (raw loads in R) into
 // prep slot it % 3 and the Kh buffer it % 2.  With NEXT, the raw loads of the
 // chunk at token cn go into Rn, spread over the step in four groups so that
-// the prep waves do not all stall on a full memory-instruction queue at the
-// start of every step.
+// the prep waves do not all stall on a full vector-memory queue at the start
+// of every step.
 template <int DK, int TV, int DECAY, bool NEXT>
 __device__ __forceinline__ void prep_chunk(Shared<DK, TV>& sh, const Raw<Cfg<DK, TV>::TPS>& R,
                                            Raw<Cfg<DK, TV>::TPS>& Rn, const Rsrc& rs, int cn,
@@ -264,37 +278,22 @@ __device__ __forceinline__ void prep_chunk(Shared<DK, TV>& sh, const Raw<Cfg<DK,
   f32x2 run = d[0];
 #pragma unroll
   for (int r = 1; r < TPS; ++r) run = mulz(run, d[r]);
-  sh.segT[pw][l] = run;   // product over this segment
-  if (ptid < L) {   // loads past the sequence returned zero
-    A.beta[ptid] = R.bt;
-    A.bw[ptid] = R.bt * R.wt;
-  }
   if (ptid < L * VPR) {
     const int r = ptid / VPR, cc = ptid % VPR;
     *(uint4*)(A.V + r * RSV + cc * 8) = R.v;
   }
-  // products over the earlier (pre) and later (post) segments of this
-  // wave's channel pairs; same wave, so no workgroup barrier is needed
-  __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront", "local");
-  __builtin_amdgcn_wave_barrier();
-  __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront", "local");
-  f32x2 pre, post, tot;
-  if constexpr (NSEG == 4) {
-    const f32x2 x0 = sh.segT[pw][pl], x1 = sh.segT[pw][pl + PPW],
-                x2 = sh.segT[pw][pl + 2 * PPW], x3 = sh.segT[pw][pl + 3 * PPW];
-    const f32x2 p2 = mulz(x0, x1), s2 = mulz(x2, x3);
-    pre = seg == 0 ? one : seg == 1 ? x0 : seg == 2 ? p2 : mulz(p2, x2);
-    post = seg == 3 ? one : seg == 2 ? x3 : seg == 1 ? s2 : mulz(x1, s2);
-    tot = mulz(p2, s2);
-  } else {
-    pre = post = tot = one;
+  // products over the earlier (pre) and later (post) segments of this lane's
+  // channel pair, and over the whole chunk (tot): a butterfly over the NSEG
+  // segments (lanes PPW apart) with cross-lane swaps; every factor is a
+  // diagonal or 2x2-rotation transition, so the products commute
+  f32x2 pre = one, post = one, tot = run;
 #pragma unroll
-    for (int s2 = 0; s2 < NSEG; ++s2) {
-      const f32x2 x = sh.segT[pw][pl + PPW * s2];
-      if (s2 < seg) pre = mulz(pre, x);
-      if (s2 > seg) post = mulz(post, x);
-      tot = mulz(tot, x);
-    }
+  for (int d = 1; d < NSEG; d *= 2) {
+    const f32x2 tp = {xor_lanes<PPW>(tot.x, d, l), xor_lanes<PPW>(tot.y, d, l)};
+    const bool upper = (seg & d) != 0;   // partner block holds earlier segments
+    pre = mulz(pre, upper ? tp : one);
+    post = mulz(post, upper ? one : tp);
+    tot = mulz(tot, tp);
   }
   if (seg == 0) A.GL[pp] = tot;
   if constexpr (NEXT) {
@@ -439,7 +438,28 @@ __global__ __launch_bounds__((NWP + NWS + TV / 16) * 64) void gdr_fwd_pipe_kerne
   } else if (wv < NWP + NWS) {
     // ================================================================ solve
     const int sw = wv - NWP;
+    // the last solve wave also stages beta and beta*w: loads one chunk ahead,
+    // written into the prep slot of the chunk being prepared in this step
+    // (tokens at or past T read as zero)
+    const rsrc_t rb = make_rsrc(p.beta + ((size_t)b * Tn * H + h), ((size_t)(Tn - 1) * H + 1) * 4);
+    const rsrc_t rw = make_rsrc(p.w + ((size_t)b * Tn * H + h), ((size_t)(Tn - 1) * H + 1) * 4);
+    const int tb = (l < L ? l : L - 1) * H * 4;
+    float nbt = 0.f, nwt = 0.f;
+    if (sw == NWS - 1) {
+      nbt = __uint_as_float(__builtin_amdgcn_raw_buffer_load_b32(rb, tb, 0, 0));
+      nwt = __uint_as_float(__builtin_amdgcn_raw_buffer_load_b32(rw, tb, 0, 0));
+    }
     for (int it = 0; it < nsteps; ++it) {
+      if (sw == NWS - 1 && it < nchunks) {
+        const float bt = nbt, wt = nwt;
+        const int cn = min(it + 1, nchunks - 1) * L * H * 4;   // uniform
+        nbt = __uint_as_float(__builtin_amdgcn_raw_buffer_load_b32(rb, tb, cn, 0));
+        nwt = __uint_as_float(__builtin_amdgcn_raw_buffer_load_b32(rw, tb, cn, 0));
+        if (l < L) {
+          sh.a[it % 3].beta[l] = bt;
+          sh.a[it % 3].bw[l] = bt * wt;
+        }
+      }
       const int j = it - 1;
       if (j >= 0 && j < nchunks) {
         const SlotA<DK, TV>& A = sh.a[j % 3];

@@ -35,14 +35,10 @@ __device__ inline int lane_id() { return threadIdx.x & 63; }
 // Workgroup barrier that orders LDS only.  All cross-wave communication in the
 // kernels goes through LDS, so global loads (prefetches) and global stores
 // (outputs) stay in flight across it; __syncthreads() would wait for them.
-// The scheduler may not move any instruction across it either: work sunk past
-// the barrier would delay the next step's dependent chain.
 __device__ inline void lds_barrier() {
-  __builtin_amdgcn_sched_barrier(0);
   __builtin_amdgcn_fence(__ATOMIC_RELEASE, "workgroup", "local");
   __builtin_amdgcn_s_barrier();
   __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "workgroup", "local");
-  __builtin_amdgcn_sched_barrier(0);
 }
 
 template <typename T>
