@@ -8,6 +8,9 @@ default workload is the 1.3B-scale mixer layer: B=8, H=16, T=4096,
 d_k = d_v = 128, chunk 64, bf16 q/k/v, fp32 gates and fp32 state, synthetic
 seeded inputs.  A token is one (b, t) position covering all H heads.
 
+The default warm-up (150 steps, about 30 ms of back-to-back work on the
+layer workload) lets the GPU clock settle before the 200 timed steps.
+
 Prints one JSON line with the throughput, a roofline object for the forward
 kernel (algorithmic bytes per launch / measured launch time, against the HBM
 peak) and a CPU baseline: the fp64 oracle timed on a bounded sample of the
@@ -175,8 +178,8 @@ def cpu_baseline(wl, x, budget_s: float = 15.0):
 def main(argv=None):
     ap = argparse.ArgumentParser()
     ap.add_argument("--gpus", type=int, default=1)
-    ap.add_argument("--steps", type=int, default=50)
-    ap.add_argument("--warmup", type=int, default=5)
+    ap.add_argument("--steps", type=int, default=200)
+    ap.add_argument("--warmup", type=int, default=150)
     ap.add_argument("--workload", default="layer",
                     choices=["layer", "small", "rot", "long", "tiny", "decode", "copy"])
     ap.add_argument("--no-cpu-baseline", action="store_true")
