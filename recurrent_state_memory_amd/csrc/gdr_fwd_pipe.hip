@@ -8,7 +8,7 @@
 //   prep waves (4), chunk i+2: load the chunk (issued one chunk ahead),
 //     running products of the key-axis transitions (forward and backward,
 //     scanned across token segments inside each wave), decayed forms
-//     K+ = g_r k, Q+ = g_r q, K- = h_r^T k, Kh = Gamma_L^{-T} K-.
+//     K+ = g_r k, Q+ = g_r q and Kh = Gamma_L^{-T} K- with K- = h_r^T k.
 //   solve waves (4), chunk i+1: Gram tiles A = strict_lower(diag(beta) K+ Kh^T)
 //     and M = lower_incl(Q+ Kh^T), and the two 16x16 diagonal blocks T00, T11
 //     of (I + A)^{-1} as the nilpotent product (I - N)(I + N^2)(I + N^4)(I + N^8)
@@ -16,7 +16,7 @@
 //   consumer waves (one per 16 value channels), chunk i:
 //     R  = diag(beta w) V - diag(beta) K+ S^T
 //     Dl = (I + A)^{-1} R by blocks: Dl0 = T00 R0, Dl1 = T11 (R1 - A10 Dl0)
-//     O  = Q+ S^T + M Dl,   S <- S Gamma_L + Dl^T K-.
+//     O  = Q+ S^T + M Dl,   S <- S Gamma_L + Dl^T K- = (S + Dl^T Kh) Gamma_L.
 //
 // g_r = prod_{s<=r} D_s and h_r = prod_{s>r} D_s inside the chunk, so only one
 // reciprocal per key channel (of Gamma_L) is needed; for 2x2 rotation-decay
@@ -83,7 +83,7 @@ struct SlotA {
   using C = Cfg<DK, TV>;
   bf Kp[L * C::RSK];
   bf Qp[L * C::RSK];
-  bf KmT[DK * RSL];
+  bf KhT[DK * RSL];
   bf V[L * C::RSV];
   float beta[L];
   float bw[L];
@@ -300,22 +300,6 @@ __device__ __forceinline__ void prep_chunk(Shared<DK, TV>& sh, const Raw<Cfg<DK,
     __builtin_amdgcn_sched_barrier(0);
     load_part<DK, TV, DECAY, 2>(Rn, rs, cn, pp, seg, ptid);
   }
-  // running products from the chunk start (gf = Gamma_r) and to its end (gb)
-  f32x2 gfv[TPS], gbv[TPS];
-  {
-    f32x2 rf = pre;
-#pragma unroll
-    for (int r = 0; r < TPS; ++r) {
-      rf = mulz(rf, d[r]);
-      gfv[r] = rf;
-    }
-    f32x2 rb = post;
-#pragma unroll
-    for (int r = TPS - 1; r >= 0; --r) {
-      gbv[r] = rb;
-      rb = mulz(rb, d[r]);
-    }
-  }
   f32x2 ig;   // Gamma_L^{-T} per channel (pair)
   if constexpr (DECAY == 0) {
     ig = f32x2{__builtin_amdgcn_rcpf(tot.x), __builtin_amdgcn_rcpf(tot.y)};
@@ -323,8 +307,25 @@ __device__ __forceinline__ void prep_chunk(Shared<DK, TV>& sh, const Raw<Cfg<DK,
     const float nz = __builtin_amdgcn_rcpf(tot.x * tot.x + tot.y * tot.y);
     ig = f32x2{tot.x * nz, tot.y * nz};
   }
+  // running products from the chunk start (gf = Gamma_r) and, for Kh, the
+  // product to the chunk end times Gamma_L^{-T} (hb = Gamma_L^{-T} h_r^T)
+  f32x2 gfv[TPS], hbv[TPS];
+  {
+    f32x2 rf = pre;
+#pragma unroll
+    for (int r = 0; r < TPS; ++r) {
+      rf = mulz(rf, d[r]);
+      gfv[r] = rf;
+    }
+    f32x2 rb = (DECAY == 0) ? mulz(post, ig) : cmul(ig, conj(post));
+#pragma unroll
+    for (int r = TPS - 1; r >= 0; --r) {
+      hbv[r] = rb;
+      rb = (DECAY == 0) ? mulz(rb, d[r]) : cmul(rb, conj(d[r]));
+    }
+  }
   const int pc = cb_pos(2 * pp);   // stored position of this channel pair
-  float km0[TPS], km1[TPS];
+  float kh0[TPS], kh1[TPS];
 #pragma unroll
   for (int r4 = 0; r4 < TPS; r4 += 4) {
     if (NEXT && r4 == (TPS > 4 ? 4 : 0)) {
@@ -336,48 +337,46 @@ __device__ __forceinline__ void prep_chunk(Shared<DK, TV>& sh, const Raw<Cfg<DK,
       const int r = r4 + u;
       const int row = seg * TPS + r;
       const f32x2 kx = bf2_to_f2(R.k[r]), qx = bf2_to_f2(R.q[r]);
-      f32x2 kp, qp, km, kh;
-      const f32x2 gf = gfv[r], gb = gbv[r];
+      f32x2 kp, qp, kh;
+      const f32x2 gf = gfv[r], hb = hbv[r];
       if constexpr (DECAY == 0) {
         kp = f32x2{kx.x * gf.x, kx.y * gf.y};
         qp = f32x2{qx.x * gf.x, qx.y * gf.y};
-        km = f32x2{kx.x * gb.x, kx.y * gb.y};
-        kh = f32x2{km.x * ig.x, km.y * ig.y};
+        kh = f32x2{kx.x * hb.x, kx.y * hb.y};
       } else {
         kp = cmul(gf, kx);
         qp = cmul(gf, qx);
-        km = cmul(conj(gb), kx);
-        kh = cmul(ig, km);
+        kh = cmul(hb, kx);
       }
       *(uint32_t*)(A.Kp + row * RSK + pc) = f2_to_bf2(kp);
       *(uint32_t*)(A.Qp + row * RSK + pc) = f2_to_bf2(qp);
       *(uint32_t*)(Kh + row * RSK + pc) = f2_to_bf2(kh);
-      km0[r] = km.x;
-      km1[r] = km.y;
+      kh0[r] = kh.x;
+      kh1[r] = kh.y;
     }
   }
-  // K- transposed: one 16-byte store per channel for 8-token segments
+  // Kh transposed: one 16-byte store per channel for 8-token segments
   // (conflict-free at the 18-dword row stride), 8-byte stores otherwise
   if constexpr (TPS == 8) {
     bf16x8 m0, m1;
 #pragma unroll
     for (int u = 0; u < 8; ++u) {
-      m0[u] = (bf)km0[u];
-      m1[u] = (bf)km1[u];
+      m0[u] = (bf)kh0[u];
+      m1[u] = (bf)kh1[u];
     }
-    *(bf16x8*)(A.KmT + (2 * pp) * RSL + seg * TPS) = m0;
-    *(bf16x8*)(A.KmT + (2 * pp + 1) * RSL + seg * TPS) = m1;
+    *(bf16x8*)(A.KhT + (2 * pp) * RSL + seg * TPS) = m0;
+    *(bf16x8*)(A.KhT + (2 * pp + 1) * RSL + seg * TPS) = m1;
   } else {
 #pragma unroll
     for (int r4 = 0; r4 < TPS; r4 += 4) {
       bf16x4 m0, m1;
 #pragma unroll
       for (int u = 0; u < 4; ++u) {
-        m0[u] = (bf)km0[r4 + u];
-        m1[u] = (bf)km1[r4 + u];
+        m0[u] = (bf)kh0[r4 + u];
+        m1[u] = (bf)kh1[r4 + u];
       }
-      *(bf16x4*)(A.KmT + (2 * pp) * RSL + seg * TPS + r4) = m0;
-      *(bf16x4*)(A.KmT + (2 * pp + 1) * RSL + seg * TPS + r4) = m1;
+      *(bf16x4*)(A.KhT + (2 * pp) * RSL + seg * TPS + r4) = m0;
+      *(bf16x4*)(A.KhT + (2 * pp + 1) * RSL + seg * TPS + r4) = m1;
     }
   }
 }
@@ -599,9 +598,11 @@ __global__ __launch_bounds__((NWP + NWS + TV / 16) * 64) void gdr_fwd_pipe_kerne
           __builtin_amdgcn_raw_buffer_store_b64(*(const u32x2*)&x0, ro, olane, c0 * so, 0);
           __builtin_amdgcn_raw_buffer_store_b64(*(const u32x2*)&x1, ro, olane, (c0 + 16) * so, 0);
         }
-        // S <- S Gamma_L + Dl^T K-
+        // S <- S Gamma_L + Dl^T K- = (S + Dl^T Kh) Gamma_L, since K- = Kh Gamma_L
+        // column-wise (per channel, or per rotation pair)
 #pragma unroll
         for (int ct = 0; ct < NCT; ++ct) {
+          O::mma(Sacc[ct], load_cb<bf>(A.KhT, RSL, 16 * ct, 0), Df);
           const f32x4 z4 = *(const f32x4*)(A.GL + 8 * ct + 2 * g);   // channels 16ct+4g..+3
 #pragma unroll
           for (int jj = 0; jj < 4; jj += 2) {
@@ -615,7 +616,6 @@ __global__ __launch_bounds__((NWP + NWS + TV / 16) * 64) void gdr_fwd_pipe_kerne
               Sacc[ct][jj + 1] = -z.y * x0 + z.x * x1;
             }
           }
-          O::mma(Sacc[ct], load_cb<bf>(A.KmT, RSL, 16 * ct, 0), Df);
         }
       }
       lds_barrier();
