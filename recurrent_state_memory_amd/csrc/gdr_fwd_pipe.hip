@@ -408,28 +408,39 @@ __global__ __launch_bounds__((NWP + NWS + TV / 16) * 64) void gdr_fwd_pipe_kerne
 
   if (wv < NWP) {
     // ================================================================ prep
-    // Raw loads run one chunk ahead (issued during the step before their use),
-    // in two register sets with the loop unrolled by two.  They are
-    // unconditional (the last chunk is loaded again at the end) so that the
-    // outstanding-load count at every use is known statically.
+    // Raw loads run two chunks ahead (issued two steps before their use, which
+    // covers the memory latency under load), in three register sets with the
+    // loop unrolled by three.  They are unconditional (the last chunk is
+    // loaded again at the end) so that the outstanding-load count at every use
+    // is known statically.
     const int pw = wv;
     const int pl = l % PPW, seg = l / PPW, pp = pw * PPW + pl;
     const int ptid = tid;                       // 0 .. NWP*64-1
     const Rsrc rs = make_rsrcs<DK, TV, DECAY>(p, b, h, v0);
     const int clast = (nchunks - 1) * L;
-    Raw<TPS> R0, R1;
+    Raw<TPS> R0, R1, R2;
     load_raw<DK, TV, DECAY>(R0, rs, 0, pp, seg, ptid);
+    load_raw<DK, TV, DECAY>(R1, rs, min(L, clast), pp, seg, ptid);
     int it = 0;
-    for (; it + 1 < nchunks; it += 2) {
-      prep_chunk<DK, TV, DECAY, true>(sh, R0, R1, rs, (it + 1) * L, it, Tn, pw, l, pl, seg, pp,
+    for (; it + 2 < nchunks; it += 3) {
+      prep_chunk<DK, TV, DECAY, true>(sh, R0, R2, rs, (it + 2) * L, it, Tn, pw, l, pl, seg, pp,
                                       ptid);
       lds_barrier();
-      prep_chunk<DK, TV, DECAY, true>(sh, R1, R0, rs, min((it + 2) * L, clast), it + 1, Tn, pw, l,
+      prep_chunk<DK, TV, DECAY, true>(sh, R1, R0, rs, min((it + 3) * L, clast), it + 1, Tn, pw, l,
+                                      pl, seg, pp, ptid);
+      lds_barrier();
+      prep_chunk<DK, TV, DECAY, true>(sh, R2, R1, rs, min((it + 4) * L, clast), it + 2, Tn, pw, l,
                                       pl, seg, pp, ptid);
       lds_barrier();
     }
-    if (it < nchunks) {   // odd chunk count: the last chunk is in R0
-      prep_chunk<DK, TV, DECAY, false>(sh, R0, R1, rs, 0, it, Tn, pw, l, pl, seg, pp, ptid);
+    // one or two chunks left: they are in R0 and R1
+    if (it < nchunks) {
+      prep_chunk<DK, TV, DECAY, false>(sh, R0, R2, rs, 0, it, Tn, pw, l, pl, seg, pp, ptid);
+      lds_barrier();
+      ++it;
+    }
+    if (it < nchunks) {
+      prep_chunk<DK, TV, DECAY, false>(sh, R1, R2, rs, 0, it, Tn, pw, l, pl, seg, pp, ptid);
       lds_barrier();
       ++it;
     }
