@@ -73,8 +73,9 @@ struct Cfg {
   static constexpr int NCT = DK / 16;
   static constexpr int NKC = DK / 32;
   static constexpr int VPR = TV / 8;             // 16-byte pieces per value row
+  static constexpr int VLD = (L * VPR + NWP * 64 - 1) / (NWP * 64);   // per prep thread
   static_assert(TPS % 4 == 0 && TPS >= 4, "prep split");
-  static_assert(L * VPR <= NWP * 64, "value tile load split");
+  static_assert(L * VPR % (NWP * 64) == 0 || L * VPR < NWP * 64, "value tile load split");
 };
 
 // Prep outputs of one chunk (3 slots: written for i+2, read for i+1 and i).
@@ -85,8 +86,8 @@ struct SlotA {
   bf Qp[L * C::RSK];
   bf KhT[DK * RSL];
   bf V[L * C::RSV];
-  float beta[L];
-  float bw[L];
+  float beta[L];   // beta (content-aware: the logit b_x)
+  float bw[L];     // beta * w (content-aware: w)
   f32x2 GL[C::NP];
 };
 
@@ -97,7 +98,8 @@ constexpr bool slot_aligned() {
   return offsetof(S, beta) % 16 == 0 && offsetof(S, bw) % 16 == 0 && offsetof(S, GL) % 16 == 0 &&
          sizeof(S) % 16 == 0;
 }
-static_assert(slot_aligned<128, 64>() && slot_aligned<128, 32>() && slot_aligned<64, 32>(),
+static_assert(slot_aligned<128, 64>() && slot_aligned<128, 32>() && slot_aligned<64, 32>() &&
+                  slot_aligned<128, 128>() && slot_aligned<64, 64>(),
               "SlotA alignment");
 
 // Solve outputs of one chunk (2 slots).
@@ -115,11 +117,11 @@ struct Shared {
   SlotS s[2];
 };
 
-template <int TPS>
+template <int TPS, int VLD>
 struct Raw {
   uint32_t k[TPS], q[TPS];
   f32x2 a[TPS];
-  uint4 v;
+  uint4 v[VLD];
 };
 
 // Buffer resources over one (b, h): element (t, c) of a [B,T,H,X] tensor sits at
@@ -167,15 +169,17 @@ __device__ inline Rsrc make_rsrcs(const FwdParams& p, int b, int h, int v0) {
 // tokens at or past T still read as zero.
 // PART 0: value tile; 1: key-axis transitions; 2: keys; 3: queries.
 template <int DK, int TV, int DECAY, int PART>
-__device__ inline void load_part(Raw<Cfg<DK, TV>::TPS>& R, const Rsrc& rs, int c0, int pp, int seg,
+__device__ inline void load_part(Raw<Cfg<DK, TV>::TPS, Cfg<DK, TV>::VLD>& R, const Rsrc& rs, int c0, int pp, int seg,
                                  int ptid) {
   using C = Cfg<DK, TV>;
   if constexpr (PART == 0) {
-    {
-      const int idx = ptid < L * C::VPR ? ptid : 0;
+#pragma unroll
+    for (int u = 0; u < C::VLD; ++u) {
+      const int idx0 = ptid + u * NWP * 64;
+      const int idx = idx0 < L * C::VPR ? idx0 : 0;
       const int r = idx / C::VPR, cc = idx % C::VPR;
       const auto x = __builtin_amdgcn_raw_buffer_load_b128(rs.v, r * rs.sv + cc * 16, c0 * rs.sv, 0);
-      R.v = uint4{x[0], x[1], x[2], x[3]};
+      R.v[u] = uint4{x[0], x[1], x[2], x[3]};
     }
   } else if constexpr (PART == 1) {
     const int al = seg * C::TPS * rs.sa + (DECAY == 0 ? 8 : 4) * pp;
@@ -202,7 +206,7 @@ __device__ inline void load_part(Raw<Cfg<DK, TV>::TPS>& R, const Rsrc& rs, int c
 }
 
 template <int DK, int TV, int DECAY>
-__device__ inline void load_raw(Raw<Cfg<DK, TV>::TPS>& R, const Rsrc& rs, int c0, int pp, int seg,
+__device__ inline void load_raw(Raw<Cfg<DK, TV>::TPS, Cfg<DK, TV>::VLD>& R, const Rsrc& rs, int c0, int pp, int seg,
                                 int ptid) {
   load_part<DK, TV, DECAY, 0>(R, rs, c0, pp, seg, ptid);
   load_part<DK, TV, DECAY, 1>(R, rs, c0, pp, seg, ptid);
@@ -229,21 +233,21 @@ __device__ inline float xor_lanes(float v, int d, int l) {
   }
 }
 
-// One prep step: decayed key/query forms of chunk `it` (raw loads in R) into
-// prep slot it % 3 and the Kh buffer it % 2.  With NEXT, the raw loads of the
+// One prep step: decayed key/query forms of 32-token block `it` (raw loads in
+// R) into prep slot vs % 3 and the Kh buffer vs % 2 (vs: the block's step).  With NEXT, the raw loads of the
 // chunk at token cn go into Rn, spread over the step in four groups so that
 // the prep waves do not all stall on a full vector-memory queue at the start
 // of every step.
 template <int DK, int TV, int DECAY, bool NEXT>
-__device__ __forceinline__ void prep_chunk(Shared<DK, TV>& sh, const Raw<Cfg<DK, TV>::TPS>& R,
-                                           Raw<Cfg<DK, TV>::TPS>& Rn, const Rsrc& rs, int cn,
-                                           int it, int Tn, int pw, int l, int pl, int seg,
-                                           int pp, int ptid) {
+__device__ __forceinline__ void prep_chunk(Shared<DK, TV>& sh, const Raw<Cfg<DK, TV>::TPS, Cfg<DK, TV>::VLD>& R,
+                                           Raw<Cfg<DK, TV>::TPS, Cfg<DK, TV>::VLD>& Rn, const Rsrc& rs, int cn,
+                                           int it, int vs, int Tn, int pw, int l, int pl,
+                                           int seg, int pp, int ptid) {
   using C = Cfg<DK, TV>;
   constexpr int PPW = C::PPW, NSEG = C::NSEG, TPS = C::TPS, RSK = C::RSK, RSV = C::RSV,
                 VPR = C::VPR;
-  SlotA<DK, TV>& A = sh.a[it % 3];
-  bf* Kh = sh.Kh[it & 1];
+  SlotA<DK, TV>& A = sh.a[vs % 3];
+  bf* Kh = sh.Kh[vs & 1];
   const int c0 = it * L;
   if constexpr (NEXT) load_part<DK, TV, DECAY, 0>(Rn, rs, cn, pp, seg, ptid);
   // transitions of this lane's token segment (identity past the end)
@@ -278,9 +282,13 @@ __device__ __forceinline__ void prep_chunk(Shared<DK, TV>& sh, const Raw<Cfg<DK,
   f32x2 run = d[0];
 #pragma unroll
   for (int r = 1; r < TPS; ++r) run = mulz(run, d[r]);
-  if (ptid < L * VPR) {
-    const int r = ptid / VPR, cc = ptid % VPR;
-    *(uint4*)(A.V + r * RSV + cc * 8) = R.v;
+#pragma unroll
+  for (int u = 0; u < C::VLD; ++u) {
+    const int idx = ptid + u * NWP * 64;
+    if (idx < L * VPR) {
+      const int r = idx / VPR, cc = idx % VPR;
+      *(uint4*)(A.V + r * RSV + cc * 8) = R.v[u];
+    }
   }
   // products over the earlier (pre) and later (post) segments of this lane's
   // channel pair, and over the whole chunk (tot): a butterfly over the NSEG
@@ -381,7 +389,7 @@ __device__ __forceinline__ void prep_chunk(Shared<DK, TV>& sh, const Raw<Cfg<DK,
   }
 }
 
-template <int DK, int TV, int DECAY>
+template <int DK, int TV, int DECAY, bool CONTENT>
 __global__ __launch_bounds__((NWP + NWS + TV / 16) * 64) void gdr_fwd_pipe_kernel(FwdParams p) {
   using C = Cfg<DK, TV>;
   using O = Op<bf>;
@@ -403,8 +411,34 @@ __global__ __launch_bounds__((NWP + NWS + TV / 16) * 64) void gdr_fwd_pipe_kerne
   const int b = unit / p.H, h = unit % p.H;
   const int v0 = vt * TV;
   const int Tn = p.T, H = p.H, DV = p.DV;
-  const int nchunks = (Tn + L - 1) / L;
-  const int nsteps = nchunks + 2;
+  const int nchunks = (Tn + L - 1) / L;   // 32-token blocks
+  // Content-aware erase: beta of a window of SPC blocks needs the previous
+  // window's mean output, which the consumers finish one step before the
+  // solve of the window's first block can use it; so one idle step follows
+  // every window.  Block j then runs its prep at step vj = j + j / SPC, its
+  // solve at vj + 1 and its consumer at vj + 2; slots rotate by step.
+  const int SPC = CONTENT ? p.window / L : 1;
+  auto vstep = [&](int j) { return CONTENT ? j + j / SPC : j; };
+  auto block_at = [&](int v) {   // block whose prep runs at step v, -1 if idle
+    return CONTENT ? ((v % (SPC + 1) == SPC) ? -1 : v - v / (SPC + 1)) : v;
+  };
+  const int nsteps = vstep(nchunks - 1) + 3;
+  // u_h = B_h^T a_h and the mean output of the previous window (the carried
+  // mean, or zero, before the first window)
+  __shared__ float sU[CONTENT ? TV : 1], sMean[CONTENT ? TV : 1];
+  // content-aware: beta and beta*w of a block, computed by the solve for the
+  // consumer (one per prep slot)
+  __shared__ __attribute__((aligned(16))) float sBc[CONTENT ? 3 : 1][CONTENT ? 2 : 1][L];
+  if constexpr (CONTENT) {
+    if (tid < TV) {
+      float acc = 0.f;
+      for (int r = 0; r < p.ub_rank; ++r)
+        acc += p.ub_up[h * p.ub_rank + r] * p.ub_down[((size_t)h * p.ub_rank + r) * DV + tid];
+      sU[tid] = acc;
+      sMean[tid] = p.m_carry ? p.m_carry[(size_t)(b * H + h) * DV + tid] : 0.f;
+    }
+    lds_barrier();
+  }
 
   if (wv < NWP) {
     // ================================================================ prep
@@ -418,40 +452,50 @@ __global__ __launch_bounds__((NWP + NWS + TV / 16) * 64) void gdr_fwd_pipe_kerne
     const int ptid = tid;                       // 0 .. NWP*64-1
     const Rsrc rs = make_rsrcs<DK, TV, DECAY>(p, b, h, v0);
     const int clast = (nchunks - 1) * L;
-    Raw<TPS> R0, R1, R2;
+    Raw<TPS, C::VLD> R0, R1, R2;
     load_raw<DK, TV, DECAY>(R0, rs, 0, pp, seg, ptid);
     load_raw<DK, TV, DECAY>(R1, rs, min(L, clast), pp, seg, ptid);
+    auto idle_after = [&](int j) {   // the idle step after a window's last block
+      if (CONTENT && j % SPC == SPC - 1 && j + 1 < nchunks) lds_barrier();
+    };
     int it = 0;
     for (; it + 2 < nchunks; it += 3) {
-      prep_chunk<DK, TV, DECAY, true>(sh, R0, R2, rs, (it + 2) * L, it, Tn, pw, l, pl, seg, pp,
-                                      ptid);
+      prep_chunk<DK, TV, DECAY, true>(sh, R0, R2, rs, (it + 2) * L, it, vstep(it), Tn, pw, l, pl,
+                                      seg, pp, ptid);
       lds_barrier();
-      prep_chunk<DK, TV, DECAY, true>(sh, R1, R0, rs, min((it + 3) * L, clast), it + 1, Tn, pw, l,
-                                      pl, seg, pp, ptid);
+      idle_after(it);
+      prep_chunk<DK, TV, DECAY, true>(sh, R1, R0, rs, min((it + 3) * L, clast), it + 1,
+                                      vstep(it + 1), Tn, pw, l, pl, seg, pp, ptid);
       lds_barrier();
-      prep_chunk<DK, TV, DECAY, true>(sh, R2, R1, rs, min((it + 4) * L, clast), it + 2, Tn, pw, l,
-                                      pl, seg, pp, ptid);
+      idle_after(it + 1);
+      prep_chunk<DK, TV, DECAY, true>(sh, R2, R1, rs, min((it + 4) * L, clast), it + 2,
+                                      vstep(it + 2), Tn, pw, l, pl, seg, pp, ptid);
       lds_barrier();
+      idle_after(it + 2);
     }
     // one or two chunks left: they are in R0 and R1
     if (it < nchunks) {
-      prep_chunk<DK, TV, DECAY, false>(sh, R0, R2, rs, 0, it, Tn, pw, l, pl, seg, pp, ptid);
+      prep_chunk<DK, TV, DECAY, false>(sh, R0, R2, rs, 0, it, vstep(it), Tn, pw, l, pl, seg, pp,
+                                       ptid);
       lds_barrier();
+      idle_after(it);
       ++it;
     }
     if (it < nchunks) {
-      prep_chunk<DK, TV, DECAY, false>(sh, R1, R2, rs, 0, it, Tn, pw, l, pl, seg, pp, ptid);
+      prep_chunk<DK, TV, DECAY, false>(sh, R1, R2, rs, 0, it, vstep(it), Tn, pw, l, pl, seg, pp,
+                                       ptid);
       lds_barrier();
       ++it;
     }
-    for (; it < nsteps; ++it) lds_barrier();
+    for (int st = vstep(nchunks - 1) + 1; st < nsteps; ++st) lds_barrier();
   } else if (wv < NWP + NWS) {
     // ================================================================ solve
     const int sw = wv - NWP;
-    // the last solve wave also stages beta and beta*w: loads one chunk ahead,
-    // written into the prep slot of the chunk being prepared in this step
-    // (tokens at or past T read as zero)
-    const rsrc_t rb = make_rsrc(p.beta + ((size_t)b * Tn * H + h), ((size_t)(Tn - 1) * H + 1) * 4);
+    // the last solve wave also stages beta and beta*w (content-aware: the
+    // logit b_x and w): loads one block ahead, written into the prep slot of
+    // the block being prepared in this step (tokens at or past T read as zero)
+    const float* pbeta = CONTENT ? p.beta_logit : p.beta;
+    const rsrc_t rb = make_rsrc(pbeta + ((size_t)b * Tn * H + h), ((size_t)(Tn - 1) * H + 1) * 4);
     const rsrc_t rw = make_rsrc(p.w + ((size_t)b * Tn * H + h), ((size_t)(Tn - 1) * H + 1) * 4);
     const int tb = (l < L ? l : L - 1) * H * 4;
     float nbt = 0.f, nwt = 0.f;
@@ -459,22 +503,45 @@ __global__ __launch_bounds__((NWP + NWS + TV / 16) * 64) void gdr_fwd_pipe_kerne
       nbt = __uint_as_float(__builtin_amdgcn_raw_buffer_load_b32(rb, tb, 0, 0));
       nwt = __uint_as_float(__builtin_amdgcn_raw_buffer_load_b32(rw, tb, 0, 0));
     }
+    float s_win = 0.f;   // content-aware: s_c = u_h . m_c of the current window
     for (int it = 0; it < nsteps; ++it) {
-      if (sw == NWS - 1 && it < nchunks) {
+      const int jp = CONTENT ? block_at(it) : it;
+      if (sw == NWS - 1 && (CONTENT ? (jp >= 0 && jp < nchunks) : (it < nchunks))) {
         const float bt = nbt, wt = nwt;
-        const int cn = min(it + 1, nchunks - 1) * L * H * 4;   // uniform
+        const int cn = min(jp + 1, nchunks - 1) * L * H * 4;   // uniform
         nbt = __uint_as_float(__builtin_amdgcn_raw_buffer_load_b32(rb, tb, cn, 0));
         nwt = __uint_as_float(__builtin_amdgcn_raw_buffer_load_b32(rw, tb, cn, 0));
         if (l < L) {
           sh.a[it % 3].beta[l] = bt;
-          sh.a[it % 3].bw[l] = bt * wt;
+          sh.a[it % 3].bw[l] = CONTENT ? wt : bt * wt;
         }
       }
-      const int j = it - 1;
+      const int vj = it - 1;
+      const int j = CONTENT ? (vj >= 0 ? block_at(vj) : -1) : vj;
       if (j >= 0 && j < nchunks) {
-        const SlotA<DK, TV>& A = sh.a[j % 3];
-        const bf* Kh = sh.Kh[j & 1];
-        SlotS& S = sh.s[j & 1];
+        const SlotA<DK, TV>& A = sh.a[vj % 3];
+        const bf* Kh = sh.Kh[vj & 1];
+        SlotS& S = sh.s[vj & 1];
+        if constexpr (CONTENT) {
+          if (j % SPC == 0) {   // new window: s_c from the previous window's mean (fixed order)
+            float acc = 0.f;
+            for (int vv = l; vv < TV; vv += 64) acc += sU[vv] * sMean[vv];
+#pragma unroll
+            for (int off = 32; off > 0; off >>= 1) acc += __shfl_xor(acc, off);
+            s_win = acc;
+          }
+        }
+        auto beta_at = [&](int r) {
+          if constexpr (CONTENT) return 1.f / (1.f + __expf(-(A.beta[r] + s_win)));
+          else return A.beta[r];
+        };
+        if constexpr (CONTENT) {   // beta and beta*w of this block for the consumer
+          if (sw == NWS - 1 && l < L) {
+            const float bt = beta_at(l);
+            sBc[vj % 3][0][l] = bt;
+            sBc[vj % 3][1][l] = bt * A.bw[l];
+          }
+        }
         if (sw < 2) {
           // diagonal block bb: N and N^T as accumulator tiles, then
           // T_bb = (I + N)^{-1} = (I - N)(I + N^2)(I + N^4)(I + N^8).
@@ -489,11 +556,11 @@ __global__ __launch_bounds__((NWP + NWS + TV / 16) * 64) void gdr_fwd_pipe_kerne
             O::mma(g1, kh, kp);   // (K+ Kh^T)[n][4g+j]
           }
           f32x4 Nc, Nt, Pt;
-          const float bn = A.beta[16 * bb + n];
+          const float bn = beta_at(16 * bb + n);
 #pragma unroll
           for (int jj = 0; jj < 4; ++jj) {
             const int rr = 4 * g + jj;
-            Nc[jj] = (n < rr) ? A.beta[16 * bb + rr] * g0[jj] : 0.f;   // N[rr][n]
+            Nc[jj] = (n < rr) ? beta_at(16 * bb + rr) * g0[jj] : 0.f;   // N[rr][n]
             Nt[jj] = (rr < n) ? bn * g1[jj] : 0.f;                     // N[n][rr]
             Pt[jj] = ((rr == n) ? 1.f : 0.f) - Nt[jj];                  // (I - N)^T
           }
@@ -529,7 +596,7 @@ __global__ __launch_bounds__((NWP + NWS + TV / 16) * 64) void gdr_fwd_pipe_kerne
             for (int jj = 0; jj < 4; ++jj) {
               const int rr = 16 * rb + 4 * g + jj, cc = 16 * cbk + n;
               if (isA) {
-                S.A10[(4 * g + jj) * RS16 + n] = (bf)(A.beta[rr] * acc[jj]);
+                S.A10[(4 * g + jj) * RS16 + n] = (bf)(beta_at(rr) * acc[jj]);
               } else {
                 S.M[rr * RSL + cc] = (bf)((cc <= rr) ? acc[jj] : 0.f);
               }
@@ -562,11 +629,13 @@ __global__ __launch_bounds__((NWP + NWS + TV / 16) * 64) void gdr_fwd_pipe_kerne
     const rsrc_t ro = make_rsrc((bf*)p.o + obh * DV + ocol, orows * DV * 2 - (size_t)ocol * 2);
     const int so = H * DV * 2;                     // bytes per token row
     const int olane = n * so + 8 * g;              // token n, value channels 4g..4g+3
+    float colsum[4] = {0.f, 0.f, 0.f, 0.f};   // content-aware: window sums of 4 channels
     for (int it = 0; it < nsteps; ++it) {
-      const int i = it - 2;
-      if (i >= 0) {
-        const SlotA<DK, TV>& A = sh.a[i % 3];
-        const SlotS& S = sh.s[i & 1];
+      const int vi = it - 2;
+      const int i = CONTENT ? (vi >= 0 ? block_at(vi) : -1) : vi;
+      if (CONTENT ? (i >= 0 && i < nchunks) : (i >= 0)) {
+        const SlotA<DK, TV>& A = sh.a[vi % 3];
+        const SlotS& S = sh.s[vi & 1];
         const int c0 = i * L;
         // R = diag(bw) V - diag(beta) K+ S^T;  Qs^T = (Q+ S^T)^T, kept transposed
         // (lane holds one token and four value channels) for 8-byte o stores
@@ -582,8 +651,8 @@ __global__ __launch_bounds__((NWP + NWS + TV / 16) * 64) void gdr_fwd_pipe_kerne
             O::mma(P, load_plain<bf>(A.Kp, RSK, 16 * t, 32 * kk), Sf[kk]);
             O::mma(Q, Sf[kk], load_plain<bf>(A.Qp, RSK, 16 * t, 32 * kk));
           }
-          const f32x4 bw4 = *(const f32x4*)(A.bw + 16 * t + 4 * g);
-          const f32x4 bt4 = *(const f32x4*)(A.beta + 16 * t + 4 * g);
+          const f32x4 bw4 = *(const f32x4*)((CONTENT ? sBc[vi % 3][1] : A.bw) + 16 * t + 4 * g);
+          const f32x4 bt4 = *(const f32x4*)((CONTENT ? sBc[vi % 3][0] : A.beta) + 16 * t + 4 * g);
 #pragma unroll
           for (int jj = 0; jj < 4; ++jj) {
             const int r = 16 * t + 4 * g + jj;
@@ -608,6 +677,23 @@ __global__ __launch_bounds__((NWP + NWS + TV / 16) * 64) void gdr_fwd_pipe_kerne
           typedef __attribute__((ext_vector_type(2))) unsigned u32x2;
           __builtin_amdgcn_raw_buffer_store_b64(*(const u32x2*)&x0, ro, olane, c0 * so, 0);
           __builtin_amdgcn_raw_buffer_store_b64(*(const u32x2*)&x1, ro, olane, (c0 + 16) * so, 0);
+        }
+        if constexpr (CONTENT) {
+          // window sums of the fp32 outputs (tokens past T contribute zero);
+          // at a window's last block its per-channel mean goes to LDS, to be
+          // read by the solve of the next window's first block
+#pragma unroll
+          for (int jj = 0; jj < 4; ++jj) colsum[jj] += O0[jj] + O1[jj];
+          if (i % SPC == SPC - 1) {
+#pragma unroll
+            for (int jj = 0; jj < 4; ++jj) {
+              float sum = colsum[jj];
+#pragma unroll
+              for (int off = 1; off < 16; off <<= 1) sum += __shfl_xor(sum, off);
+              if (n == 0) sMean[16 * cw + 4 * g + jj] = sum * (1.f / (float)(SPC * L));
+              colsum[jj] = 0.f;
+            }
+          }
         }
         // S <- S Gamma_L + Dl^T K- = (S + Dl^T Kh) Gamma_L, since K- = Kh Gamma_L
         // column-wise (per channel, or per rotation pair)
@@ -635,16 +721,23 @@ __global__ __launch_bounds__((NWP + NWS + TV / 16) * 64) void gdr_fwd_pipe_kerne
 #pragma unroll
       for (int ct = 0; ct < NCT; ++ct) *(f32x4*)(p.S_out + srow + 16 * ct + 4 * g) = Sacc[ct];
     }
+    if constexpr (CONTENT) {   // the last window's mean (T is a multiple of the window)
+      if (p.m_carry && n == 0) {
+#pragma unroll
+        for (int jj = 0; jj < 4; ++jj)
+          p.m_carry[(size_t)(b * H + h) * DV + 16 * cw + 4 * g + jj] = sMean[16 * cw + 4 * g + jj];
+      }
+    }
   }
 }
 
-template <int DK, int TV, int DECAY>
+template <int DK, int TV, int DECAY, bool CONTENT = false>
 hipError_t launch(const FwdParams& p0, hipStream_t s) {
   FwdParams p = p0;
   p.n_vt = p.DV / TV;
   p.n_units = p.B * p.H;
   const int groups = (p.n_units + 7) / 8;
-  hipLaunchKernelGGL((gdr_fwd_pipe_kernel<DK, TV, DECAY>), dim3(groups * 8 * p.n_vt),
+  hipLaunchKernelGGL((gdr_fwd_pipe_kernel<DK, TV, DECAY, CONTENT>), dim3(groups * 8 * p.n_vt),
                      dim3(Cfg<DK, TV>::NT), 0, s, p);
   return hipGetLastError();
 }
@@ -654,12 +747,17 @@ hipError_t launch(const FwdParams& p0, hipStream_t s) {
 bool fwd_pipe_supported(const FwdParams& p) {
   // buffer resources address one (b, h) with 32-bit byte offsets
   const bool fits = (unsigned long long)p.T * p.H * p.DK * 4ull < (1ull << 31);
-  return p.io_bf16 && p.beta_logit == nullptr && (p.DK == 64 || p.DK == 128) && p.DV == p.DK &&
-         fits;
+  // content-aware: the window must be a whole number of 32-token blocks
+  const bool content_ok = p.beta_logit == nullptr || (p.window >= 32 && p.window % 32 == 0);
+  return p.io_bf16 && content_ok && (p.DK == 64 || p.DK == 128) && p.DV == p.DK && fits;
 }
 
 hipError_t launch_fwd_pipe(const FwdParams& p, hipStream_t s) {
   const bool rot = p.decay != 0;
+  if (p.beta_logit != nullptr) {   // content-aware: one workgroup covers all value channels
+    if (p.DK == 128) return rot ? pipe::launch<128, 128, 1, true>(p, s) : pipe::launch<128, 128, 0, true>(p, s);
+    return rot ? pipe::launch<64, 64, 1, true>(p, s) : pipe::launch<64, 64, 0, true>(p, s);
+  }
   if (p.DK == 128) {
     if ((long)p.B * p.H * 2 >= 192) {
       return rot ? pipe::launch<128, 64, 1>(p, s) : pipe::launch<128, 64, 0>(p, s);

@@ -179,6 +179,22 @@ def test_content_aware_stress(io, dk, chunk):
     assert max_rel_err(og, o0) > 0.1
 
 
+@pytest.mark.parametrize("decay", ["diag", "rot2"])
+@pytest.mark.parametrize("dk", [64, 128])
+@pytest.mark.parametrize("chunk", [32, 128])
+def test_content_aware_rotation_window_s0(decay, dk, chunk):
+    """Content-aware erase with rotation-decay blocks or the per-channel decay, a
+    window of one or four 32-token blocks, a non-zero initial state and a ragged
+    tail (bf16 io)."""
+    wl = _wl("bf16", decay, dk, B=2, H=2, T=3 * chunk + 9, chunk=chunk, content=True,
+             seed=33 + dk + chunk)
+    x = generate(wl, ub_std=1.0)
+    S0 = random_state(wl.B, wl.H, wl.dv, wl.dk, seed=7)
+    o, S = run_gpu(x, S0=S0)
+    compare_heads(o, S, oracle_heads(x, S0=S0), TOL["bf16"],
+                  f"content {decay}/d{dk}/L{chunk}/S0")
+
+
 @pytest.mark.parametrize("io", ["f32", "bf16"])
 def test_content_aware_resume_with_carry(io):
     wl = _wl(io, "diag", 64, B=2, H=2, T=256, chunk=64, content=True, seed=32)
