@@ -452,13 +452,34 @@ __global__ __launch_bounds__((NWP + NWS + TV / 16) * 64) void gdr_fwd_pipe_kerne
     const int ptid = tid;                       // 0 .. NWP*64-1
     const Rsrc rs = make_rsrcs<DK, TV, DECAY>(p, b, h, v0);
     const int clast = (nchunks - 1) * L;
-    Raw<TPS, C::VLD> R0, R1, R2;
-    load_raw<DK, TV, DECAY>(R0, rs, 0, pp, seg, ptid);
-    load_raw<DK, TV, DECAY>(R1, rs, min(L, clast), pp, seg, ptid);
     auto idle_after = [&](int j) {   // the idle step after a window's last block
       if (CONTENT && j % SPC == SPC - 1 && j + 1 < nchunks) lds_barrier();
     };
     int it = 0;
+    if constexpr (C::NT > 12 * 64) {
+      // 16 waves leave 128 VGPRs per wave: one chunk ahead, two register sets
+      Raw<TPS, C::VLD> R0, R1;
+      load_raw<DK, TV, DECAY>(R0, rs, 0, pp, seg, ptid);
+      for (; it + 1 < nchunks; it += 2) {
+        prep_chunk<DK, TV, DECAY, true>(sh, R0, R1, rs, (it + 1) * L, it, vstep(it), Tn, pw, l, pl,
+                                        seg, pp, ptid);
+        lds_barrier();
+        idle_after(it);
+        prep_chunk<DK, TV, DECAY, true>(sh, R1, R0, rs, min((it + 2) * L, clast), it + 1,
+                                        vstep(it + 1), Tn, pw, l, pl, seg, pp, ptid);
+        lds_barrier();
+        idle_after(it + 1);
+      }
+      if (it < nchunks) {   // odd chunk count: the last chunk is in R0
+        prep_chunk<DK, TV, DECAY, false>(sh, R0, R1, rs, 0, it, vstep(it), Tn, pw, l, pl, seg, pp,
+                                         ptid);
+        lds_barrier();
+        ++it;
+      }
+    } else {
+    Raw<TPS, C::VLD> R0, R1, R2;
+    load_raw<DK, TV, DECAY>(R0, rs, 0, pp, seg, ptid);
+    load_raw<DK, TV, DECAY>(R1, rs, min(L, clast), pp, seg, ptid);
     for (; it + 2 < nchunks; it += 3) {
       prep_chunk<DK, TV, DECAY, true>(sh, R0, R2, rs, (it + 2) * L, it, vstep(it), Tn, pw, l, pl,
                                       seg, pp, ptid);
@@ -486,6 +507,7 @@ __global__ __launch_bounds__((NWP + NWS + TV / 16) * 64) void gdr_fwd_pipe_kerne
                                        ptid);
       lds_barrier();
       ++it;
+    }
     }
     for (int st = vstep(nchunks - 1) + 1; st < nsteps; ++st) lds_barrier();
   } else if (wv < NWP + NWS) {
