@@ -448,6 +448,11 @@ __global__ __launch_bounds__((NWP + NWS + TV / 16) * 64) void gdr_fwd_pipe_kerne
     // loaded again at the end) so that the outstanding-load count at every use
     // is known statically.
     const int pw = wv;
+    // With one block per (b, h) the content-aware launch keeps one workgroup
+    // per CU; there the consumer's chain sets the step time, so it issues
+    // first, then the prep, then the solve.  (The plain launches run faster
+    // at equal priority.)
+    if constexpr (CONTENT) __builtin_amdgcn_s_setprio(1);
     const int pl = l % PPW, seg = l / PPW, pp = pw * PPW + pl;
     const int ptid = tid;                       // 0 .. NWP*64-1
     const Rsrc rs = make_rsrcs<DK, TV, DECAY>(p, b, h, v0);
@@ -631,6 +636,7 @@ __global__ __launch_bounds__((NWP + NWS + TV / 16) * 64) void gdr_fwd_pipe_kerne
   } else {
     // ============================================================ consumer
     const int cw = wv - NWP - NWS;              // value block of 16 channels
+    if constexpr (CONTENT) __builtin_amdgcn_s_setprio(2);
     f32x4 Sacc[NCT];
     const size_t srow = ((size_t)(b * H + h) * DV + v0 + 16 * cw + n) * DK;
     if (p.S0) {
