@@ -57,6 +57,11 @@ __device__ constexpr int cb_pos(int c) {
 constexpr int L = 32;      // tokens per chunk
 constexpr int NWP = 4;     // prep waves
 constexpr int NWS = 4;     // solve waves
+// LDS bank rules of gfx950 (measured with the bank-conflict counter): 4-byte
+// accesses go to 32 banks, lanes 0-31 and 32-63 in separate cycles; 8-byte
+// accesses to 64 banks, 32 lanes per cycle; 16-byte reads to 64 banks, 16 lanes
+// per cycle in a lane grouping that is not plain lane order.  The strides and
+// the swizzle below keep the hot accesses free of conflicts under these rules.
 constexpr int RSL = L + 4; // row stride of [.][L] arrays
 constexpr int RS16 = 20;   // row stride of 16x16 blocks
 
@@ -68,7 +73,12 @@ struct Cfg {
   static constexpr int PPW = NP / NWP;           // channel pairs per prep wave
   static constexpr int NSEG = 64 / PPW;          // token segments per prep wave
   static constexpr int TPS = L / NSEG;           // tokens per prep lane
-  static constexpr int RSK = DK + 8;
+  // K+, Q+ and Kh rows: 128 key channels use an 80-dword stride and, in rows
+  // with bit 3 set, 16-byte unit u stored at u ^ 6; so the 16-byte fragment
+  // reads of 16 rows and the prep's 4-byte stores of rows 8 apart are both
+  // conflict-free.  64 key channels keep a 36-dword stride and no swizzle.
+  static constexpr int RSK = DK == 128 ? 160 : DK + 8;
+  static constexpr int SWZ = DK == 128 ? 6 : 0;
   static constexpr int RSV = TV + 8;
   static constexpr int NCT = DK / 16;
   static constexpr int NKC = DK / 32;
@@ -162,6 +172,16 @@ __device__ inline Rsrc make_rsrcs(const FwdParams& p, int b, int h, int v0) {
   r.beta = make_rsrc(p.beta + bh, rows * 4);
   r.w = make_rsrc(p.w + bh, rows * 4);
   return r;
+}
+
+// A or B operand from K+, Q+ or Kh rows: rows row0 + n (row0 a multiple of 16),
+// contraction over key positions 32 kk .. 32 kk + 31 in the plain slot map.
+template <int DK, int TV>
+__device__ inline bf16x8 load_kq(const bf* base, int row0, int kk) {
+  using C = Cfg<DK, TV>;
+  const int l = lane_id(), n = l & 15, g = l >> 4;
+  const int sw = C::SWZ * ((n >> 3) & 1);
+  return *(const bf16x8*)(base + (row0 + n) * C::RSK + (((4 * kk + g) ^ sw) << 3));
 }
 
 // Byte offsets: the per-lane part goes in voffset, the per-token part (uniform)
@@ -332,7 +352,11 @@ __device__ __forceinline__ void prep_chunk(Shared<DK, TV>& sh, const Raw<Cfg<DK,
       rb = (DECAY == 0) ? mulz(rb, d[r]) : cmul(rb, conj(d[r]));
     }
   }
-  const int pc = cb_pos(2 * pp);   // stored position of this channel pair
+  // stored position of this channel pair (rows of one lane share bit 3 when
+  // segments are 8 tokens, so one swizzled position serves all of them)
+  static_assert(C::SWZ == 0 || TPS == 8, "K+/Q+/Kh swizzle assumes 8-token segments");
+  const int pc0 = cb_pos(2 * pp);
+  const int pc = (((pc0 >> 3) ^ (C::SWZ * (seg & 1))) << 3) | (pc0 & 7);
   float kh0[TPS], kh1[TPS];
 #pragma unroll
   for (int r4 = 0; r4 < TPS; r4 += 4) {
@@ -577,8 +601,8 @@ __global__ __launch_bounds__((NWP + NWS + TV / 16) * 64) void gdr_fwd_pipe_kerne
           f32x4 g0 = {0.f, 0.f, 0.f, 0.f}, g1 = {0.f, 0.f, 0.f, 0.f};
 #pragma unroll
           for (int kk = 0; kk < NKC; ++kk) {
-            const frag kp = load_plain<bf>(A.Kp, RSK, 16 * bb, 32 * kk);
-            const frag kh = load_plain<bf>(Kh, RSK, 16 * bb, 32 * kk);
+            const frag kp = load_kq<DK, TV>(A.Kp, 16 * bb, kk);
+            const frag kh = load_kq<DK, TV>(Kh, 16 * bb, kk);
             O::mma(g0, kp, kh);   // (K+ Kh^T)[4g+j][n]
             O::mma(g1, kh, kp);   // (K+ Kh^T)[n][4g+j]
           }
@@ -617,8 +641,7 @@ __global__ __launch_bounds__((NWP + NWS + TV / 16) * 64) void gdr_fwd_pipe_kerne
             f32x4 acc = {0.f, 0.f, 0.f, 0.f};
 #pragma unroll
             for (int kk = 0; kk < NKC; ++kk)
-              O::mma(acc, load_plain<bf>(src, RSK, 16 * rb, 32 * kk),
-                     load_plain<bf>(Kh, RSK, 16 * cbk, 32 * kk));
+              O::mma(acc, load_kq<DK, TV>(src, 16 * rb, kk), load_kq<DK, TV>(Kh, 16 * cbk, kk));
 #pragma unroll
             for (int jj = 0; jj < 4; ++jj) {
               const int rr = 16 * rb + 4 * g + jj, cc = 16 * cbk + n;
@@ -676,8 +699,8 @@ __global__ __launch_bounds__((NWP + NWS + TV / 16) * 64) void gdr_fwd_pipe_kerne
           f32x4 P = {0.f, 0.f, 0.f, 0.f}, Q = {0.f, 0.f, 0.f, 0.f};
 #pragma unroll
           for (int kk = 0; kk < NKC; ++kk) {
-            O::mma(P, load_plain<bf>(A.Kp, RSK, 16 * t, 32 * kk), Sf[kk]);
-            O::mma(Q, Sf[kk], load_plain<bf>(A.Qp, RSK, 16 * t, 32 * kk));
+            O::mma(P, load_kq<DK, TV>(A.Kp, 16 * t, kk), Sf[kk]);
+            O::mma(Q, Sf[kk], load_kq<DK, TV>(A.Qp, 16 * t, kk));
           }
           const f32x4 bw4 = *(const f32x4*)((CONTENT ? sBc[vi % 3][1] : A.bw) + 16 * t + 4 * g);
           const f32x4 bt4 = *(const f32x4*)((CONTENT ? sBc[vi % 3][0] : A.beta) + 16 * t + 4 * g);
