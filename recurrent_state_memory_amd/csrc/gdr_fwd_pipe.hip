@@ -631,7 +631,9 @@ __global__ __launch_bounds__((NWP + NWS + TV / 16) * 64) void gdr_fwd_pipe_kerne
           for (int jj = 0; jj < 4; ++jj) tv[jj] = (bf)Pt[jj];
           *(bf16x4*)(S.Td + (bb * 16 + n) * RS16 + 4 * g) = tv;
         } else {
-          // wave 2: A10 and M00; wave 3: M10 and M11
+          // wave 2: A10 and M00; wave 3: M10 and M11.  Y = R1 - A10 Dl0 takes
+          // -A10: with rotation decay the solve stores it negated, with
+          // diagonal decay the consumer negates it (the faster schedule of each)
 #pragma unroll
           for (int ti = 0; ti < 2; ++ti) {
             const bool isA = (sw == 2 && ti == 0);
@@ -646,7 +648,7 @@ __global__ __launch_bounds__((NWP + NWS + TV / 16) * 64) void gdr_fwd_pipe_kerne
             for (int jj = 0; jj < 4; ++jj) {
               const int rr = 16 * rb + 4 * g + jj, cc = 16 * cbk + n;
               if (isA) {
-                S.A10[(4 * g + jj) * RS16 + n] = (bf)(beta_at(rr) * acc[jj]);
+                S.A10[(4 * g + jj) * RS16 + n] = (bf)((DECAY != 0 ? -1.f : 1.f) * beta_at(rr) * acc[jj]);
               } else {
                 S.M[rr * RSL + cc] = (bf)((cc <= rr) ? acc[jj] : 0.f);
               }
@@ -714,13 +716,19 @@ __global__ __launch_bounds__((NWP + NWS + TV / 16) * 64) void gdr_fwd_pipe_kerne
         // Dl by blocks, O = Qs + M Dl
         f32x4 D0 = {0.f, 0.f, 0.f, 0.f}, D1 = {0.f, 0.f, 0.f, 0.f};
         O::mma(D0, load_cb_half<bf>(S.Td, RS16, 0, 0), O::from_acc_half(Rt[0]));
+        const frag d0 = O::from_acc_half(D0);
         f32x4 Y = Rt[1];
-        O::mma(Y, O::neg(load_cb_half<bf>(S.A10, RS16, 0, 0)), O::from_acc_half(D0));
+        {
+          const frag a10 = load_cb_half<bf>(S.A10, RS16, 0, 0);
+          O::mma(Y, DECAY != 0 ? a10 : O::neg(a10), d0);
+        }
         O::mma(D1, load_cb_half<bf>(S.Td + 16 * RS16, RS16, 0, 0), O::from_acc_half(Y));
-        const frag Df = O::from_acc(D0, D1);
+        frag Df = d0;   // slots 0..3 from D0, 4..7 from D1
+#pragma unroll
+        for (int jj = 0; jj < 4; ++jj) Df[4 + jj] = (bf)D1[jj];
         // O^T = Qs^T + (M Dl)^T = Qs^T + Dl^T M^T
         f32x4 O0 = Qs[0], O1 = Qs[1];
-        O::mma(O0, O::from_acc_half(D0), load_cb_half<bf>(S.M, RSL, 0, 0));
+        O::mma(O0, d0, load_cb_half<bf>(S.M, RSL, 0, 0));
         O::mma(O1, Df, load_cb<bf>(S.M, RSL, 16, 0));
         {
           const bf16x4 x0 = {(bf)O0[0], (bf)O0[1], (bf)O0[2], (bf)O0[3]};
