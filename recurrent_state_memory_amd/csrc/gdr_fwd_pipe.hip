@@ -730,13 +730,8 @@ __global__ __launch_bounds__((NWP + NWS + TV / 16) * 64) void gdr_fwd_pipe_kerne
         f32x4 O0 = Qs[0], O1 = Qs[1];
         O::mma(O0, d0, load_cb_half<bf>(S.M, RSL, 0, 0));
         O::mma(O1, Df, load_cb<bf>(S.M, RSL, 16, 0));
-        {
-          const bf16x4 x0 = {(bf)O0[0], (bf)O0[1], (bf)O0[2], (bf)O0[3]};
-          const bf16x4 x1 = {(bf)O1[0], (bf)O1[1], (bf)O1[2], (bf)O1[3]};
-          typedef __attribute__((ext_vector_type(2))) unsigned u32x2;
-          __builtin_amdgcn_raw_buffer_store_b64(*(const u32x2*)&x0, ro, olane, c0 * so, 0);
-          __builtin_amdgcn_raw_buffer_store_b64(*(const u32x2*)&x1, ro, olane, (c0 + 16) * so, 0);
-        }
+        const bf16x4 ox0 = {(bf)O0[0], (bf)O0[1], (bf)O0[2], (bf)O0[3]};
+        const bf16x4 ox1 = {(bf)O1[0], (bf)O1[1], (bf)O1[2], (bf)O1[3]};
         if constexpr (CONTENT) {
           // window sums of the fp32 outputs (tokens past T contribute zero);
           // at a window's last block its per-channel mean goes to LDS, to be
@@ -772,6 +767,11 @@ __global__ __launch_bounds__((NWP + NWS + TV / 16) * 64) void gdr_fwd_pipe_kerne
               Sacc[ct][jj + 1] = -z.y * x0 + z.x * x1;
             }
           }
+        }
+        {   // o stores last, off the chain from the barrier to the state update
+          typedef __attribute__((ext_vector_type(2))) unsigned u32x2;
+          __builtin_amdgcn_raw_buffer_store_b64(*(const u32x2*)&ox0, ro, olane, c0 * so, 0);
+          __builtin_amdgcn_raw_buffer_store_b64(*(const u32x2*)&ox1, ro, olane, (c0 + 16) * so, 0);
         }
       }
       lds_barrier();
