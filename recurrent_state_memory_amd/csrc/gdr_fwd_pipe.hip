@@ -235,21 +235,17 @@ __device__ inline void load_raw(Raw<Cfg<DK, TV>::TPS, Cfg<DK, TV>::VLD>& R, cons
 }
 
 // Value held by lane l ^ (PPW * d) (d = 1, 2, 4; PPW * d in {8, 16, 32}):
-// a row rotation by 8 within rows of 16 lanes, or the gfx950 lane swaps, which
-// return rows (v0, v0, v2, v2) and (v1, v1, v3, v3) for 16 and
-// (v0, v1, v0, v1) and (v2, v3, v2, v3) for 32.
+// a row rotation by 8 within rows of 16 lanes (one DPP move), else a backward
+// permute through the LDS crossbar, which takes one DS instruction and no VALU
+// issue slot (the v_permlane swaps need two copies and a select per value).
 template <int PPW>
 __device__ inline float xor_lanes(float v, int d, int l) {
   const int dist = PPW * d;
   const unsigned u = __float_as_uint(v);
   if (dist == 8) {
     return __uint_as_float(__builtin_amdgcn_mov_dpp(u, 0x128, 0xf, 0xf, false));   // row_ror:8
-  } else if (dist == 16) {
-    const auto e = __builtin_amdgcn_permlane16_swap(u, u, false, false);
-    return __uint_as_float((l & 16) ? e[0] : e[1]);
-  } else {
-    const auto e = __builtin_amdgcn_permlane32_swap(u, u, false, false);
-    return __uint_as_float((l & 32) ? e[0] : e[1]);
+  } else {   // LDS crossbar: one DS instruction, no VALU issue
+    return __uint_as_float((unsigned)__builtin_amdgcn_ds_bpermute((l ^ dist) << 2, (int)u));
   }
 }
 
