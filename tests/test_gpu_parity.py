@@ -102,6 +102,19 @@ def test_single_token_and_short(io):
         compare_heads(o, S, oracle_heads(x, S0=S0), TOL[io], f"T={T}")
 
 
+@pytest.mark.parametrize("decay", ["diag", "rot2"])
+def test_wide_grid_value_halves(decay):
+    """B*H = 96 at d = 128 selects the launch with 64 value channels per workgroup
+    (two value halves per head, 8 workgroup ids apart); ragged T, non-zero S0,
+    every output of sampled heads including both halves of each."""
+    x = generate(_wl("bf16", decay, 128, B=8, H=12, T=3 * 32 + 7, chunk=64, seed=31))
+    S0 = random_state(8, 12, 128, 128, 31)
+    o, S = run_gpu(x, S0=S0)
+    assert np.all(np.isfinite(o)) and np.all(np.isfinite(S))
+    heads = [(0, 0), (2, 5), (5, 11), (7, 6)]
+    compare_heads(o, S, oracle_heads(x, heads, S0=S0), TOL["bf16"], f"wide/{decay}")
+
+
 def test_many_heads_grid_padding():
     """B*H not a multiple of 8 exercises the padded workgroup grid."""
     x = generate(_wl("bf16", "diag", 128, B=3, H=5, T=130, chunk=64, seed=5))
