@@ -26,6 +26,7 @@ import argparse
 import hashlib
 import json
 import os
+import re
 import sys
 import time
 
@@ -59,11 +60,21 @@ def algorithmic_flops(wl, L: int) -> float:
     return per_th * wl.B * wl.T * wl.H
 
 
+def _code_only(text: str) -> str:
+    """C/C++ source with comments removed and whitespace runs collapsed."""
+    text = re.sub(r"/\*.*?\*/", " ", text, flags=re.S)
+    text = re.sub(r"//[^\n]*", " ", text)
+    return " ".join(text.split())
+
+
 def _kernel_hash() -> str:
+    """First 16 hex digits of the sha256 of the kernel sources' code (comments
+    and whitespace removed): a comment edit keeps the recorded counters valid,
+    any code change invalidates them."""
     h = hashlib.sha256()
     for path in KERNEL_SRCS:
-        with open(path, "rb") as f:
-            h.update(f.read())
+        with open(path, encoding="utf-8") as f:
+            h.update(_code_only(f.read()).encode())
     return h.hexdigest()[:16]
 
 

@@ -5,7 +5,8 @@
 // affine chunk transfer), as a three-stage pipeline inside one workgroup with
 // a single workgroup barrier per 32-token step:
 //
-//   prep waves (4), chunk i+2: load the chunk (issued one chunk ahead),
+//   prep waves (4), chunk i+2: load the chunk (issued two chunks ahead; one in
+//     the 16-wave content-aware variant),
 //     running products of the key-axis transitions (forward and backward,
 //     scanned across token segments inside each wave), decayed forms
 //     K+ = g_r k, Q+ = g_r q and Kh = Gamma_L^{-T} K- with K- = h_r^T k.
@@ -22,6 +23,10 @@
 // reciprocal per key channel (of Gamma_L) is needed; for 2x2 rotation-decay
 // blocks the same holds with complex products per channel pair.  Prep outputs
 // are triple-buffered and solve outputs double-buffered in LDS.
+//
+// Content-aware erase (CONTENT): one workgroup covers all value channels of a
+// (b, h); beta of each window comes from the previous window's mean output,
+// formed by the consumers and read by the solve after one idle step.
 #include "gdr_kernels.h"
 #include "gdr_mfma.h"
 
@@ -250,10 +255,10 @@ __device__ inline float xor_lanes(float v, int d, int l) {
 }
 
 // One prep step: decayed key/query forms of 32-token block `it` (raw loads in
-// R) into prep slot vs % 3 and the Kh buffer vs % 2 (vs: the block's step).  With NEXT, the raw loads of the
-// chunk at token cn go into Rn, spread over the step in four groups so that
-// the prep waves do not all stall on a full vector-memory queue at the start
-// of every step.
+// R) into prep slot vs % 3 and the Kh buffer vs % 2 (vs: the block's step).
+// With NEXT, the raw loads of the chunk at token cn go into Rn, spread over the
+// step in four groups so that the prep waves do not all stall on a full
+// vector-memory queue at the start of every step.
 template <int DK, int TV, int DECAY, bool NEXT>
 __device__ __forceinline__ void prep_chunk(Shared<DK, TV>& sh, const Raw<Cfg<DK, TV>::TPS, Cfg<DK, TV>::VLD>& R,
                                            Raw<Cfg<DK, TV>::TPS, Cfg<DK, TV>::VLD>& Rn, const Rsrc& rs, int cn,
