@@ -46,19 +46,23 @@ def test_layer_sampled():
     compare_heads(o, S, oracle_heads(x, heads), TOL["bf16"], "layer")
 
 
-def test_layer_head_permutation():
-    """Full-size layer run on inputs with permuted batch rows and heads: every output
-    of every head must match the unpermuted run bitwise (each (b, h) is computed
-    independently of where the grid places it).  With the sampled oracle comparison
-    above, this covers all 128 heads of the workload."""
+@pytest.mark.parametrize("name", ["layer", "rot", "long"])
+def test_head_permutation(name):
+    """Full-size run on inputs with permuted batch rows and heads: every output of
+    every head must match the unpermuted run bitwise (each (b, h) is computed
+    independently of where the grid places it).  With the sampled oracle
+    comparisons above, this covers every head of the workload."""
     import dataclasses
-    x = generate(WORKLOADS["layer"])
+    x = generate(WORKLOADS[name])
     o1, S1 = run_gpu(x)
     rng = np.random.default_rng(11)
     pb, ph = rng.permutation(x.wl.B), rng.permutation(x.wl.H)
     perm = lambda a: None if a is None else np.ascontiguousarray(a[pb][:, :, ph])
+    per_head = lambda a: None if a is None else np.ascontiguousarray(a[ph])
     x2 = dataclasses.replace(x, q=perm(x.q), k=perm(x.k), v=perm(x.v), beta=perm(x.beta),
-                             w=perm(x.w), alpha=perm(x.alpha), theta=perm(x.theta))
+                             w=perm(x.w), alpha=perm(x.alpha), theta=perm(x.theta),
+                             beta_logit=perm(x.beta_logit), ub_down=per_head(x.ub_down),
+                             ub_up=per_head(x.ub_up))
     o2, S2 = run_gpu(x2)
     np.testing.assert_array_equal(o2, o1[pb][:, :, ph])
     np.testing.assert_array_equal(S2, S1[pb][:, ph])
