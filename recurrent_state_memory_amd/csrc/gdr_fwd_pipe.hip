@@ -609,10 +609,17 @@ __global__ __launch_bounds__((NWP + NWS + TV / 16) * 64) void gdr_fwd_pipe_kerne
           }
           f32x4 Nc, Nt, Pt;
           const float bn = beta_at(16 * bb + n);
+          // content-aware: beta of rows 4g..4g+3 (a sigmoid each) for all lanes
+          // up front, so that no divergent branch guards them
+          f32x4 br = {0.f, 0.f, 0.f, 0.f};
+          if constexpr (CONTENT) {
+#pragma unroll
+            for (int jj = 0; jj < 4; ++jj) br[jj] = beta_at(16 * bb + 4 * g + jj);
+          }
 #pragma unroll
           for (int jj = 0; jj < 4; ++jj) {
             const int rr = 4 * g + jj;
-            Nc[jj] = (n < rr) ? beta_at(16 * bb + rr) * g0[jj] : 0.f;   // N[rr][n]
+            Nc[jj] = (n < rr) ? (CONTENT ? br[jj] : beta_at(16 * bb + rr)) * g0[jj] : 0.f;   // N[rr][n]
             Nt[jj] = (rr < n) ? bn * g1[jj] : 0.f;                     // N[n][rr]
             Pt[jj] = ((rr == n) ? 1.f : 0.f) - Nt[jj];                  // (I - N)^T
           }
