@@ -108,6 +108,21 @@ def _ptr(t) -> Optional[int]:
     return t.data_ptr()
 
 
+def _expect(t, name: str, shape, dtype, required: bool = True):
+    """Check one argument's presence, shape and dtype (before any pointer is taken,
+    so that a wrong shape can never make a kernel read past an allocation)."""
+    if t is None:
+        if required:
+            raise ValueError(f"gdr: {name} is required")
+        return
+    if tuple(t.shape) != tuple(shape):
+        raise ValueError(f"gdr: {name} has shape {tuple(t.shape)}, expected {tuple(shape)}")
+    if t.dtype != dtype:
+        raise ValueError(f"gdr: {name} has dtype {t.dtype}, expected {dtype}")
+    if not t.is_contiguous():
+        raise ValueError(f"gdr: {name} must be contiguous")
+
+
 def _stream(stream):
     import torch
     s = stream if stream is not None else torch.cuda.current_stream()
@@ -148,29 +163,59 @@ def gdr_chunk_fwd(q, k, v, alpha, w, beta=None, *, theta=None, S0=None, chunk=64
     rotation-decay blocks); beta, w fp32 [B,T,H].  Content-aware erase: pass
     ``beta_logit``, ``ub_down`` [H,r,dv], ``ub_up`` [H,r] instead of ``beta``.
     Returns (o [B,T,H,dv], S_out [B,H,dv,dk] fp32 or None).
+
+    Every tensor's shape, dtype and contiguity is checked against (B, T, H,
+    dk, dv) before anything reaches the library.
     """
     import torch
+    if q.dim() != 4 or k.dim() != 4 or v.dim() != 4:
+        raise ValueError("gdr: q, k and v must be [B,T,H,d]")
     B, T, H, dk = q.shape
     dv = v.shape[-1]
+    io = q.dtype
+    f32 = torch.float32
+    _io(q)
+    _expect(k, "k", (B, T, H, dk), io)
+    _expect(v, "v", (B, T, H, dv), io)
+    rot = theta is not None
+    content = beta_logit is not None
+    gshape = (B, T, H, dk // 2) if rot else (B, T, H, dk)
+    if rot and dk % 2:
+        raise ValueError("gdr: rotation-decay blocks need an even d_k")
+    _expect(alpha, "alpha", gshape, f32)
+    _expect(theta, "theta", gshape, f32, required=False)
+    _expect(w, "w", (B, T, H), f32)
+    if content:
+        if beta is not None:
+            raise ValueError("gdr: pass either beta or beta_logit, not both")
+        if ub_down is None or ub_up is None or ub_up.dim() != 2:
+            raise ValueError("gdr: the content-aware erase needs ub_down [H,r,dv] and ub_up [H,r]")
+        r = ub_up.shape[-1]
+        _expect(beta_logit, "beta_logit", (B, T, H), f32)
+        _expect(ub_down, "ub_down", (H, r, dv), f32)
+        _expect(ub_up, "ub_up", (H, r), f32)
+        _expect(m_carry, "m_carry", (B, H, dv), f32, required=False)
+    else:
+        if ub_down is not None or ub_up is not None or m_carry is not None:
+            raise ValueError("gdr: ub_down, ub_up and m_carry belong to the content-aware erase")
+        _expect(beta, "beta", (B, T, H), f32)
+    _expect(S0, "S0", (B, H, dv, dk), f32, required=False)
     if o is None:
-        o = torch.empty((B, T, H, dv), dtype=q.dtype, device=q.device)
+        o = torch.empty((B, T, H, dv), dtype=io, device=q.device)
+    _expect(o, "o", (B, T, H, dv), io)
     if S_out is None and return_state:
-        S_out = torch.empty((B, H, dv, dk), dtype=torch.float32, device=q.device)
+        S_out = torch.empty((B, H, dv, dk), dtype=f32, device=q.device)
+    _expect(S_out, "S_out", (B, H, dv, dk), f32, required=False)
     a = FwdArgs()
     a.B, a.T, a.H, a.dk, a.dv, a.chunk = B, T, H, dk, dv, chunk
     a.io_dtype = _io(q)
-    if k.dtype != q.dtype or v.dtype != q.dtype or o.dtype != q.dtype:
-        raise ValueError("gdr: q, k, v and o must share one dtype")
-    a.decay = GDR_DECAY_ROT2 if theta is not None else GDR_DECAY_DIAG
+    a.decay = GDR_DECAY_ROT2 if rot else GDR_DECAY_DIAG
     a.q, a.k, a.v, a.alpha, a.theta = map(_ptr, (q, k, v, alpha, theta))
     a.beta, a.w, a.beta_logit = map(_ptr, (beta, w, beta_logit))
     a.ub_down, a.ub_up, a.m_carry = map(_ptr, (ub_down, ub_up, m_carry))
     a.ub_rank = 0 if ub_up is None else int(ub_up.shape[-1])
     a.S0, a.o, a.S_out = _ptr(S0), _ptr(o), _ptr(S_out)
     a.workspace, a.workspace_bytes = None, 0
-    for t in (alpha, theta, beta, w, beta_logit, ub_down, ub_up, m_carry, S0, S_out):
-        if t is not None and t.dtype != torch.float32:
-            raise ValueError("gdr: gates, projections and states must be float32")
     _check(call_chunk_fwd(a, _stream(stream)))
     return o, S_out
 
@@ -180,15 +225,32 @@ def gdr_step_decode(S, q, k, v, alpha, beta, w, *, theta=None, o=None, stream=No
 
     S [N,H,dv,dk] fp32 (overwritten), q,k [N,H,dk], v [N,H,dv], alpha [N,H,dk]
     or gamma [N,H,dk/2] with theta, beta, w [N,H].  Returns o [N,H,dv].
+    Every tensor's shape, dtype and contiguity is checked first.
     """
     import torch
+    if S.dim() != 4:
+        raise ValueError("gdr: S must be [N,H,dv,dk]")
     N, H, dv, dk = S.shape
+    f32 = torch.float32
+    io = q.dtype
+    _io(q)
+    _expect(S, "S", (N, H, dv, dk), f32)
+    _expect(q, "q", (N, H, dk), io)
+    _expect(k, "k", (N, H, dk), io)
+    _expect(v, "v", (N, H, dv), io)
+    rot = theta is not None
+    gshape = (N, H, dk // 2) if rot else (N, H, dk)
+    _expect(alpha, "alpha", gshape, f32)
+    _expect(theta, "theta", gshape, f32, required=False)
+    _expect(beta, "beta", (N, H), f32)
+    _expect(w, "w", (N, H), f32)
     if o is None:
-        o = torch.empty((N, H, dv), dtype=q.dtype, device=q.device)
+        o = torch.empty((N, H, dv), dtype=io, device=q.device)
+    _expect(o, "o", (N, H, dv), io)
     a = StepArgs()
     a.N, a.H, a.dk, a.dv = N, H, dk, dv
     a.io_dtype = _io(q)
-    a.decay = GDR_DECAY_ROT2 if theta is not None else GDR_DECAY_DIAG
+    a.decay = GDR_DECAY_ROT2 if rot else GDR_DECAY_DIAG
     a.q, a.k, a.v, a.alpha, a.theta = map(_ptr, (q, k, v, alpha, theta))
     a.beta, a.w, a.S, a.o = map(_ptr, (beta, w, S, o))
     _check(call_step_decode(a, _stream(stream)))

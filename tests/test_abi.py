@@ -160,3 +160,85 @@ def test_product_path_has_no_oracle_or_fallback():
                 txt = open(os.path.join(dirpath, f)).read()
                 assert "oracle" not in txt.replace("no oracle", ""), f
                 assert "import numpy" not in txt, f
+
+
+# ------------------------------------------------------------ binding checks
+def _cpu_fwd_args(B=2, T=5, H=3, dk=8, dv=8, rot=False, content=False):
+    import torch
+    bf, f32 = torch.bfloat16, torch.float32
+    g = dk // 2 if rot else dk
+    a = dict(q=torch.zeros(B, T, H, dk, dtype=bf), k=torch.zeros(B, T, H, dk, dtype=bf),
+             v=torch.zeros(B, T, H, dv, dtype=bf), alpha=torch.ones(B, T, H, g, dtype=f32),
+             w=torch.zeros(B, T, H, dtype=f32))
+    if rot:
+        a["theta"] = torch.zeros(B, T, H, g, dtype=f32)
+    if content:
+        a.update(beta_logit=torch.zeros(B, T, H, dtype=f32), ub_down=torch.zeros(H, 4, dv),
+                 ub_up=torch.zeros(H, 4))
+    else:
+        a["beta"] = torch.zeros(B, T, H, dtype=f32)
+    return a
+
+
+def test_binding_accepts_good_shapes_then_needs_gpu():
+    """Correct shapes pass every check; the first thing rejected is the CPU device."""
+    for kw in (dict(), dict(rot=True), dict(content=True)):
+        with pytest.raises(ValueError, match="GPU"):
+            gdr.gdr_chunk_fwd(**_cpu_fwd_args(**kw))
+
+
+@pytest.mark.parametrize("name,bad", [
+    ("alpha", lambda a: a["alpha"][..., :4].contiguous()),       # scalar-ish gate, short
+    ("alpha", lambda a: a["alpha"].to(__import__("torch").bfloat16)),
+    ("w", lambda a: a["w"][:, :, :2].contiguous()),
+    ("beta", lambda a: a["beta"][:1].contiguous()),
+    ("k", lambda a: a["k"][:, :4].contiguous()),
+    ("v", lambda a: a["v"].float()),
+    ("S0", lambda a: __import__("torch").zeros(2, 3, 8, 4)),
+    ("S_out", lambda a: __import__("torch").zeros(2, 3, 8, 8, dtype=__import__("torch").bfloat16)),
+    ("o", lambda a: __import__("torch").zeros(2, 5, 3, 4, dtype=__import__("torch").bfloat16)),
+    ("alpha", lambda a: a["alpha"].transpose(1, 2).contiguous().transpose(1, 2)),  # not contiguous
+])
+def test_binding_rejects_bad_argument(name, bad):
+    a = _cpu_fwd_args()
+    a[name] = bad(a)
+    with pytest.raises(ValueError, match=name):
+        gdr.gdr_chunk_fwd(**a)
+
+
+def test_binding_rejects_bad_content_and_rotation_arguments():
+    import torch
+    a = _cpu_fwd_args(rot=True)
+    a["theta"] = torch.zeros(2, 5, 3, 8)                       # per channel, not per pair
+    with pytest.raises(ValueError, match="theta"):
+        gdr.gdr_chunk_fwd(**a)
+    a = _cpu_fwd_args(content=True)
+    a["ub_down"] = torch.zeros(3, 4, 4)
+    with pytest.raises(ValueError, match="ub_down"):
+        gdr.gdr_chunk_fwd(**a)
+    a = _cpu_fwd_args(content=True)
+    a["m_carry"] = torch.zeros(2, 3, 4)
+    with pytest.raises(ValueError, match="m_carry"):
+        gdr.gdr_chunk_fwd(**a)
+    a = _cpu_fwd_args()
+    a["m_carry"] = torch.zeros(2, 3, 8)
+    with pytest.raises(ValueError, match="content-aware"):
+        gdr.gdr_chunk_fwd(**a)
+
+
+def test_decode_binding_checks():
+    import torch
+    bf, f32 = torch.bfloat16, torch.float32
+    N, H, d = 3, 2, 8
+    good = dict(S=torch.zeros(N, H, d, d), q=torch.zeros(N, H, d, dtype=bf),
+                k=torch.zeros(N, H, d, dtype=bf), v=torch.zeros(N, H, d, dtype=bf),
+                alpha=torch.ones(N, H, d), beta=torch.zeros(N, H), w=torch.zeros(N, H))
+    with pytest.raises(ValueError, match="GPU"):
+        gdr.gdr_step_decode(**good)
+    for name, val in (("S", torch.zeros(N, H, d, d, dtype=bf)), ("alpha", torch.ones(N, H)),
+                      ("beta", torch.zeros(N, H, dtype=bf)), ("k", torch.zeros(N, H, d)),
+                      ("v", torch.zeros(N, H, 4, dtype=bf)), ("w", torch.zeros(N, 1))):
+        a = dict(good)
+        a[name] = val
+        with pytest.raises(ValueError, match=name):
+            gdr.gdr_step_decode(**a)

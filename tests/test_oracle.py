@@ -376,3 +376,74 @@ def test_bf16_rounding_ties_to_even():
     vals = np.array([1.0, 1 + 2 ** -8, 1 + 3 * 2 ** -8, -2.5, 3.0e38], np.float32)
     bits = bf16_bits(vals)
     assert list(bits[:4]) == [0x3F80, 0x3F80, 0x3F82, 0xC020]
+
+
+# ---------------------------------------------------------------- error measure
+def test_max_rel_err_hand_cases():
+    """The parity measure is max|x - r| / max|r| over the whole tensor (hand values)."""
+    from oracle.errors import max_rel_err
+    # errors 0.1 and 0.5, reference magnitudes 4 and 2: 0.5 / 4.  (An element-wise
+    # relative error would give 0.25, a mean 0.1, a relative Frobenius norm 0.114.)
+    assert max_rel_err([4.1, 1.5], [4.0, 2.0]) == pytest.approx(0.125, abs=1e-15)
+    # the sign of x and of the difference both count: |-1 - 1| / 1
+    assert max_rel_err([-1.0], [1.0]) == 2.0
+    assert max_rel_err([[0.0, -3.0]], [[0.0, 3.0]]) == 2.0
+    # all-zero reference: the absolute error
+    assert max_rel_err([0.0, -0.25], [0.0, 0.0]) == 0.25
+    assert max_rel_err([0.0], [0.0]) == 0.0
+    # identical tensors and the empty tensor
+    assert max_rel_err(np.arange(6.0).reshape(2, 3), np.arange(6.0).reshape(2, 3)) == 0.0
+    assert max_rel_err(np.zeros((0, 3)), np.zeros((0, 3))) == 0.0
+    # non-finite values never pass a tolerance
+    assert max_rel_err([np.nan, 1.0], [1.0, 1.0]) == math.inf
+    assert max_rel_err([np.inf], [1.0]) == math.inf
+    assert max_rel_err([1.0], [np.nan]) == math.inf
+    # no broadcasting: a shape mismatch is an error
+    with pytest.raises(ValueError):
+        max_rel_err(np.zeros((2, 3)), np.zeros((3,)))
+    with pytest.raises(ValueError):
+        max_rel_err(np.zeros((2, 1)), np.zeros((2, 2)))
+    # float32 input is upcast before subtracting: 1 + 2^-23 vs 1 is not zero
+    assert max_rel_err(np.float32([1 + 2 ** -23]), [1.0]) == pytest.approx(2 ** -23, rel=1e-12)
+
+
+# ---------------------------------------------------------------- strong decay
+@pytest.mark.parametrize("decay", ["diag", "rot2"])
+def test_pure_reset_register(decay):
+    """alpha = 0 (or a zero-magnitude rotation block), beta = w = 1, unit keys: the
+    state forgets everything and holds exactly the last write, S_t = v_t k_t^T, so
+    o_t = v_t (k_t . q_t) -- the reset/register construction of the SFDA page
+    (finite-state expressivity, with delta correction)."""
+    x = _small(decay, T=20)
+    k = x.k.astype(np.float64)
+    k /= np.linalg.norm(k, axis=-1, keepdims=True)
+    ones = np.ones_like(x.w)
+    zero_a = np.zeros_like(x.alpha)
+    rng = np.random.default_rng(3)
+    S0 = rng.standard_normal((2, 3, 6, 8))
+    o, S = seq.forward(x.q, k, x.v, ones, zero_a, beta=ones, theta=x.theta, decay=decay, S0=S0)
+    q = x.q.astype(np.float64)
+    v = x.v.astype(np.float64)
+    o_ref = v * np.sum(k * q, axis=-1)[..., None]
+    np.testing.assert_allclose(o, o_ref, rtol=0, atol=1e-14)
+    S_ref = v[:, -1, :, :, None] * k[:, -1, :, None, :]
+    np.testing.assert_allclose(S, S_ref, rtol=0, atol=1e-14)
+
+
+def test_strong_decay_closed_form():
+    """beta = 0 with per-token decays far below the fp32 range of a running product
+    (alpha in [1e-3, 0.01], cumulative log-decay below -150 within 32 tokens): the
+    oracle still gives S_t = S_0 Gamma_t exactly (fp64 has the range)."""
+    x = _small("diag", T=48)
+    rng = np.random.default_rng(4)
+    a = rng.uniform(1e-3, 0.01, size=x.alpha.shape)
+    S0 = rng.standard_normal((2, 3, 6, 8))
+    o, S = seq.forward(x.q, x.k, x.v, x.w, a, beta=np.zeros_like(x.w), S0=S0)
+    G = np.cumprod(a, axis=1)                                   # [B,T,H,dk]
+    lg = np.log(G[:, 31])
+    assert lg.max() < -150                         # every channel leaves fp32's range
+    q = x.q.astype(np.float64)
+    o_ref = np.einsum("bhvk,bthk,bthk->bthv", S0, G, q)
+    scale = np.einsum("bhvk,bthk,bthk->bthv", np.abs(S0), G, np.abs(q))   # sum of |terms|
+    assert np.all(np.abs(o - o_ref) <= 1e-13 * scale)
+    np.testing.assert_allclose(S, S0 * G[:, -1, :, None, :], rtol=1e-12, atol=0)
