@@ -29,6 +29,7 @@
 // gates sigmoid(b_x + u_h . m) with u_h = B_h^T a_h.
 #include "gdr_kernels.h"
 #include "gdr_mfma.h"
+#include "gdr_token.h"
 
 namespace gdr {
 
@@ -186,9 +187,13 @@ __global__ __launch_bounds__(TV / 16 * 64) void gdr_fwd_kernel(FwdParams p) {
                 NCT = C::NCT, NKC = C::NKC, NKT = C::NKT, NCW = C::NCW;
 
   __shared__ __attribute__((aligned(16))) T sKp[L * RSK];
-  __shared__ __attribute__((aligned(16))) T sKh[L * RSK];   // reused for W after stage G
+  // Kh (reused for W after stage G) and K-^T, contiguous: a chunk that takes the
+  // token path keeps its fp32 transition [L][DK] there instead
+  __shared__ __attribute__((aligned(16))) T sKhKm[L * RSK + DK * RSL];
+  static_assert(sizeof(T) * (L * RSK + DK * RSL) >= sizeof(float) * L * DK, "raw transition");
+  T* const sKh = sKhKm;
+  T* const sKmT = sKhKm + L * RSK;
   __shared__ __attribute__((aligned(16))) T sQp[L * RSK];
-  __shared__ __attribute__((aligned(16))) T sKmT[DK * RSL];
   __shared__ __attribute__((aligned(16))) T sA[L * RSL];
   __shared__ __attribute__((aligned(16))) T sM[L * RSL];
   __shared__ __attribute__((aligned(16))) T sTd[NB * 16 * RST];
@@ -202,6 +207,7 @@ __global__ __launch_bounds__(TV / 16 * 64) void gdr_fwd_kernel(FwdParams p) {
   __shared__ float sMean[CONTENT ? TV : 1];   // previous window's mean output
   __shared__ float sRed[CONTENT ? 64 : 1];
   __shared__ float sS[CONTENT ? 64 : 1];
+  __shared__ int sFlag[NW];   // per wave: a channel's chunk decay leaves the split form's range
 
   const int tid = threadIdx.x;
   const int l = tid & 63, wv = tid >> 6;
@@ -330,9 +336,13 @@ __global__ __launch_bounds__(TV / 16 * 64) void gdr_fwd_kernel(FwdParams p) {
     lds_barrier();
 
     // ------------------------------------------------------------ stage P2
+    // running products before this segment (pre) and over the chunk (tot); the
+    // chunk takes the token path (gdr_token.h) when some channel's Gamma_L
+    // leaves the split form's range
+    f32x2 pre = {1.f, DECAY == 0 ? 1.f : 0.f};
+    f32x2 tot = pre;
+    bool in_range = true;
     if (prep) {
-      f32x2 pre = {1.f, DECAY == 0 ? 1.f : 0.f};
-      f32x2 tot = pre;
 #pragma unroll
       for (int s = 0; s < NSEG; ++s) {
         const f32x2 x = sSeg[s * NP + pp];
@@ -349,6 +359,35 @@ __global__ __launch_bounds__(TV / 16 * 64) void gdr_fwd_kernel(FwdParams p) {
         }
       }
       if (seg == 0) sGL[pp] = tot;
+      in_range = decay_in_range<DECAY>(tot);
+    }
+    {
+      const unsigned long long bad = __ballot(!in_range);
+      if (l == 0) sFlag[wv] = bad != 0ull;
+    }
+    lds_barrier();
+    int any_bad = 0;
+#pragma unroll
+    for (int w = 0; w < NW; ++w) any_bad |= sFlag[w];
+    const bool token_path = __builtin_amdgcn_readfirstlane(any_bad) != 0;
+    if (prep && token_path) {
+      // raw keys and queries into K+ and Q+, the transition (ROT2: gamma cos,
+      // gamma sin per pair) as fp32 into Kh|K-^T
+      float* sTr = (float*)sKhKm;
+#pragma unroll
+      for (int r = 0; r < TPS; ++r) {
+        const int row = seg * TPS + r;
+        Pair<T>::store(sKp + row * RSK + 2 * pp, RP::cvt(R.k[r]));
+        Pair<T>::store(sQp + row * RSK + 2 * pp, RP::cvt(R.q[r]));
+        f32x2 z = R.a[r];
+        if constexpr (DECAY != 0) {
+          float sn, cs;
+          __sincosf(z.y, &sn, &cs);
+          z = f32x2{z.x * cs, z.x * sn};
+        }
+        *(f32x2*)(sTr + row * DK + 2 * pp) = z;
+      }
+    } else if (prep) {
 #pragma unroll
       for (int r4 = 0; r4 < TPS; r4 += 4) {
         float km0[4], km1[4];
@@ -392,6 +431,17 @@ __global__ __launch_bounds__(TV / 16 * 64) void gdr_fwd_kernel(FwdParams p) {
       load_raw<T, DK, L, TV, DECAY, CONTENT>(R, p, c0 + L, pp, seg, tid, b, h, v0);
     lds_barrier();
 
+    if (token_path) {
+      // ---------------------------------------------------------- token path
+      token_steps<DK, DECAY, T>(
+          Sacc, (const float*)sKhKm, sKp, sQp, RSK, sV + 16 * wv + n, RSV, sBeta, sBW,
+          min(L, Tn - c0), [&](int t, float ov) {
+            if (g == 0) {
+              go[((size_t)(b * Tn + c0 + t) * H + h) * DV + v0 + 16 * wv + n] = (T)ov;
+              if constexpr (CONTENT) colsum += ov;
+            }
+          });
+    } else {
     // ------------------------------------------------------------ stage G
     {
       constexpr int NTRI = NB * (NB + 1) / 2;
@@ -565,6 +615,8 @@ __global__ __launch_bounds__(TV / 16 * 64) void gdr_fwd_kernel(FwdParams p) {
         }
       }
     }
+
+    }   // split form
 
     if constexpr (CONTENT) {
       const int cend = c0 + L;

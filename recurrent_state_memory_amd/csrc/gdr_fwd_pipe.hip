@@ -29,6 +29,7 @@
 // formed by the consumers and read by the solve after one idle step.
 #include "gdr_kernels.h"
 #include "gdr_mfma.h"
+#include "gdr_token.h"
 
 namespace gdr {
 namespace pipe {
@@ -93,25 +94,48 @@ struct Cfg {
   static_assert(L * VPR % (NWP * 64) == 0 || L * VPR < NWP * 64, "value tile load split");
 };
 
+// Bytes of one chunk in raw form for the token path (gdr_token.h): the
+// transition as fp32 per channel, then raw keys and queries.
+template <int DK>
+constexpr int raw_bytes() { return L * DK * (4 + 2 + 2); }
+
+template <int DK>
+constexpr int raw_pad() {   // bf16 elements that extend Kp|Qp|KhT to raw_bytes()
+  constexpr int have = 2 * (2 * L * (DK == 128 ? 160 : DK + 8) + DK * RSL);
+  return raw_bytes<DK>() > have ? (raw_bytes<DK>() - have + 15) / 16 * 8 : 8;
+}
+
 // Prep outputs of one chunk (3 slots: written for i+2, read for i+1 and i).
+// Kp, Qp, KhT and pad are contiguous: a chunk whose decay leaves the split
+// form's range holds its raw transition, keys and queries there instead
+// (written by the solve, read by the consumer's token path).
 template <int DK, int TV>
 struct SlotA {
   using C = Cfg<DK, TV>;
   bf Kp[L * C::RSK];
   bf Qp[L * C::RSK];
   bf KhT[DK * RSL];
+  bf pad[raw_pad<DK>()];
   bf V[L * C::RSV];
   float beta[L];   // beta (content-aware: the logit b_x)
   float bw[L];     // beta * w (content-aware: w)
   f32x2 GL[C::NP];
+  int flag[NWP];   // per prep wave: some channel's Gamma_L is out of range
 };
+
+template <int DK, int TV>
+__device__ inline bool slot_out_of_range(const SlotA<DK, TV>& A) {
+  const int4 f = *(const int4*)A.flag;
+  return __builtin_amdgcn_readfirstlane(f.x | f.y | f.z | f.w) != 0;
+}
 
 // 16-byte LDS reads of beta, bw and GL rely on these offsets
 template <int DK, int TV>
 constexpr bool slot_aligned() {
   using S = SlotA<DK, TV>;
   return offsetof(S, beta) % 16 == 0 && offsetof(S, bw) % 16 == 0 && offsetof(S, GL) % 16 == 0 &&
-         sizeof(S) % 16 == 0;
+         offsetof(S, flag) % 16 == 0 && offsetof(S, V) % 16 == 0 && sizeof(S) % 16 == 0 &&
+         offsetof(S, V) - offsetof(S, Kp) >= (size_t)raw_bytes<DK>();
 }
 static_assert(slot_aligned<128, 64>() && slot_aligned<128, 32>() && slot_aligned<64, 32>() &&
                   slot_aligned<128, 128>() && slot_aligned<64, 64>(),
@@ -325,6 +349,10 @@ __device__ __forceinline__ void prep_chunk(Shared<DK, TV>& sh, const Raw<Cfg<DK,
     tot = mulz(tot, tp);
   }
   if (seg == 0) A.GL[pp] = tot;
+  {   // chunk-level range check of the split form (gdr_token.h)
+    const unsigned long long bad = __ballot(!decay_in_range<DECAY>(tot));
+    if (l == 0) A.flag[pw] = bad != 0ull;
+  }
   if constexpr (NEXT) {
     __builtin_amdgcn_sched_barrier(0);
     load_part<DK, TV, DECAY, 2>(Rn, rs, cn, pp, seg, ptid);
@@ -410,6 +438,53 @@ __device__ __forceinline__ void prep_chunk(Shared<DK, TV>& sh, const Raw<Cfg<DK,
       }
       *(bf16x4*)(A.KhT + (2 * pp) * RSL + seg * TPS + r4) = m0;
       *(bf16x4*)(A.KhT + (2 * pp + 1) * RSL + seg * TPS + r4) = m1;
+    }
+  }
+}
+
+// Raw form of chunk c0 .. c0+L-1 for the token path, written by the 4 solve
+// waves (lane id ix in 0..255: token ix / 8, channels (ix % 8) * DK / 8 ...):
+// the transition as fp32 per channel (ROT2: gamma cos theta, gamma sin theta
+// per pair), then the raw keys and queries.  Tokens past T read as zero.
+template <int DK, int TV, int DECAY>
+__device__ inline void stage_raw(SlotA<DK, TV>& A, const Rsrc& rs, int c0, int ix) {
+  constexpr int CPL = DK / 8;   // channels per lane
+  static_assert(NWS * 64 == 8 * L, "one solve lane per (token, channel block)");
+  char* raw = (char*)A.Kp;
+  float* ra = (float*)raw;
+  bf* rk = (bf*)(raw + L * DK * 4);
+  bf* rq = rk + L * DK;
+  const int t = ix >> 3, c = (ix & 7) * CPL;
+  const int tok = c0 + t;
+#pragma unroll
+  for (int u = 0; u < CPL; u += 8) {
+    const auto xk = __builtin_amdgcn_raw_buffer_load_b128(rs.k, (c + u) * 2, tok * rs.sk, 0);
+    const auto xq = __builtin_amdgcn_raw_buffer_load_b128(rs.q, (c + u) * 2, tok * rs.sk, 0);
+    *(uint4*)(rk + t * DK + c + u) = uint4{xk[0], xk[1], xk[2], xk[3]};
+    *(uint4*)(rq + t * DK + c + u) = uint4{xq[0], xq[1], xq[2], xq[3]};
+  }
+  if constexpr (DECAY == 0) {
+#pragma unroll
+    for (int u = 0; u < CPL; u += 4) {
+      const auto x = __builtin_amdgcn_raw_buffer_load_b128(rs.a, (c + u) * 4, tok * rs.sa, 0);
+      *(uint4*)(ra + t * DK + c + u) = uint4{x[0], x[1], x[2], x[3]};
+    }
+  } else {
+#pragma unroll
+    for (int u = 0; u < CPL / 2; u += 4) {   // pairs c/2 + u .. c/2 + u + 3
+      const auto xg = __builtin_amdgcn_raw_buffer_load_b128(rs.a, (c / 2 + u) * 4, tok * rs.sa, 0);
+      const auto xt = __builtin_amdgcn_raw_buffer_load_b128(rs.th, (c / 2 + u) * 4, tok * rs.sa, 0);
+      f32x4 lo, hi;
+#pragma unroll
+      for (int e = 0; e < 4; ++e) {
+        float sn, cs;
+        __sincosf(__uint_as_float(xt[e]), &sn, &cs);
+        const float gm = __uint_as_float(xg[e]);
+        (e < 2 ? lo : hi)[2 * (e & 1)] = gm * cs;
+        (e < 2 ? lo : hi)[2 * (e & 1) + 1] = gm * sn;
+      }
+      *(f32x4*)(ra + t * DK + c + 2 * u) = lo;
+      *(f32x4*)(ra + t * DK + c + 2 * u + 4) = hi;
     }
   }
 }
@@ -556,6 +631,7 @@ __global__ __launch_bounds__((NWP + NWS + TV / 16) * 64) void gdr_fwd_pipe_kerne
       nwt = __uint_as_float(__builtin_amdgcn_raw_buffer_load_b32(rw, tb, 0, 0));
     }
     float s_win = 0.f;   // content-aware: s_c = u_h . m_c of the current window
+    const Rsrc rss = make_rsrcs<DK, TV, DECAY>(p, b, h, v0);
     for (int it = 0; it < nsteps; ++it) {
       const int jp = CONTENT ? block_at(it) : it;
       if (sw == NWS - 1 && (CONTENT ? (jp >= 0 && jp < nchunks) : (it < nchunks))) {
@@ -594,7 +670,11 @@ __global__ __launch_bounds__((NWP + NWS + TV / 16) * 64) void gdr_fwd_pipe_kerne
             sBc[vj % 3][1][l] = bt * A.bw[l];
           }
         }
-        if (sw < 2) {
+        if (slot_out_of_range(A)) {
+          // some channel leaves the split form's range: the consumer runs this
+          // chunk token by token from its raw inputs
+          stage_raw<DK, TV, DECAY>(sh.a[vj % 3], rss, j * L, sw * 64 + l);
+        } else if (sw < 2) {
           // diagonal block bb: N and N^T as accumulator tiles, then
           // T_bb = (I + N)^{-1} = (I - N)(I + N^2)(I + N^4)(I + N^8).
           // mul(Q, Y) = C(Q^T Y): a tile feeds the left operand as its transpose.
@@ -698,6 +778,33 @@ __global__ __launch_bounds__((NWP + NWS + TV / 16) * 64) void gdr_fwd_pipe_kerne
         const SlotA<DK, TV>& A = sh.a[vi % 3];
         const SlotS& S = sh.s[vi & 1];
         const int c0 = i * L;
+        if (slot_out_of_range(A)) {
+          // token path (gdr_token.h): raw transition, keys and queries staged by
+          // the solve; o_t[n] is stored as one bf16 by the lanes with g == 0
+          const char* raw = (const char*)A.Kp;
+          const float* bt = CONTENT ? sBc[vi % 3][0] : A.beta;
+          const float* bwp = CONTENT ? sBc[vi % 3][1] : A.bw;
+          float fsum = 0.f;
+          token_steps<DK, DECAY, bf>(
+              Sacc, (const float*)raw, (const bf*)(raw + L * DK * 4),
+              (const bf*)(raw + L * DK * 6), DK, A.V + 16 * cw + n, RSV, bt, bwp,
+              min(L, Tn - c0), [&](int t, float ov) {
+                if (g == 0) {
+                  const bf ob = (bf)ov;
+                  __builtin_amdgcn_raw_buffer_store_b16(*(const unsigned short*)&ob, ro, 2 * n,
+                                                        (c0 + t) * so, 0);
+                }
+                fsum += ov;
+              });
+          if constexpr (CONTENT) {
+            // window sums: value channel 4g + jj is kept by a lane of group g
+#pragma unroll
+            for (int jj = 0; jj < 4; ++jj) {
+              const float x = __shfl(fsum, 4 * g + jj);
+              colsum[jj] += n == 0 ? x : 0.f;
+            }
+          }
+        } else {
         // R = diag(bw) V - diag(beta) K+ S^T;  Qs^T = (Q+ S^T)^T, kept transposed
         // (lane holds one token and four value channels) for 8-byte o stores
         frag Sf[NKC];
@@ -746,16 +853,6 @@ __global__ __launch_bounds__((NWP + NWS + TV / 16) * 64) void gdr_fwd_pipe_kerne
           // read by the solve of the next window's first block
 #pragma unroll
           for (int jj = 0; jj < 4; ++jj) colsum[jj] += O0[jj] + O1[jj];
-          if (i % SPC == SPC - 1) {
-#pragma unroll
-            for (int jj = 0; jj < 4; ++jj) {
-              float sum = colsum[jj];
-#pragma unroll
-              for (int off = 1; off < 16; off <<= 1) sum += __shfl_xor(sum, off);
-              if (n == 0) sMean[16 * cw + 4 * g + jj] = sum * (1.f / (float)(SPC * L));
-              colsum[jj] = 0.f;
-            }
-          }
         }
         // S <- S Gamma_L + Dl^T K- = (S + Dl^T Kh) Gamma_L, since K- = Kh Gamma_L
         // column-wise (per channel, or per rotation pair)
@@ -780,6 +877,21 @@ __global__ __launch_bounds__((NWP + NWS + TV / 16) * 64) void gdr_fwd_pipe_kerne
           typedef __attribute__((ext_vector_type(2))) unsigned u32x2;
           __builtin_amdgcn_raw_buffer_store_b64(*(const u32x2*)&ox0, ro, olane, c0 * so, 0);
           __builtin_amdgcn_raw_buffer_store_b64(*(const u32x2*)&ox1, ro, olane, (c0 + 16) * so, 0);
+        }
+        }   // split form
+        if constexpr (CONTENT) {
+          // at a window's last block its per-channel mean goes to LDS, to be
+          // read by the solve of the next window's first block
+          if (i % SPC == SPC - 1) {
+#pragma unroll
+            for (int jj = 0; jj < 4; ++jj) {
+              float sum = colsum[jj];
+#pragma unroll
+              for (int off = 1; off < 16; off <<= 1) sum += __shfl_xor(sum, off);
+              if (n == 0) sMean[16 * cw + 4 * g + jj] = sum * (1.f / (float)(SPC * L));
+              colsum[jj] = 0.f;
+            }
+          }
         }
       }
       lds_barrier();

@@ -46,13 +46,27 @@ def run_gpu(x, chunk=None, S0=None, m_carry=None, alias=False, return_m=False):
 
 
 def oracle_heads(x, heads=None, S0=None, m_carry=None, return_m=False):
-    """fp64 oracle on the (b, h) pairs in ``heads`` (all when None).
+    """fp64 oracle on the (b, h) pairs in ``heads``, or on every head at once with
+    one call vectorised over (B, H) when ``heads`` is None.
 
     Returns dict (b, h) -> (o [T, dv], S [dv, dk] (, m [dv])).
     """
     wl = x.wl
     if heads is None:
-        heads = [(b, h) for b in range(wl.B) for h in range(wl.H)]
+        kw = {}
+        if wl.content:
+            kw = dict(beta_logit=x.beta_logit, ub_down=x.ub_down, ub_up=x.ub_up,
+                      chunk=wl.chunk, m_carry=m_carry, return_m=return_m)
+        r = seq.forward(x.q, x.k, x.v, x.w, x.alpha, beta=x.beta, theta=x.theta,
+                        decay=wl.decay, S0=S0, **kw)
+        out = {}
+        for b in range(wl.B):
+            for h in range(wl.H):
+                item = (r[0][b, :, h], r[1][b, h])
+                if return_m and wl.content:
+                    item = item + (r[2][b, h],)
+                out[(b, h)] = item
+        return out
     out = {}
     for b, h in heads:
         sl = (slice(b, b + 1), slice(None), slice(h, h + 1))
