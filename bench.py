@@ -60,6 +60,15 @@ def algorithmic_flops(wl, L: int) -> float:
     return per_th * wl.B * wl.T * wl.H
 
 
+def wy_block(wl) -> int:
+    """Token block of the WY solve that actually runs for this workload: the
+    pipelined bf16 kernel (d in {64, 128}) always uses 32-token blocks; the
+    sequential-stage kernel uses min(chunk, 64), or 32 for fp32 at d = 128."""
+    if wl.io == "bf16" and wl.dk in (64, 128) and (not wl.content or wl.chunk % 32 == 0):
+        return 32
+    return min(wl.chunk, 32 if (wl.io == "f32" and wl.dk == 128) else 64)
+
+
 def _code_only(text: str) -> str:
     """C/C++ source with comments removed and whitespace runs collapsed."""
     text = re.sub(r"/\*.*?\*/", " ", text, flags=re.S)
@@ -139,51 +148,94 @@ def _decode_closure():
     return step, d
 
 
-def _time(step, steps, warmup):
+MALL_BYTES = 256 << 20   # MI355X Infinity Cache
+
+
+def _time(step, steps, warmup, flush=False):
+    """Seconds for ``steps`` launches after ``warmup`` untimed ones, with HIP
+    events on the stream the launches use.  With ``flush`` every launch is timed
+    on its own and a 512 MB buffer is written between launches, so inputs that
+    would fit in the 256 MB Infinity Cache are read from HBM each time."""
     import torch
+    scratch = torch.empty(2 * MALL_BYTES // 4, dtype=torch.float32, device="cuda") if flush else None
     for _ in range(warmup):
         step()
+        if flush:
+            scratch.fill_(1.0)
     torch.cuda.synchronize()
     stream = torch.cuda.current_stream()
-    e0 = torch.cuda.Event(enable_timing=True)
-    e1 = torch.cuda.Event(enable_timing=True)
     t0 = time.perf_counter()
-    e0.record(stream)
-    for _ in range(steps):
+    if not flush:
+        e0 = torch.cuda.Event(enable_timing=True)
+        e1 = torch.cuda.Event(enable_timing=True)
+        e0.record(stream)
+        for _ in range(steps):
+            step()
+        e1.record(stream)
+        torch.cuda.synchronize()
+        return e0.elapsed_time(e1) / 1e3, time.perf_counter() - t0
+    ev = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True))
+          for _ in range(steps)]
+    for a, b in ev:
+        scratch.fill_(1.0)
+        a.record(stream)
         step()
-    e1.record(stream)
+        b.record(stream)
     torch.cuda.synchronize()
-    wall = time.perf_counter() - t0
-    return e0.elapsed_time(e1) / 1e3, wall
+    return sum(a.elapsed_time(b) for a, b in ev) / 1e3, time.perf_counter() - t0
+
+
+def _cpu_model() -> str:
+    try:
+        for ln in open("/proc/cpuinfo"):
+            if ln.lower().startswith("model name"):
+                return ln.split(":", 1)[1].strip()
+    except OSError:
+        pass
+    return "unknown"
 
 
 def cpu_baseline(wl, x, budget_s: float = 15.0):
-    """Time the fp64 oracle (single thread) on all B*H heads over a prefix of
-    the sequence sized to roughly ``budget_s`` seconds; tokens/s = B * T_sample / s."""
+    """Time the fp64 oracle on this host's cores: one worker thread per group of
+    batch rows (numpy releases the interpreter lock inside its array operations),
+    BLAS single-threaded in each, all B*H heads over a prefix of the sequence
+    sized to roughly ``budget_s`` seconds; tokens/s = B * T_sample / s."""
+    import concurrent.futures as cf
     import numpy as np
     from threadpoolctl import threadpool_limits
     from oracle import seq
-    with threadpool_limits(limits=1):
+
+    cores = max(1, min(16, len(os.sched_getaffinity(0))))
+    workers = min(cores, wl.B * wl.H)
+    # (b, h-range) slices: one per worker, heads split when B is small
+    per_b = max(1, -(-workers // wl.B))
+    hs = -(-wl.H // per_b)
+    parts = [(b, h0, min(wl.H, h0 + hs)) for b in range(wl.B) for h0 in range(0, wl.H, hs)]
+    workers = min(workers, len(parts))
+
+    def run(part, T_s):
+        b, h0, h1 = part
+        sl = (slice(b, b + 1), slice(0, T_s), slice(h0, h1))
+        return seq.forward(x.q[sl], x.k[sl], x.v[sl], x.w[sl], x.alpha[sl],
+                           beta=x.beta[sl], decay=wl.decay,
+                           theta=None if x.theta is None else x.theta[sl])[0]
+
+    with threadpool_limits(limits=1), cf.ThreadPoolExecutor(max_workers=workers) as ex:
         # probe the per-token cost on a short prefix, then size the sample
         probe = 32
-        sl = slice(0, probe)
         t0 = time.perf_counter()
-        seq.forward(x.q[:, sl], x.k[:, sl], x.v[:, sl], x.w[:, sl], x.alpha[:, sl],
-                    beta=x.beta[:, sl], decay=wl.decay,
-                    theta=None if x.theta is None else x.theta[:, sl])
+        list(ex.map(lambda pt: run(pt, probe), parts))
         per_tok = (time.perf_counter() - t0) / probe
         T_s = int(max(64, min(wl.T, budget_s / max(per_tok, 1e-9))))
-        sl = slice(0, T_s)
         t0 = time.perf_counter()
-        o, _ = seq.forward(x.q[:, sl], x.k[:, sl], x.v[:, sl], x.w[:, sl], x.alpha[:, sl],
-                           beta=x.beta[:, sl], decay=wl.decay,
-                           theta=None if x.theta is None else x.theta[:, sl])
+        outs = list(ex.map(lambda pt: run(pt, T_s), parts))
         secs = time.perf_counter() - t0
-    assert np.all(np.isfinite(o))
-    return {"value": round(wl.B * T_s / secs, 2), "unit": "tokens/s", "cores": 1,
+    assert all(np.all(np.isfinite(o)) for o in outs)
+    return {"value": round(wl.B * T_s / secs, 2), "unit": "tokens/s", "cores": workers,
             "kind": "oracle",
-            "sample": (f"fp64 numpy token-by-token oracle, single thread, all {wl.B}x{wl.H} "
-                       f"heads, first {T_s} of {wl.T} tokens, {secs:.1f} s")}
+            "sample": (f"fp64 numpy token-by-token oracle, {workers} worker threads "
+                       f"(BLAS single-threaded) on {_cpu_model()}, all {wl.B}x{wl.H} heads, "
+                       f"first {T_s} of {wl.T} tokens, {secs:.1f} s")}
 
 
 def main(argv=None):
@@ -233,13 +285,14 @@ def main(argv=None):
 
     wl = WORKLOADS[a.workload]
     step, x = _fwd_closure(wl)
-    secs, wall = _time(step, a.steps, a.warmup)
+    flush = algorithmic_bytes(wl) < MALL_BYTES
+    secs, wall = _time(step, a.steps, a.warmup, flush=flush)
     per = secs / a.steps
     tokens = wl.B * wl.T
     value = tokens / per
     from recurrent_state_memory_amd.build import ARCH  # noqa: F401  (built for gfx950)
     nbytes = algorithmic_bytes(wl)
-    L_eff = min(wl.chunk, 64)
+    L_eff = wy_block(wl)
     flops = algorithmic_flops(wl, L_eff)
     achieved = nbytes / per / 1e9
     mfma_peak = MFMA_BF16_PEAK_TFS if wl.io == "bf16" else MFMA_F32_PEAK_TFS
@@ -259,6 +312,7 @@ def main(argv=None):
         "data": "synthetic (seeded; q,k L2-normalised, gates from the stated distributions)",
         "config": {
             "workload": (f"{wl.name}: B={wl.B} H={wl.H} T={wl.T} d_k=d_v={wl.dk} chunk={wl.chunk} "
+                         f"({L_eff}-token WY blocks{', MALL flushed between launches' if flush else ''}) "
                          f"{wl.io} q/k/v, fp32 gates and state, "
                          f"{'2x2 rotation-decay' if wl.decay == 'rot2' else 'per-channel decay'}"
                          f"{', content-aware erase' if wl.content else ''}"),

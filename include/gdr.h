@@ -44,6 +44,16 @@
  *     exception and no abort crosses this ABI.
  *   - NaN / Inf inputs are not checked; they propagate.
  *   - Calls on different streams touching disjoint outputs may overlap.
+ *
+ * Decay range.  Every decay factor (alpha, or the rotation magnitude gamma)
+ * may take any value in [0, 1], including 0 (a full reset of that key channel,
+ * the register/reset construction of the SFDA technical summary, finite-state
+ * expressivity) and subnormals.  The chunked kernels pair Gamma_r k with
+ * Gamma_r^{-1} k inside a block; a block in which some key channel's running
+ * decay falls below e^-40 is computed token by token in fp32 instead, so no
+ * legal input produces an overflow or NaN and results stay exact to rounding.
+ * Such blocks run several times slower than the matrix-core path.  Factors
+ * above 1 are outside the supported domain and are not checked.
  */
 #ifndef GDR_H_
 #define GDR_H_
@@ -81,16 +91,20 @@ typedef struct gdr_fwd_args {
                         /* {32, 64, 128}                                       */
   int32_t chunk;        /* L, in {16, 32, 64, 128}.  For the content-aware     */
                         /* erase it is the window of the output mean and       */
-                        /* changes the result.  Otherwise it is the WY block   */
-                        /* size and changes only rounding; 128 runs as two     */
-                        /* 64-token blocks.                                    */
+                        /* changes the result.  Otherwise it only selects the  */
+                        /* WY block size, which changes rounding, not the      */
+                        /* result: bf16 io at dk in {64, 128} runs 32-token    */
+                        /* blocks whatever the value; fp32 io, dk = 32, a      */
+                        /* 16-token content window and T*H*dk >= 2^29 run      */
+                        /* min(chunk, 64)-token blocks (32 for fp32 at         */
+                        /* dk = 128).                                          */
   int32_t io_dtype;     /* gdr_dtype of q, k, v and o                          */
   int32_t decay;        /* gdr_decay                                           */
   const void *q;        /* [B,T,H,dk] io_dtype                                 */
   const void *k;        /* [B,T,H,dk] io_dtype                                 */
   const void *v;        /* [B,T,H,dv] io_dtype                                 */
-  const float *alpha;   /* DIAG: [B,T,H,dk] decays in (0,1].                   */
-                        /* ROT2: [B,T,H,dk/2] block magnitudes gamma in (0,1]. */
+  const float *alpha;   /* DIAG: [B,T,H,dk] decays in [0,1].                   */
+                        /* ROT2: [B,T,H,dk/2] block magnitudes gamma in [0,1]. */
   const float *theta;   /* ROT2: [B,T,H,dk/2] angles (radians).  DIAG: NULL.   */
   const float *beta;    /* [B,T,H] erase strengths; NULL iff content-aware.    */
   const float *w;       /* [B,T,H] scalar write gates.                         */
@@ -130,7 +144,7 @@ typedef struct gdr_step_args {
   const void *q;        /* [N,H,dk]                                            */
   const void *k;        /* [N,H,dk]                                            */
   const void *v;        /* [N,H,dv]                                            */
-  const float *alpha;   /* DIAG [N,H,dk]; ROT2 gamma [N,H,dk/2]                */
+  const float *alpha;   /* DIAG [N,H,dk]; ROT2 gamma [N,H,dk/2]; in [0,1]      */
   const float *theta;   /* ROT2 [N,H,dk/2]; DIAG NULL                          */
   const float *beta;    /* [N,H]                                               */
   const float *w;       /* [N,H]                                               */

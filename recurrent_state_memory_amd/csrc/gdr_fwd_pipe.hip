@@ -27,6 +27,8 @@
 // Content-aware erase (CONTENT): one workgroup covers all value channels of a
 // (b, h); beta of each window comes from the previous window's mean output,
 // formed by the consumers and read by the solve after one idle step.
+#include <type_traits>
+
 #include "gdr_kernels.h"
 #include "gdr_mfma.h"
 #include "gdr_token.h"
@@ -123,11 +125,6 @@ struct SlotA {
   int flag[NWP];   // per prep wave: some channel's Gamma_L is out of range
 };
 
-template <int DK, int TV>
-__device__ inline bool slot_out_of_range(const SlotA<DK, TV>& A) {
-  const int4 f = *(const int4*)A.flag;
-  return __builtin_amdgcn_readfirstlane(f.x | f.y | f.z | f.w) != 0;
-}
 
 // 16-byte LDS reads of beta, bw and GL rely on these offsets
 template <int DK, int TV>
@@ -283,11 +280,11 @@ __device__ inline float xor_lanes(float v, int d, int l) {
 // With NEXT, the raw loads of the chunk at token cn go into Rn, spread over the
 // step in four groups so that the prep waves do not all stall on a full
 // vector-memory queue at the start of every step.
-template <int DK, int TV, int DECAY, bool NEXT>
+template <int DK, int TV, int DECAY, bool NEXT, bool ROBUST>
 __device__ __forceinline__ void prep_chunk(Shared<DK, TV>& sh, const Raw<Cfg<DK, TV>::TPS, Cfg<DK, TV>::VLD>& R,
                                            Raw<Cfg<DK, TV>::TPS, Cfg<DK, TV>::VLD>& Rn, const Rsrc& rs, int cn,
                                            int it, int vs, int Tn, int pw, int l, int pl,
-                                           int seg, int pp, int ptid) {
+                                           int seg, int pp, int ptid, int& any_out) {
   using C = Cfg<DK, TV>;
   constexpr int PPW = C::PPW, NSEG = C::NSEG, TPS = C::TPS, RSK = C::RSK, RSV = C::RSV,
                 VPR = C::VPR;
@@ -351,7 +348,11 @@ __device__ __forceinline__ void prep_chunk(Shared<DK, TV>& sh, const Raw<Cfg<DK,
   if (seg == 0) A.GL[pp] = tot;
   {   // chunk-level range check of the split form (gdr_token.h)
     const unsigned long long bad = __ballot(!decay_in_range<DECAY>(tot));
-    if (l == 0) A.flag[pw] = bad != 0ull;
+    if constexpr (ROBUST) {
+      if (l == 0) A.flag[pw] = bad != 0ull;
+    } else {
+      any_out |= bad != 0ull;
+    }
   }
   if constexpr (NEXT) {
     __builtin_amdgcn_sched_barrier(0);
@@ -540,7 +541,35 @@ __global__ __launch_bounds__((NWP + NWS + TV / 16) * 64) void gdr_fwd_pipe_kerne
     lds_barrier();
   }
 
+  // Each role runs the pipeline twice at most.  Pass 1 (ROBUST = false) is the
+  // matrix-core path only; the prep records whether any block of this (b, h)
+  // left the split form's range, in which case pass 1's results are invalid
+  // and pass 2 (ROBUST = true) recomputes the whole (b, h) with a range check
+  // per block and the token path for out-of-range blocks, overwriting every
+  // output of pass 1 (same lanes, same addresses, in program order).  Keeping
+  // the two apart leaves the hot loop free of data-dependent branches, which
+  // otherwise cost it ~10 % through a worse instruction schedule.  Every role
+  // keeps its state inside its own branch so none of it is live in another.
+  __shared__ __attribute__((aligned(16))) int sRedo[NWP];   // read as one int4
+  static_assert(NWP == 4, "sRedo is read as one int4");
+  auto redo_needed = [&](int bad) {
+    if (wv < NWP && (threadIdx.x & 63) == 0) sRedo[wv] = bad;
+    lds_barrier();
+    const int4 r4 = *(const int4*)sRedo;
+    return __builtin_amdgcn_readfirstlane(r4.x | r4.y | r4.z | r4.w) != 0;
+  };
+  // restart state shared by all roles before pass 2 (content-aware: the
+  // carried mean of the window before the call)
+  auto reset_for_pass2 = [&]() {
+    if constexpr (CONTENT) {
+      if (tid < TV) sMean[tid] = p.m_carry ? p.m_carry[(size_t)(b * H + h) * DV + tid] : 0.f;
+    }
+    lds_barrier();
+  };
   if (wv < NWP) {
+    auto prep_role = [&](auto robust_tag) -> int {
+      constexpr bool ROBUST = decltype(robust_tag)::value;
+      int any_bad = 0;
     // ================================================================ prep
     // Raw loads run two chunks ahead (issued two steps before their use, which
     // covers the memory latency under load), in three register sets with the
@@ -566,18 +595,18 @@ __global__ __launch_bounds__((NWP + NWS + TV / 16) * 64) void gdr_fwd_pipe_kerne
       Raw<TPS, C::VLD> R0, R1;
       load_raw<DK, TV, DECAY>(R0, rs, 0, pp, seg, ptid);
       for (; it + 1 < nchunks; it += 2) {
-        prep_chunk<DK, TV, DECAY, true>(sh, R0, R1, rs, (it + 1) * L, it, vstep(it), Tn, pw, l, pl,
-                                        seg, pp, ptid);
+        prep_chunk<DK, TV, DECAY, true, ROBUST>(sh, R0, R1, rs, (it + 1) * L, it, vstep(it), Tn, pw, l, pl,
+                                        seg, pp, ptid, any_bad);
         lds_barrier();
         idle_after(it);
-        prep_chunk<DK, TV, DECAY, true>(sh, R1, R0, rs, min((it + 2) * L, clast), it + 1,
-                                        vstep(it + 1), Tn, pw, l, pl, seg, pp, ptid);
+        prep_chunk<DK, TV, DECAY, true, ROBUST>(sh, R1, R0, rs, min((it + 2) * L, clast), it + 1,
+                                        vstep(it + 1), Tn, pw, l, pl, seg, pp, ptid, any_bad);
         lds_barrier();
         idle_after(it + 1);
       }
       if (it < nchunks) {   // odd chunk count: the last chunk is in R0
-        prep_chunk<DK, TV, DECAY, false>(sh, R0, R1, rs, 0, it, vstep(it), Tn, pw, l, pl, seg, pp,
-                                         ptid);
+        prep_chunk<DK, TV, DECAY, false, ROBUST>(sh, R0, R1, rs, 0, it, vstep(it), Tn, pw, l, pl, seg, pp,
+                                         ptid, any_bad);
         lds_barrier();
         ++it;
       }
@@ -586,36 +615,44 @@ __global__ __launch_bounds__((NWP + NWS + TV / 16) * 64) void gdr_fwd_pipe_kerne
     load_raw<DK, TV, DECAY>(R0, rs, 0, pp, seg, ptid);
     load_raw<DK, TV, DECAY>(R1, rs, min(L, clast), pp, seg, ptid);
     for (; it + 2 < nchunks; it += 3) {
-      prep_chunk<DK, TV, DECAY, true>(sh, R0, R2, rs, (it + 2) * L, it, vstep(it), Tn, pw, l, pl,
-                                      seg, pp, ptid);
+      prep_chunk<DK, TV, DECAY, true, ROBUST>(sh, R0, R2, rs, (it + 2) * L, it, vstep(it), Tn, pw, l, pl,
+                                      seg, pp, ptid, any_bad);
       lds_barrier();
       idle_after(it);
-      prep_chunk<DK, TV, DECAY, true>(sh, R1, R0, rs, min((it + 3) * L, clast), it + 1,
-                                      vstep(it + 1), Tn, pw, l, pl, seg, pp, ptid);
+      prep_chunk<DK, TV, DECAY, true, ROBUST>(sh, R1, R0, rs, min((it + 3) * L, clast), it + 1,
+                                      vstep(it + 1), Tn, pw, l, pl, seg, pp, ptid, any_bad);
       lds_barrier();
       idle_after(it + 1);
-      prep_chunk<DK, TV, DECAY, true>(sh, R2, R1, rs, min((it + 4) * L, clast), it + 2,
-                                      vstep(it + 2), Tn, pw, l, pl, seg, pp, ptid);
+      prep_chunk<DK, TV, DECAY, true, ROBUST>(sh, R2, R1, rs, min((it + 4) * L, clast), it + 2,
+                                      vstep(it + 2), Tn, pw, l, pl, seg, pp, ptid, any_bad);
       lds_barrier();
       idle_after(it + 2);
     }
     // one or two chunks left: they are in R0 and R1
     if (it < nchunks) {
-      prep_chunk<DK, TV, DECAY, false>(sh, R0, R2, rs, 0, it, vstep(it), Tn, pw, l, pl, seg, pp,
-                                       ptid);
+      prep_chunk<DK, TV, DECAY, false, ROBUST>(sh, R0, R2, rs, 0, it, vstep(it), Tn, pw, l, pl, seg, pp,
+                                       ptid, any_bad);
       lds_barrier();
       idle_after(it);
       ++it;
     }
     if (it < nchunks) {
-      prep_chunk<DK, TV, DECAY, false>(sh, R1, R2, rs, 0, it, vstep(it), Tn, pw, l, pl, seg, pp,
-                                       ptid);
+      prep_chunk<DK, TV, DECAY, false, ROBUST>(sh, R1, R2, rs, 0, it, vstep(it), Tn, pw, l, pl, seg, pp,
+                                       ptid, any_bad);
       lds_barrier();
       ++it;
     }
     }
     for (int st = vstep(nchunks - 1) + 1; st < nsteps; ++st) lds_barrier();
+      return any_bad;
+    };
+    if (redo_needed(prep_role(std::false_type{}))) {
+      reset_for_pass2();
+      prep_role(std::true_type{});
+    }
   } else if (wv < NWP + NWS) {
+    auto solve_role = [&](auto robust_tag) {
+      constexpr bool ROBUST = decltype(robust_tag)::value;
     // ================================================================ solve
     const int sw = wv - NWP;
     // the last solve wave also stages beta and beta*w (content-aware: the
@@ -670,11 +707,11 @@ __global__ __launch_bounds__((NWP + NWS + TV / 16) * 64) void gdr_fwd_pipe_kerne
             sBc[vj % 3][1][l] = bt * A.bw[l];
           }
         }
-        if (slot_out_of_range(A)) {
-          // some channel leaves the split form's range: the consumer runs this
-          // chunk token by token from its raw inputs
-          stage_raw<DK, TV, DECAY>(sh.a[vj % 3], rss, j * L, sw * 64 + l);
-        } else if (sw < 2) {
+        // some channel leaves the split form's range: the consumer runs this
+        // chunk token by token from raw inputs staged below (the flag is read
+        // now and used after the Gram and inverse work, which then is unused)
+        const int4 rflag = ROBUST ? *(const int4*)A.flag : int4{0, 0, 0, 0};
+        if (sw < 2) {
           // diagonal block bb: N and N^T as accumulator tiles, then
           // T_bb = (I + N)^{-1} = (I - N)(I + N^2)(I + N^4)(I + N^8).
           // mul(Q, Y) = C(Q^T Y): a tile feeds the left operand as its transpose.
@@ -743,14 +780,27 @@ __global__ __launch_bounds__((NWP + NWS + TV / 16) * 64) void gdr_fwd_pipe_kerne
             }
           }
         }
+        if (ROBUST && __builtin_amdgcn_readfirstlane(rflag.x | rflag.y | rflag.z | rflag.w) != 0) {
+          // the other solve waves may still be reading K+ / Q+ of this slot for
+          // their Gram tiles; those results are discarded for this chunk
+          stage_raw<DK, TV, DECAY>(sh.a[vj % 3], rss, j * L, sw * 64 + l);
+        }
       }
       lds_barrier();
     }
+    };
+    solve_role(std::false_type{});
+    if (redo_needed(0)) {
+      reset_for_pass2();
+      solve_role(std::true_type{});
+    }
   } else {
+    f32x4 Sacc[NCT];
+    auto consumer_role = [&](auto robust_tag) {
+      constexpr bool ROBUST = decltype(robust_tag)::value;
     // ============================================================ consumer
     const int cw = wv - NWP - NWS;              // value block of 16 channels
     if constexpr (CONTENT) __builtin_amdgcn_s_setprio(2);
-    f32x4 Sacc[NCT];
     const size_t srow = ((size_t)(b * H + h) * DV + v0 + 16 * cw + n) * DK;
     if (p.S0) {
 #pragma unroll
@@ -771,132 +821,166 @@ __global__ __launch_bounds__((NWP + NWS + TV / 16) * 64) void gdr_fwd_pipe_kerne
     const int so = H * DV * 2;                     // bytes per token row
     const int olane = n * so + 8 * g;              // token n, value channels 4g..4g+3
     float colsum[4] = {0.f, 0.f, 0.f, 0.f};   // content-aware: window sums of 4 channels
-    for (int it = 0; it < nsteps; ++it) {
-      const int vi = it - 2;
-      const int i = CONTENT ? (vi >= 0 ? block_at(vi) : -1) : vi;
-      if (CONTENT ? (i >= 0 && i < nchunks) : (i >= 0)) {
-        const SlotA<DK, TV>& A = sh.a[vi % 3];
-        const SlotS& S = sh.s[vi & 1];
-        const int c0 = i * L;
-        if (slot_out_of_range(A)) {
-          // token path (gdr_token.h): raw transition, keys and queries staged by
-          // the solve; o_t[n] is stored as one bf16 by the lanes with g == 0
-          const char* raw = (const char*)A.Kp;
-          const float* bt = CONTENT ? sBc[vi % 3][0] : A.beta;
-          const float* bwp = CONTENT ? sBc[vi % 3][1] : A.bw;
-          float fsum = 0.f;
-          token_steps<DK, DECAY, bf>(
-              Sacc, (const float*)raw, (const bf*)(raw + L * DK * 4),
-              (const bf*)(raw + L * DK * 6), DK, A.V + 16 * cw + n, RSV, bt, bwp,
-              min(L, Tn - c0), [&](int t, float ov) {
-                if (g == 0) {
-                  const bf ob = (bf)ov;
-                  __builtin_amdgcn_raw_buffer_store_b16(*(const unsigned short*)&ob, ro, 2 * n,
-                                                        (c0 + t) * so, 0);
+    int token_next = 0;   // range flag of the slot consumed at the next step
+    // One consumer step; TOKEN selects the token path (gdr_token.h) for a chunk
+    // whose decay leaves the split form's range.  The matrix-core steps run in
+    // an inner loop of their own that exits before such a chunk, so the rare
+    // path adds no branch to that loop's body.
+    auto step = [&](int it, auto token_tag) {
+      constexpr bool TOKEN = decltype(token_tag)::value;
+        const int vi = it - 2;
+        const int i = CONTENT ? (vi >= 0 ? block_at(vi) : -1) : vi;
+        if (CONTENT ? (i >= 0 && i < nchunks) : (i >= 0)) {
+          const SlotA<DK, TV>& A = sh.a[vi % 3];
+          const SlotS& S = sh.s[vi & 1];
+          const int c0 = i * L;
+          if constexpr (TOKEN) {
+              // token path (gdr_token.h): raw transition, keys and queries staged by
+              // the solve; o_t[n] is stored as one bf16 by the lanes with g == 0
+              const char* raw = (const char*)A.Kp;
+              const float* bt = CONTENT ? sBc[vi % 3][0] : A.beta;
+              const float* bwp = CONTENT ? sBc[vi % 3][1] : A.bw;
+              float fsum = 0.f;
+              token_steps<DK, DECAY, bf>(
+                  Sacc, (const float*)raw, (const bf*)(raw + L * DK * 4),
+                  (const bf*)(raw + L * DK * 6), DK, A.V + 16 * cw + n, RSV, bt, bwp,
+                  min(L, Tn - c0), [&](int t, float ov) {
+                    if (g == 0) {
+                      const bf ob = (bf)ov;
+                      __builtin_amdgcn_raw_buffer_store_b16(*(const unsigned short*)&ob, ro, 2 * n,
+                                                            (c0 + t) * so, 0);
+                    }
+                    fsum += ov;
+                  });
+              if constexpr (CONTENT) {
+                // window sums: value channel 4g + jj is kept by a lane of group g
+    #pragma unroll
+                for (int jj = 0; jj < 4; ++jj) {
+                  const float x = __shfl(fsum, 4 * g + jj);
+                  colsum[jj] += n == 0 ? x : 0.f;
                 }
-                fsum += ov;
-              });
+              }
+          } else {
+          // R = diag(bw) V - diag(beta) K+ S^T;  Qs^T = (Q+ S^T)^T, kept transposed
+          // (lane holds one token and four value channels) for 8-byte o stores
+          frag Sf[NKC];
+  #pragma unroll
+          for (int kk = 0; kk < NKC; ++kk) Sf[kk] = O::from_acc(Sacc[2 * kk], Sacc[2 * kk + 1]);
+          f32x4 Rt[2], Qs[2];
+  #pragma unroll
+          for (int t = 0; t < 2; ++t) {
+            f32x4 P = {0.f, 0.f, 0.f, 0.f}, Q = {0.f, 0.f, 0.f, 0.f};
+  #pragma unroll
+            for (int kk = 0; kk < NKC; ++kk) {
+              O::mma(P, load_kq<DK, TV>(A.Kp, 16 * t, kk), Sf[kk]);
+              O::mma(Q, Sf[kk], load_kq<DK, TV>(A.Qp, 16 * t, kk));
+            }
+            const f32x4 bw4 = *(const f32x4*)((CONTENT ? sBc[vi % 3][1] : A.bw) + 16 * t + 4 * g);
+            const f32x4 bt4 = *(const f32x4*)((CONTENT ? sBc[vi % 3][0] : A.beta) + 16 * t + 4 * g);
+  #pragma unroll
+            for (int jj = 0; jj < 4; ++jj) {
+              const int r = 16 * t + 4 * g + jj;
+              Rt[t][jj] = bw4[jj] * (float)A.V[r * RSV + 16 * cw + n] - bt4[jj] * P[jj];
+            }
+            Qs[t] = Q;
+          }
+          // Dl by blocks, O = Qs + M Dl
+          f32x4 D0 = {0.f, 0.f, 0.f, 0.f}, D1 = {0.f, 0.f, 0.f, 0.f};
+          O::mma(D0, load_cb_half<bf>(S.Td, RS16, 0, 0), O::from_acc_half(Rt[0]));
+          const frag d0 = O::from_acc_half(D0);
+          f32x4 Y = Rt[1];
+          {
+            const frag a10 = load_cb_half<bf>(S.A10, RS16, 0, 0);
+            O::mma(Y, DECAY != 0 ? a10 : O::neg(a10), d0);
+          }
+          O::mma(D1, load_cb_half<bf>(S.Td + 16 * RS16, RS16, 0, 0), O::from_acc_half(Y));
+          frag Df = d0;   // slots 0..3 from D0, 4..7 from D1
+  #pragma unroll
+          for (int jj = 0; jj < 4; ++jj) Df[4 + jj] = (bf)D1[jj];
+          // O^T = Qs^T + (M Dl)^T = Qs^T + Dl^T M^T
+          f32x4 O0 = Qs[0], O1 = Qs[1];
+          O::mma(O0, d0, load_cb_half<bf>(S.M, RSL, 0, 0));
+          O::mma(O1, Df, load_cb<bf>(S.M, RSL, 16, 0));
+          const bf16x4 ox0 = {(bf)O0[0], (bf)O0[1], (bf)O0[2], (bf)O0[3]};
+          const bf16x4 ox1 = {(bf)O1[0], (bf)O1[1], (bf)O1[2], (bf)O1[3]};
           if constexpr (CONTENT) {
-            // window sums: value channel 4g + jj is kept by a lane of group g
-#pragma unroll
-            for (int jj = 0; jj < 4; ++jj) {
-              const float x = __shfl(fsum, 4 * g + jj);
-              colsum[jj] += n == 0 ? x : 0.f;
+            // window sums of the fp32 outputs (tokens past T contribute zero);
+            // at a window's last block its per-channel mean goes to LDS, to be
+            // read by the solve of the next window's first block
+  #pragma unroll
+            for (int jj = 0; jj < 4; ++jj) colsum[jj] += O0[jj] + O1[jj];
+          }
+          // S <- S Gamma_L + Dl^T K- = (S + Dl^T Kh) Gamma_L, since K- = Kh Gamma_L
+          // column-wise (per channel, or per rotation pair)
+  #pragma unroll
+          for (int ct = 0; ct < NCT; ++ct) {
+            O::mma(Sacc[ct], load_cb<bf>(A.KhT, RSL, 16 * ct, 0), Df);
+            const f32x4 z4 = *(const f32x4*)(A.GL + 8 * ct + 2 * g);   // channels 16ct+4g..+3
+  #pragma unroll
+            for (int jj = 0; jj < 4; jj += 2) {
+              const f32x2 z = {z4[jj], z4[jj + 1]};
+              const float x0 = Sacc[ct][jj], x1 = Sacc[ct][jj + 1];
+              if constexpr (DECAY == 0) {
+                Sacc[ct][jj] = x0 * z.x;
+                Sacc[ct][jj + 1] = x1 * z.y;
+              } else {
+                Sacc[ct][jj] = z.x * x0 + z.y * x1;
+                Sacc[ct][jj + 1] = -z.y * x0 + z.x * x1;
+              }
             }
           }
-        } else {
-        // R = diag(bw) V - diag(beta) K+ S^T;  Qs^T = (Q+ S^T)^T, kept transposed
-        // (lane holds one token and four value channels) for 8-byte o stores
-        frag Sf[NKC];
-#pragma unroll
-        for (int kk = 0; kk < NKC; ++kk) Sf[kk] = O::from_acc(Sacc[2 * kk], Sacc[2 * kk + 1]);
-        f32x4 Rt[2], Qs[2];
-#pragma unroll
-        for (int t = 0; t < 2; ++t) {
-          f32x4 P = {0.f, 0.f, 0.f, 0.f}, Q = {0.f, 0.f, 0.f, 0.f};
-#pragma unroll
-          for (int kk = 0; kk < NKC; ++kk) {
-            O::mma(P, load_kq<DK, TV>(A.Kp, 16 * t, kk), Sf[kk]);
-            O::mma(Q, Sf[kk], load_kq<DK, TV>(A.Qp, 16 * t, kk));
+          {   // o stores last, off the chain from the barrier to the state update
+            typedef __attribute__((ext_vector_type(2))) unsigned u32x2;
+            __builtin_amdgcn_raw_buffer_store_b64(*(const u32x2*)&ox0, ro, olane, c0 * so, 0);
+            __builtin_amdgcn_raw_buffer_store_b64(*(const u32x2*)&ox1, ro, olane, (c0 + 16) * so, 0);
           }
-          const f32x4 bw4 = *(const f32x4*)((CONTENT ? sBc[vi % 3][1] : A.bw) + 16 * t + 4 * g);
-          const f32x4 bt4 = *(const f32x4*)((CONTENT ? sBc[vi % 3][0] : A.beta) + 16 * t + 4 * g);
-#pragma unroll
-          for (int jj = 0; jj < 4; ++jj) {
-            const int r = 16 * t + 4 * g + jj;
-            Rt[t][jj] = bw4[jj] * (float)A.V[r * RSV + 16 * cw + n] - bt4[jj] * P[jj];
           }
-          Qs[t] = Q;
-        }
-        // Dl by blocks, O = Qs + M Dl
-        f32x4 D0 = {0.f, 0.f, 0.f, 0.f}, D1 = {0.f, 0.f, 0.f, 0.f};
-        O::mma(D0, load_cb_half<bf>(S.Td, RS16, 0, 0), O::from_acc_half(Rt[0]));
-        const frag d0 = O::from_acc_half(D0);
-        f32x4 Y = Rt[1];
-        {
-          const frag a10 = load_cb_half<bf>(S.A10, RS16, 0, 0);
-          O::mma(Y, DECAY != 0 ? a10 : O::neg(a10), d0);
-        }
-        O::mma(D1, load_cb_half<bf>(S.Td + 16 * RS16, RS16, 0, 0), O::from_acc_half(Y));
-        frag Df = d0;   // slots 0..3 from D0, 4..7 from D1
-#pragma unroll
-        for (int jj = 0; jj < 4; ++jj) Df[4 + jj] = (bf)D1[jj];
-        // O^T = Qs^T + (M Dl)^T = Qs^T + Dl^T M^T
-        f32x4 O0 = Qs[0], O1 = Qs[1];
-        O::mma(O0, d0, load_cb_half<bf>(S.M, RSL, 0, 0));
-        O::mma(O1, Df, load_cb<bf>(S.M, RSL, 16, 0));
-        const bf16x4 ox0 = {(bf)O0[0], (bf)O0[1], (bf)O0[2], (bf)O0[3]};
-        const bf16x4 ox1 = {(bf)O1[0], (bf)O1[1], (bf)O1[2], (bf)O1[3]};
-        if constexpr (CONTENT) {
-          // window sums of the fp32 outputs (tokens past T contribute zero);
-          // at a window's last block its per-channel mean goes to LDS, to be
-          // read by the solve of the next window's first block
-#pragma unroll
-          for (int jj = 0; jj < 4; ++jj) colsum[jj] += O0[jj] + O1[jj];
-        }
-        // S <- S Gamma_L + Dl^T K- = (S + Dl^T Kh) Gamma_L, since K- = Kh Gamma_L
-        // column-wise (per channel, or per rotation pair)
-#pragma unroll
-        for (int ct = 0; ct < NCT; ++ct) {
-          O::mma(Sacc[ct], load_cb<bf>(A.KhT, RSL, 16 * ct, 0), Df);
-          const f32x4 z4 = *(const f32x4*)(A.GL + 8 * ct + 2 * g);   // channels 16ct+4g..+3
-#pragma unroll
-          for (int jj = 0; jj < 4; jj += 2) {
-            const f32x2 z = {z4[jj], z4[jj + 1]};
-            const float x0 = Sacc[ct][jj], x1 = Sacc[ct][jj + 1];
-            if constexpr (DECAY == 0) {
-              Sacc[ct][jj] = x0 * z.x;
-              Sacc[ct][jj + 1] = x1 * z.y;
-            } else {
-              Sacc[ct][jj] = z.x * x0 + z.y * x1;
-              Sacc[ct][jj + 1] = -z.y * x0 + z.x * x1;
+          if constexpr (CONTENT) {
+            // at a window's last block its per-channel mean goes to LDS, to be
+            // read by the solve of the next window's first block
+            if (i % SPC == SPC - 1) {
+  #pragma unroll
+              for (int jj = 0; jj < 4; ++jj) {
+                float sum = colsum[jj];
+  #pragma unroll
+                for (int off = 1; off < 16; off <<= 1) sum += __shfl_xor(sum, off);
+                if (n == 0) sMean[16 * cw + 4 * g + jj] = sum * (1.f / (float)(SPC * L));
+                colsum[jj] = 0.f;
+              }
             }
           }
         }
-        {   // o stores last, off the chain from the barrier to the state update
-          typedef __attribute__((ext_vector_type(2))) unsigned u32x2;
-          __builtin_amdgcn_raw_buffer_store_b64(*(const u32x2*)&ox0, ro, olane, c0 * so, 0);
-          __builtin_amdgcn_raw_buffer_store_b64(*(const u32x2*)&ox1, ro, olane, (c0 + 16) * so, 0);
+        // the slot of virtual step it - 1 (consumed next step) was completed by
+        // the prep before the last barrier; reading its flag now keeps the LDS
+        // latency off the start of the next step's chain
+        if (ROBUST && it >= 1) {
+          const int4 f = *(const int4*)sh.a[(it - 1) % 3].flag;
+          token_next = __builtin_amdgcn_readfirstlane(f.x | f.y | f.z | f.w);
         }
-        }   // split form
-        if constexpr (CONTENT) {
-          // at a window's last block its per-channel mean goes to LDS, to be
-          // read by the solve of the next window's first block
-          if (i % SPC == SPC - 1) {
-#pragma unroll
-            for (int jj = 0; jj < 4; ++jj) {
-              float sum = colsum[jj];
-#pragma unroll
-              for (int off = 1; off < 16; off <<= 1) sum += __shfl_xor(sum, off);
-              if (n == 0) sMean[16 * cw + 4 * g + jj] = sum * (1.f / (float)(SPC * L));
-              colsum[jj] = 0.f;
-            }
-          }
+        lds_barrier();
+    };
+    if constexpr (!ROBUST) {
+      for (int it = 0; it < nsteps; ++it) step(it, std::false_type{});
+    } else {
+      // the flag read in step it is that of the chunk consumed in step it + 1
+      int it = 0;
+      while (it < nsteps) {
+        for (; it < nsteps && token_next == 0; ++it) step(it, std::false_type{});
+        if (it < nsteps) {
+          step(it, std::true_type{});
+          ++it;
         }
       }
-      lds_barrier();
     }
+      };
+    consumer_role(std::false_type{});
+    if (redo_needed(0)) {
+      reset_for_pass2();
+      consumer_role(std::true_type{});
+    }
+    const int cw = wv - NWP - NWS;
     if (p.S_out) {
+      const size_t srow = ((size_t)(b * H + h) * DV + v0 + 16 * cw + n) * DK;
 #pragma unroll
       for (int ct = 0; ct < NCT; ++ct) *(f32x4*)(p.S_out + srow + 16 * ct + 4 * g) = Sacc[ct];
     }
