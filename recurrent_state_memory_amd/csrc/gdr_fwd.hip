@@ -434,7 +434,8 @@ __global__ __launch_bounds__(TV / 16 * 64) void gdr_fwd_kernel(FwdParams p) {
     if (token_path) {
       // ---------------------------------------------------------- token path
       token_steps<DK, DECAY, T>(
-          Sacc, (const float*)sKhKm, sKp, sQp, RSK, sV + 16 * wv + n, RSV, sBeta, sBW,
+          Sacc, (const float*)sKhKm, sKp, sQp, RSK,
+          [&](int t) { return (float)sV[t * RSV + 16 * wv + n]; }, sBeta, sBW,
           min(L, Tn - c0), [&](int t, float ov) {
             if (g == 0) {
               go[((size_t)(b * Tn + c0 + t) * H + h) * DV + v0 + 16 * wv + n] = (T)ov;

@@ -92,8 +92,13 @@ struct Cfg {
   static constexpr int NKC = DK / 32;
   static constexpr int VPR = TV / 8;             // 16-byte pieces per value row
   static constexpr int VLD = (L * VPR + NWP * 64 - 1) / (NWP * 64);   // per prep thread
+  // content-aware erase: the prep loads whole value rows (DK == DV pieces of
+  // 8), stores this workgroup's tile and reduces u_h . v_t over the row
+  static constexpr int VPRF = DK / 8;
+  static constexpr int VLDF = L * VPRF / (NWP * 64);
   static_assert(TPS % 4 == 0 && TPS >= 4, "prep split");
   static_assert(L * VPR % (NWP * 64) == 0 || L * VPR < NWP * 64, "value tile load split");
+  static_assert(L * VPRF % (NWP * 64) == 0 && (NWP * 64) % VPRF == 0, "value row load split");
 };
 
 // Bytes of one chunk in raw form for the token path (gdr_token.h): the
@@ -123,6 +128,7 @@ struct SlotA {
   float bw[L];     // beta * w (content-aware: w)
   f32x2 GL[C::NP];
   int flag[NWP];   // per prep wave: some channel's Gamma_L is out of range
+  float uv[L];     // content-aware: u_h . v_t, the projected row's value
 };
 
 
@@ -131,11 +137,12 @@ template <int DK, int TV>
 constexpr bool slot_aligned() {
   using S = SlotA<DK, TV>;
   return offsetof(S, beta) % 16 == 0 && offsetof(S, bw) % 16 == 0 && offsetof(S, GL) % 16 == 0 &&
-         offsetof(S, flag) % 16 == 0 && offsetof(S, V) % 16 == 0 && sizeof(S) % 16 == 0 &&
+         offsetof(S, flag) % 16 == 0 && offsetof(S, uv) % 16 == 0 && offsetof(S, V) % 16 == 0 &&
+         sizeof(S) % 16 == 0 &&
          offsetof(S, V) - offsetof(S, Kp) >= (size_t)raw_bytes<DK>();
 }
 static_assert(slot_aligned<128, 64>() && slot_aligned<128, 32>() && slot_aligned<64, 32>() &&
-                  slot_aligned<128, 128>() && slot_aligned<64, 64>(),
+                  slot_aligned<128, 16>() && slot_aligned<64, 16>(),
               "SlotA alignment");
 
 // Solve outputs of one chunk (2 slots).
@@ -159,6 +166,10 @@ struct Raw {
   f32x2 a[TPS];
   uint4 v[VLD];
 };
+
+// raw loads of one prep lane for one chunk
+template <int DK, int TV, bool CONTENT>
+using RawT = Raw<Cfg<DK, TV>::TPS, CONTENT ? Cfg<DK, TV>::VLDF : Cfg<DK, TV>::VLD>;
 
 // Buffer resources over one (b, h): element (t, c) of a [B,T,H,X] tensor sits at
 // byte (t * H * X + c) * size from the resource base, and the resource ends
@@ -214,11 +225,19 @@ __device__ inline bf16x8 load_kq(const bf* base, int row0, int kk) {
 // in soffset.  Both count in the range check of a raw buffer (no stride), so
 // tokens at or past T still read as zero.
 // PART 0: value tile; 1: key-axis transitions; 2: keys; 3: queries.
-template <int DK, int TV, int DECAY, int PART>
-__device__ inline void load_part(Raw<Cfg<DK, TV>::TPS, Cfg<DK, TV>::VLD>& R, const Rsrc& rs, int c0, int pp, int seg,
+template <int DK, int TV, int DECAY, bool CONTENT, int PART>
+__device__ inline void load_part(RawT<DK, TV, CONTENT>& R, const Rsrc& rs, int c0, int pp, int seg,
                                  int ptid) {
   using C = Cfg<DK, TV>;
-  if constexpr (PART == 0) {
+  if constexpr (PART == 0 && CONTENT) {   // whole value rows (the resource starts at column 0)
+#pragma unroll
+    for (int u = 0; u < C::VLDF; ++u) {
+      const int idx = ptid + u * NWP * 64;
+      const int r = idx / C::VPRF, cc = idx % C::VPRF;
+      const auto x = __builtin_amdgcn_raw_buffer_load_b128(rs.v, r * rs.sv + cc * 16, c0 * rs.sv, 0);
+      R.v[u] = uint4{x[0], x[1], x[2], x[3]};
+    }
+  } else if constexpr (PART == 0) {
 #pragma unroll
     for (int u = 0; u < C::VLD; ++u) {
       const int idx0 = ptid + u * NWP * 64;
@@ -251,13 +270,13 @@ __device__ inline void load_part(Raw<Cfg<DK, TV>::TPS, Cfg<DK, TV>::VLD>& R, con
   }
 }
 
-template <int DK, int TV, int DECAY>
-__device__ inline void load_raw(Raw<Cfg<DK, TV>::TPS, Cfg<DK, TV>::VLD>& R, const Rsrc& rs, int c0, int pp, int seg,
+template <int DK, int TV, int DECAY, bool CONTENT>
+__device__ inline void load_raw(RawT<DK, TV, CONTENT>& R, const Rsrc& rs, int c0, int pp, int seg,
                                 int ptid) {
-  load_part<DK, TV, DECAY, 0>(R, rs, c0, pp, seg, ptid);
-  load_part<DK, TV, DECAY, 1>(R, rs, c0, pp, seg, ptid);
-  load_part<DK, TV, DECAY, 2>(R, rs, c0, pp, seg, ptid);
-  load_part<DK, TV, DECAY, 3>(R, rs, c0, pp, seg, ptid);
+  load_part<DK, TV, DECAY, CONTENT, 0>(R, rs, c0, pp, seg, ptid);
+  load_part<DK, TV, DECAY, CONTENT, 1>(R, rs, c0, pp, seg, ptid);
+  load_part<DK, TV, DECAY, CONTENT, 2>(R, rs, c0, pp, seg, ptid);
+  load_part<DK, TV, DECAY, CONTENT, 3>(R, rs, c0, pp, seg, ptid);
 }
 
 // Value held by lane l ^ (PPW * d) (d = 1, 2, 4; PPW * d in {8, 16, 32}):
@@ -280,18 +299,19 @@ __device__ inline float xor_lanes(float v, int d, int l) {
 // With NEXT, the raw loads of the chunk at token cn go into Rn, spread over the
 // step in four groups so that the prep waves do not all stall on a full
 // vector-memory queue at the start of every step.
-template <int DK, int TV, int DECAY, bool NEXT, bool ROBUST>
-__device__ __forceinline__ void prep_chunk(Shared<DK, TV>& sh, const Raw<Cfg<DK, TV>::TPS, Cfg<DK, TV>::VLD>& R,
-                                           Raw<Cfg<DK, TV>::TPS, Cfg<DK, TV>::VLD>& Rn, const Rsrc& rs, int cn,
+template <int DK, int TV, int DECAY, bool CONTENT, bool NEXT, bool ROBUST>
+__device__ __forceinline__ void prep_chunk(Shared<DK, TV>& sh, const RawT<DK, TV, CONTENT>& R,
+                                           RawT<DK, TV, CONTENT>& Rn, const Rsrc& rs, int cn,
                                            int it, int vs, int Tn, int pw, int l, int pl,
-                                           int seg, int pp, int ptid, int& any_out) {
+                                           int seg, int pp, int ptid, int& any_out,
+                                           const float (&uh)[8], int vc0) {
   using C = Cfg<DK, TV>;
   constexpr int PPW = C::PPW, NSEG = C::NSEG, TPS = C::TPS, RSK = C::RSK, RSV = C::RSV,
                 VPR = C::VPR;
   SlotA<DK, TV>& A = sh.a[vs % 3];
   bf* Kh = sh.Kh[vs & 1];
   const int c0 = it * L;
-  if constexpr (NEXT) load_part<DK, TV, DECAY, 0>(Rn, rs, cn, pp, seg, ptid);
+  if constexpr (NEXT) load_part<DK, TV, DECAY, CONTENT, 0>(Rn, rs, cn, pp, seg, ptid);
   // transitions of this lane's token segment (identity past the end)
   f32x2 d[TPS];
   if (c0 + L <= Tn) {
@@ -319,11 +339,32 @@ __device__ __forceinline__ void prep_chunk(Shared<DK, TV>& sh, const Raw<Cfg<DK,
   const f32x2 one = {1.f, DECAY == 0 ? 1.f : 0.f};
   if constexpr (NEXT) {
     __builtin_amdgcn_sched_barrier(0);
-    load_part<DK, TV, DECAY, 1>(Rn, rs, cn, pp, seg, ptid);
+    load_part<DK, TV, DECAY, CONTENT, 1>(Rn, rs, cn, pp, seg, ptid);
   }
   f32x2 run = d[0];
 #pragma unroll
   for (int r = 1; r < TPS; ++r) run = mulz(run, d[r]);
+  if constexpr (CONTENT) {
+    // whole rows: the tile (columns vc0 .. vc0 + TV - 1) goes to LDS, and
+    // u_h . v_t is reduced over the VPRF lanes that hold token t's row
+#pragma unroll
+    for (int u = 0; u < C::VLDF; ++u) {
+      const int idx = ptid + u * NWP * 64;
+      const int r = idx / C::VPRF, cc = idx % C::VPRF;
+      const int tc = cc * 8 - vc0;
+      if (tc >= 0 && tc < TV) *(uint4*)(A.V + r * RSV + tc) = R.v[u];
+      const uint32_t w4[4] = {R.v[u].x, R.v[u].y, R.v[u].z, R.v[u].w};
+      float dot = 0.f;
+#pragma unroll
+      for (int e = 0; e < 4; ++e) {
+        const f32x2 x = bf2_to_f2(w4[e]);
+        dot += uh[2 * e] * x.x + uh[2 * e + 1] * x.y;
+      }
+#pragma unroll
+      for (int off = 1; off < C::VPRF; off <<= 1) dot += __shfl_xor(dot, off);
+      if (cc == 0) A.uv[r] = dot;
+    }
+  } else {
 #pragma unroll
   for (int u = 0; u < C::VLD; ++u) {
     const int idx = ptid + u * NWP * 64;
@@ -331,6 +372,7 @@ __device__ __forceinline__ void prep_chunk(Shared<DK, TV>& sh, const Raw<Cfg<DK,
       const int r = idx / VPR, cc = idx % VPR;
       *(uint4*)(A.V + r * RSV + cc * 8) = R.v[u];
     }
+  }
   }
   // products over the earlier (pre) and later (post) segments of this lane's
   // channel pair, and over the whole chunk (tot): a butterfly over the NSEG
@@ -356,7 +398,7 @@ __device__ __forceinline__ void prep_chunk(Shared<DK, TV>& sh, const Raw<Cfg<DK,
   }
   if constexpr (NEXT) {
     __builtin_amdgcn_sched_barrier(0);
-    load_part<DK, TV, DECAY, 2>(Rn, rs, cn, pp, seg, ptid);
+    load_part<DK, TV, DECAY, CONTENT, 2>(Rn, rs, cn, pp, seg, ptid);
   }
   f32x2 ig;   // Gamma_L^{-T} per channel (pair)
   if constexpr (DECAY == 0) {
@@ -392,7 +434,7 @@ __device__ __forceinline__ void prep_chunk(Shared<DK, TV>& sh, const Raw<Cfg<DK,
   for (int r4 = 0; r4 < TPS; r4 += 4) {
     if (NEXT && r4 == (TPS > 4 ? 4 : 0)) {
       __builtin_amdgcn_sched_barrier(0);
-      load_part<DK, TV, DECAY, 3>(Rn, rs, cn, pp, seg, ptid);
+      load_part<DK, TV, DECAY, CONTENT, 3>(Rn, rs, cn, pp, seg, ptid);
     }
 #pragma unroll
     for (int u = 0; u < 4; ++u) {
@@ -491,7 +533,8 @@ __device__ inline void stage_raw(SlotA<DK, TV>& A, const Rsrc& rs, int c0, int i
 }
 
 template <int DK, int TV, int DECAY, bool CONTENT>
-__global__ __launch_bounds__((NWP + NWS + TV / 16) * 64) void gdr_fwd_pipe_kernel(FwdParams p) {
+__global__ __launch_bounds__((NWP + NWS + TV / 16 + (CONTENT ? 1 : 0)) * 64) void gdr_fwd_pipe_kernel(
+    FwdParams p) {
   using C = Cfg<DK, TV>;
   using O = Op<bf>;
   using frag = O::frag;
@@ -524,14 +567,24 @@ __global__ __launch_bounds__((NWP + NWS + TV / 16) * 64) void gdr_fwd_pipe_kerne
     return CONTENT ? ((v % (SPC + 1) == SPC) ? -1 : v - v / (SPC + 1)) : v;
   };
   const int nsteps = vstep(nchunks - 1) + 3;
-  // u_h = B_h^T a_h and the mean output of the previous window (the carried
-  // mean, or zero, before the first window)
-  __shared__ float sU[CONTENT ? TV : 1], sMean[CONTENT ? TV : 1];
+  // Content-aware erase.  Every gate acts on the key axis, so the value rows of
+  // S evolve independently and any fixed combination of them does too (CARVE
+  // technical summary, section 2.3 and section 3 item 1): the projected row
+  // r = u_h^T S follows the same recurrence with value u_h . v_t, and
+  // r_t . q_t = u_h . o_t.  So every value-tile workgroup carries r in one extra
+  // consumer wave (the projection wave) and forms the window signal
+  // s_c = u_h . m_c = (1/window) sum_t r_t . q_t itself, with no exchange
+  // between workgroups.  u_h = B_h^T a_h; sMean holds the carried mean of the
+  // window before the call (or zero), which gives the first window's signal;
+  // sS holds the signal of the window after the last finished one.
+  constexpr int NWC = C::NWC;
+  __shared__ __attribute__((aligned(16))) float sU[CONTENT ? DK : 1], sMean[CONTENT ? DK : 1];
+  __shared__ float sS[1];
   // content-aware: beta and beta*w of a block, computed by the solve for the
   // consumer (one per prep slot)
   __shared__ __attribute__((aligned(16))) float sBc[CONTENT ? 3 : 1][CONTENT ? 2 : 1][L];
   if constexpr (CONTENT) {
-    if (tid < TV) {
+    if (tid < DV) {
       float acc = 0.f;
       for (int r = 0; r < p.ub_rank; ++r)
         acc += p.ub_up[h * p.ub_rank + r] * p.ub_down[((size_t)h * p.ub_rank + r) * DV + tid];
@@ -584,61 +637,68 @@ __global__ __launch_bounds__((NWP + NWS + TV / 16) * 64) void gdr_fwd_pipe_kerne
     if constexpr (CONTENT) __builtin_amdgcn_s_setprio(1);
     const int pl = l % PPW, seg = l / PPW, pp = pw * PPW + pl;
     const int ptid = tid;                       // 0 .. NWP*64-1
-    const Rsrc rs = make_rsrcs<DK, TV, DECAY>(p, b, h, v0);
+    const Rsrc rs = make_rsrcs<DK, TV, DECAY>(p, b, h, CONTENT ? 0 : v0);
     const int clast = (nchunks - 1) * L;
+    // content-aware: u_h over the 8 value channels of this lane's row piece
+    float uh[8] = {0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f};
+    if constexpr (CONTENT) {
+      const int cc = ptid % C::VPRF;
+#pragma unroll
+      for (int e = 0; e < 8; ++e) uh[e] = sU[cc * 8 + e];
+    }
     auto idle_after = [&](int j) {   // the idle step after a window's last block
       if (CONTENT && j % SPC == SPC - 1 && j + 1 < nchunks) lds_barrier();
     };
     int it = 0;
     if constexpr (C::NT > 12 * 64) {
       // 16 waves leave 128 VGPRs per wave: one chunk ahead, two register sets
-      Raw<TPS, C::VLD> R0, R1;
-      load_raw<DK, TV, DECAY>(R0, rs, 0, pp, seg, ptid);
+      RawT<DK, TV, CONTENT> R0, R1;
+      load_raw<DK, TV, DECAY, CONTENT>(R0, rs, 0, pp, seg, ptid);
       for (; it + 1 < nchunks; it += 2) {
-        prep_chunk<DK, TV, DECAY, true, ROBUST>(sh, R0, R1, rs, (it + 1) * L, it, vstep(it), Tn, pw, l, pl,
-                                        seg, pp, ptid, any_bad);
+        prep_chunk<DK, TV, DECAY, CONTENT, true, ROBUST>(sh, R0, R1, rs, (it + 1) * L, it, vstep(it), Tn, pw, l, pl,
+                                        seg, pp, ptid, any_bad, uh, v0);
         lds_barrier();
         idle_after(it);
-        prep_chunk<DK, TV, DECAY, true, ROBUST>(sh, R1, R0, rs, min((it + 2) * L, clast), it + 1,
-                                        vstep(it + 1), Tn, pw, l, pl, seg, pp, ptid, any_bad);
+        prep_chunk<DK, TV, DECAY, CONTENT, true, ROBUST>(sh, R1, R0, rs, min((it + 2) * L, clast), it + 1,
+                                        vstep(it + 1), Tn, pw, l, pl, seg, pp, ptid, any_bad, uh, v0);
         lds_barrier();
         idle_after(it + 1);
       }
       if (it < nchunks) {   // odd chunk count: the last chunk is in R0
-        prep_chunk<DK, TV, DECAY, false, ROBUST>(sh, R0, R1, rs, 0, it, vstep(it), Tn, pw, l, pl, seg, pp,
-                                         ptid, any_bad);
+        prep_chunk<DK, TV, DECAY, CONTENT, false, ROBUST>(sh, R0, R1, rs, 0, it, vstep(it), Tn, pw, l, pl, seg, pp,
+                                         ptid, any_bad, uh, v0);
         lds_barrier();
         ++it;
       }
     } else {
-    Raw<TPS, C::VLD> R0, R1, R2;
-    load_raw<DK, TV, DECAY>(R0, rs, 0, pp, seg, ptid);
-    load_raw<DK, TV, DECAY>(R1, rs, min(L, clast), pp, seg, ptid);
+    RawT<DK, TV, CONTENT> R0, R1, R2;
+    load_raw<DK, TV, DECAY, CONTENT>(R0, rs, 0, pp, seg, ptid);
+    load_raw<DK, TV, DECAY, CONTENT>(R1, rs, min(L, clast), pp, seg, ptid);
     for (; it + 2 < nchunks; it += 3) {
-      prep_chunk<DK, TV, DECAY, true, ROBUST>(sh, R0, R2, rs, (it + 2) * L, it, vstep(it), Tn, pw, l, pl,
-                                      seg, pp, ptid, any_bad);
+      prep_chunk<DK, TV, DECAY, CONTENT, true, ROBUST>(sh, R0, R2, rs, (it + 2) * L, it, vstep(it), Tn, pw, l, pl,
+                                      seg, pp, ptid, any_bad, uh, v0);
       lds_barrier();
       idle_after(it);
-      prep_chunk<DK, TV, DECAY, true, ROBUST>(sh, R1, R0, rs, min((it + 3) * L, clast), it + 1,
-                                      vstep(it + 1), Tn, pw, l, pl, seg, pp, ptid, any_bad);
+      prep_chunk<DK, TV, DECAY, CONTENT, true, ROBUST>(sh, R1, R0, rs, min((it + 3) * L, clast), it + 1,
+                                      vstep(it + 1), Tn, pw, l, pl, seg, pp, ptid, any_bad, uh, v0);
       lds_barrier();
       idle_after(it + 1);
-      prep_chunk<DK, TV, DECAY, true, ROBUST>(sh, R2, R1, rs, min((it + 4) * L, clast), it + 2,
-                                      vstep(it + 2), Tn, pw, l, pl, seg, pp, ptid, any_bad);
+      prep_chunk<DK, TV, DECAY, CONTENT, true, ROBUST>(sh, R2, R1, rs, min((it + 4) * L, clast), it + 2,
+                                      vstep(it + 2), Tn, pw, l, pl, seg, pp, ptid, any_bad, uh, v0);
       lds_barrier();
       idle_after(it + 2);
     }
     // one or two chunks left: they are in R0 and R1
     if (it < nchunks) {
-      prep_chunk<DK, TV, DECAY, false, ROBUST>(sh, R0, R2, rs, 0, it, vstep(it), Tn, pw, l, pl, seg, pp,
-                                       ptid, any_bad);
+      prep_chunk<DK, TV, DECAY, CONTENT, false, ROBUST>(sh, R0, R2, rs, 0, it, vstep(it), Tn, pw, l, pl, seg, pp,
+                                       ptid, any_bad, uh, v0);
       lds_barrier();
       idle_after(it);
       ++it;
     }
     if (it < nchunks) {
-      prep_chunk<DK, TV, DECAY, false, ROBUST>(sh, R1, R2, rs, 0, it, vstep(it), Tn, pw, l, pl, seg, pp,
-                                       ptid, any_bad);
+      prep_chunk<DK, TV, DECAY, CONTENT, false, ROBUST>(sh, R1, R2, rs, 0, it, vstep(it), Tn, pw, l, pl, seg, pp,
+                                       ptid, any_bad, uh, v0);
       lds_barrier();
       ++it;
     }
@@ -688,12 +748,14 @@ __global__ __launch_bounds__((NWP + NWS + TV / 16) * 64) void gdr_fwd_pipe_kerne
         const bf* Kh = sh.Kh[vj & 1];
         SlotS& S = sh.s[vj & 1];
         if constexpr (CONTENT) {
-          if (j % SPC == 0) {   // new window: s_c from the previous window's mean (fixed order)
+          if (j == 0) {   // first window: u_h . (carried mean), fixed-order reduction
             float acc = 0.f;
-            for (int vv = l; vv < TV; vv += 64) acc += sU[vv] * sMean[vv];
+            for (int vv = l; vv < DV; vv += 64) acc += sU[vv] * sMean[vv];
 #pragma unroll
             for (int off = 32; off > 0; off >>= 1) acc += __shfl_xor(acc, off);
             s_win = acc;
+          } else if (j % SPC == 0) {   // later windows: formed by the projection wave
+            s_win = sS[0];
           }
         }
         auto beta_at = [&](int r) {
@@ -795,39 +857,73 @@ __global__ __launch_bounds__((NWP + NWS + TV / 16) * 64) void gdr_fwd_pipe_kerne
       solve_role(std::true_type{});
     }
   } else {
-    f32x4 Sacc[NCT];
-    auto consumer_role = [&](auto robust_tag) {
-      constexpr bool ROBUST = decltype(robust_tag)::value;
     // ============================================================ consumer
-    const int cw = wv - NWP - NWS;              // value block of 16 channels
-    if constexpr (CONTENT) __builtin_amdgcn_s_setprio(2);
-    const size_t srow = ((size_t)(b * H + h) * DV + v0 + 16 * cw + n) * DK;
-    if (p.S0) {
+    // cw < NWC: value rows v0 + 16 cw + n of S.  Content-aware, cw == NWC is the
+    // projection wave: row 0 of its tile is r = u_h^T S with value u_h . v_t,
+    // rows 1..15 stay zero; its outputs are not stored, they form the signal.
+    const int cw = wv - NWP - NWS;
+    f32x4 Sacc[NCT];
+    float wmean[4] = {0.f, 0.f, 0.f, 0.f};   // content-aware: last finished window's mean
+    auto consumer_role = [&](auto robust_tag, auto xw_tag) {
+      constexpr bool ROBUST = decltype(robust_tag)::value;
+      constexpr bool XW = decltype(xw_tag)::value;
+      if constexpr (CONTENT) __builtin_amdgcn_s_setprio(2);
+      const size_t sbh = (size_t)(b * H + h) * DV;
+      if constexpr (XW) {
+        // r = u_h^T S0: rows n, n + 16, ... summed per lane, then over n
+        f32x4 acc[NCT];
 #pragma unroll
-      for (int ct = 0; ct < NCT; ++ct) Sacc[ct] = *(const f32x4*)(p.S0 + srow + 16 * ct + 4 * g);
-    } else {
+        for (int ct = 0; ct < NCT; ++ct) acc[ct] = f32x4{0.f, 0.f, 0.f, 0.f};
+        if (p.S0) {
+          for (int i = n; i < DV; i += 16) {
+            const float ui = sU[i];
+            const float* row = p.S0 + (sbh + i) * DK + 4 * g;
 #pragma unroll
-      for (int ct = 0; ct < NCT; ++ct) Sacc[ct] = f32x4{0.f, 0.f, 0.f, 0.f};
-    }
-    // drain the state load here, so that inside the loop only the loop's own
-    // output stores are outstanding and no wait on them is needed
-    __builtin_amdgcn_s_waitcnt(0x0F70);   // vmcnt(0)
-    // o through a buffer resource over this wave's 16 value channels of (b, h):
-    // stores past token T-1 fall outside the resource and are dropped.
-    const size_t obh = (size_t)b * Tn * H + h;
-    const size_t orows = (size_t)(Tn - 1) * H + 1;
-    const int ocol = v0 + 16 * cw;
-    const rsrc_t ro = make_rsrc((bf*)p.o + obh * DV + ocol, orows * DV * 2 - (size_t)ocol * 2);
-    const int so = H * DV * 2;                     // bytes per token row
-    const int olane = n * so + 8 * g;              // token n, value channels 4g..4g+3
-    float colsum[4] = {0.f, 0.f, 0.f, 0.f};   // content-aware: window sums of 4 channels
-    int token_next = 0;   // range flag of the slot consumed at the next step
-    // One consumer step; TOKEN selects the token path (gdr_token.h) for a chunk
-    // whose decay leaves the split form's range.  The matrix-core steps run in
-    // an inner loop of their own that exits before such a chunk, so the rare
-    // path adds no branch to that loop's body.
-    auto step = [&](int it, auto token_tag) {
-      constexpr bool TOKEN = decltype(token_tag)::value;
+            for (int ct = 0; ct < NCT; ++ct) acc[ct] += ui * *(const f32x4*)(row + 16 * ct);
+          }
+        }
+#pragma unroll
+        for (int ct = 0; ct < NCT; ++ct) {
+#pragma unroll
+          for (int jj = 0; jj < 4; ++jj) {
+            float v = acc[ct][jj];
+#pragma unroll
+            for (int off = 1; off < 16; off <<= 1) v += __shfl_xor(v, off);
+            Sacc[ct][jj] = n == 0 ? v : 0.f;
+          }
+        }
+      } else {
+        const size_t srow = (sbh + v0 + 16 * cw + n) * DK;
+        if (p.S0) {
+#pragma unroll
+          for (int ct = 0; ct < NCT; ++ct) Sacc[ct] = *(const f32x4*)(p.S0 + srow + 16 * ct + 4 * g);
+        } else {
+#pragma unroll
+          for (int ct = 0; ct < NCT; ++ct) Sacc[ct] = f32x4{0.f, 0.f, 0.f, 0.f};
+        }
+      }
+      // drain the state load here, so that inside the loop only the loop's own
+      // output stores are outstanding and no wait on them is needed
+      __builtin_amdgcn_s_waitcnt(0x0F70);   // vmcnt(0)
+      // o through a buffer resource over this wave's 16 value channels of (b, h):
+      // stores past token T-1 fall outside the resource and are dropped.
+      const size_t obh = (size_t)b * Tn * H + h;
+      const size_t orows = (size_t)(Tn - 1) * H + 1;
+      const int ocol = XW ? 0 : v0 + 16 * cw;
+      const rsrc_t ro = make_rsrc((bf*)p.o + obh * DV + ocol, orows * DV * 2 - (size_t)ocol * 2);
+      const int so = H * DV * 2;                     // bytes per token row
+      const int olane = n * so + 8 * g;              // token n, value channels 4g..4g+3
+      // value of this lane's row n at token r of a chunk
+      auto vat = [&](const SlotA<DK, TV>& A, int r) {
+        if constexpr (XW) return n == 0 ? A.uv[r] : 0.f;
+        else return (float)A.V[r * RSV + 16 * cw + n];
+      };
+      float colsum[4] = {0.f, 0.f, 0.f, 0.f};   // content-aware: window sums
+      int token_next = 0;   // range flag of the slot consumed at the next step
+      // One consumer step; TOKEN selects the token path (gdr_token.h) for a
+      // chunk whose decay leaves the split form's range.
+      auto step = [&](int it, auto token_tag) {
+        constexpr bool TOKEN = decltype(token_tag)::value;
         const int vi = it - 2;
         const int i = CONTENT ? (vi >= 0 ? block_at(vi) : -1) : vi;
         if (CONTENT ? (i >= 0 && i < nchunks) : (i >= 0)) {
@@ -835,117 +931,132 @@ __global__ __launch_bounds__((NWP + NWS + TV / 16) * 64) void gdr_fwd_pipe_kerne
           const SlotS& S = sh.s[vi & 1];
           const int c0 = i * L;
           if constexpr (TOKEN) {
-              // token path (gdr_token.h): raw transition, keys and queries staged by
-              // the solve; o_t[n] is stored as one bf16 by the lanes with g == 0
-              const char* raw = (const char*)A.Kp;
-              const float* bt = CONTENT ? sBc[vi % 3][0] : A.beta;
-              const float* bwp = CONTENT ? sBc[vi % 3][1] : A.bw;
-              float fsum = 0.f;
-              token_steps<DK, DECAY, bf>(
-                  Sacc, (const float*)raw, (const bf*)(raw + L * DK * 4),
-                  (const bf*)(raw + L * DK * 6), DK, A.V + 16 * cw + n, RSV, bt, bwp,
-                  min(L, Tn - c0), [&](int t, float ov) {
-                    if (g == 0) {
-                      const bf ob = (bf)ov;
-                      __builtin_amdgcn_raw_buffer_store_b16(*(const unsigned short*)&ob, ro, 2 * n,
-                                                            (c0 + t) * so, 0);
-                    }
-                    fsum += ov;
-                  });
-              if constexpr (CONTENT) {
-                // window sums: value channel 4g + jj is kept by a lane of group g
-    #pragma unroll
+            // raw transition, keys and queries staged by the solve; o_t[n] is
+            // stored as one bf16 by the lanes with g == 0
+            const char* raw = (const char*)A.Kp;
+            const float* bt = CONTENT ? sBc[vi % 3][0] : A.beta;
+            const float* bwp = CONTENT ? sBc[vi % 3][1] : A.bw;
+            float fsum = 0.f;
+            token_steps<DK, DECAY, bf>(
+                Sacc, (const float*)raw, (const bf*)(raw + L * DK * 4),
+                (const bf*)(raw + L * DK * 6), DK, [&](int t) { return vat(A, t); }, bt, bwp,
+                min(L, Tn - c0), [&](int t, float ov) {
+                  if (!XW && g == 0) {
+                    const bf ob = (bf)ov;
+                    __builtin_amdgcn_raw_buffer_store_b16(*(const unsigned short*)&ob, ro, 2 * n,
+                                                          (c0 + t) * so, 0);
+                  }
+                  fsum += ov;
+                });
+            if constexpr (CONTENT) {
+              if constexpr (XW) {
+                colsum[0] += (n == 0 && g == 0) ? fsum : 0.f;
+              } else {
+                // value channel 4g + jj is kept by a lane of group g
+#pragma unroll
                 for (int jj = 0; jj < 4; ++jj) {
                   const float x = __shfl(fsum, 4 * g + jj);
                   colsum[jj] += n == 0 ? x : 0.f;
                 }
               }
+            }
           } else {
-          // R = diag(bw) V - diag(beta) K+ S^T;  Qs^T = (Q+ S^T)^T, kept transposed
-          // (lane holds one token and four value channels) for 8-byte o stores
-          frag Sf[NKC];
-  #pragma unroll
-          for (int kk = 0; kk < NKC; ++kk) Sf[kk] = O::from_acc(Sacc[2 * kk], Sacc[2 * kk + 1]);
-          f32x4 Rt[2], Qs[2];
-  #pragma unroll
-          for (int t = 0; t < 2; ++t) {
-            f32x4 P = {0.f, 0.f, 0.f, 0.f}, Q = {0.f, 0.f, 0.f, 0.f};
-  #pragma unroll
-            for (int kk = 0; kk < NKC; ++kk) {
-              O::mma(P, load_kq<DK, TV>(A.Kp, 16 * t, kk), Sf[kk]);
-              O::mma(Q, Sf[kk], load_kq<DK, TV>(A.Qp, 16 * t, kk));
+                    frag Sf[NKC];
+            #pragma unroll
+                    for (int kk = 0; kk < NKC; ++kk) Sf[kk] = O::from_acc(Sacc[2 * kk], Sacc[2 * kk + 1]);
+                    f32x4 Rt[2], Qs[2];
+            #pragma unroll
+                    for (int t = 0; t < 2; ++t) {
+                      f32x4 P = {0.f, 0.f, 0.f, 0.f}, Q = {0.f, 0.f, 0.f, 0.f};
+            #pragma unroll
+                      for (int kk = 0; kk < NKC; ++kk) {
+                        O::mma(P, load_kq<DK, TV>(A.Kp, 16 * t, kk), Sf[kk]);
+                        O::mma(Q, Sf[kk], load_kq<DK, TV>(A.Qp, 16 * t, kk));
+                      }
+                      const f32x4 bw4 = *(const f32x4*)((CONTENT ? sBc[vi % 3][1] : A.bw) + 16 * t + 4 * g);
+                      const f32x4 bt4 = *(const f32x4*)((CONTENT ? sBc[vi % 3][0] : A.beta) + 16 * t + 4 * g);
+            #pragma unroll
+                      for (int jj = 0; jj < 4; ++jj) {
+                        const int r = 16 * t + 4 * g + jj;
+                        Rt[t][jj] = bw4[jj] * vat(A, r) - bt4[jj] * P[jj];
+                      }
+                      Qs[t] = Q;
+                    }
+                    // Dl by blocks, O = Qs + M Dl
+                    f32x4 D0 = {0.f, 0.f, 0.f, 0.f}, D1 = {0.f, 0.f, 0.f, 0.f};
+                    O::mma(D0, load_cb_half<bf>(S.Td, RS16, 0, 0), O::from_acc_half(Rt[0]));
+                    const frag d0 = O::from_acc_half(D0);
+                    f32x4 Y = Rt[1];
+                    {
+                      const frag a10 = load_cb_half<bf>(S.A10, RS16, 0, 0);
+                      O::mma(Y, DECAY != 0 ? a10 : O::neg(a10), d0);
+                    }
+                    O::mma(D1, load_cb_half<bf>(S.Td + 16 * RS16, RS16, 0, 0), O::from_acc_half(Y));
+                    frag Df = d0;   // slots 0..3 from D0, 4..7 from D1
+            #pragma unroll
+                    for (int jj = 0; jj < 4; ++jj) Df[4 + jj] = (bf)D1[jj];
+                    // O^T = Qs^T + (M Dl)^T = Qs^T + Dl^T M^T
+                    f32x4 O0 = Qs[0], O1 = Qs[1];
+                    O::mma(O0, d0, load_cb_half<bf>(S.M, RSL, 0, 0));
+                    O::mma(O1, Df, load_cb<bf>(S.M, RSL, 16, 0));
+                    const bf16x4 ox0 = {(bf)O0[0], (bf)O0[1], (bf)O0[2], (bf)O0[3]};
+                    const bf16x4 ox1 = {(bf)O1[0], (bf)O1[1], (bf)O1[2], (bf)O1[3]};
+                    if constexpr (CONTENT) {
+                      // window sums of the fp32 outputs (tokens past T contribute zero);
+                      // the projection wave keeps value column 0 only: r_t . q_t
+                      if constexpr (XW) {
+                        colsum[0] += g == 0 ? O0[0] + O1[0] : 0.f;
+                      } else {
+          #pragma unroll
+                        for (int jj = 0; jj < 4; ++jj) colsum[jj] += O0[jj] + O1[jj];
+                      }
+                    }
+                    // S <- S Gamma_L + Dl^T K- = (S + Dl^T Kh) Gamma_L, since K- = Kh Gamma_L
+                    // column-wise (per channel, or per rotation pair)
+            #pragma unroll
+                    for (int ct = 0; ct < NCT; ++ct) {
+                      O::mma(Sacc[ct], load_cb<bf>(A.KhT, RSL, 16 * ct, 0), Df);
+                      const f32x4 z4 = *(const f32x4*)(A.GL + 8 * ct + 2 * g);   // channels 16ct+4g..+3
+            #pragma unroll
+                      for (int jj = 0; jj < 4; jj += 2) {
+                        const f32x2 z = {z4[jj], z4[jj + 1]};
+                        const float x0 = Sacc[ct][jj], x1 = Sacc[ct][jj + 1];
+                        if constexpr (DECAY == 0) {
+                          Sacc[ct][jj] = x0 * z.x;
+                          Sacc[ct][jj + 1] = x1 * z.y;
+                        } else {
+                          Sacc[ct][jj] = z.x * x0 + z.y * x1;
+                          Sacc[ct][jj + 1] = -z.y * x0 + z.x * x1;
+                        }
+                      }
+                    }
+            if constexpr (!XW) {   // o stores last, off the chain to the state update
+              typedef __attribute__((ext_vector_type(2))) unsigned u32x2;
+              __builtin_amdgcn_raw_buffer_store_b64(*(const u32x2*)&ox0, ro, olane, c0 * so, 0);
+              __builtin_amdgcn_raw_buffer_store_b64(*(const u32x2*)&ox1, ro, olane, (c0 + 16) * so, 0);
             }
-            const f32x4 bw4 = *(const f32x4*)((CONTENT ? sBc[vi % 3][1] : A.bw) + 16 * t + 4 * g);
-            const f32x4 bt4 = *(const f32x4*)((CONTENT ? sBc[vi % 3][0] : A.beta) + 16 * t + 4 * g);
-  #pragma unroll
-            for (int jj = 0; jj < 4; ++jj) {
-              const int r = 16 * t + 4 * g + jj;
-              Rt[t][jj] = bw4[jj] * (float)A.V[r * RSV + 16 * cw + n] - bt4[jj] * P[jj];
-            }
-            Qs[t] = Q;
           }
-          // Dl by blocks, O = Qs + M Dl
-          f32x4 D0 = {0.f, 0.f, 0.f, 0.f}, D1 = {0.f, 0.f, 0.f, 0.f};
-          O::mma(D0, load_cb_half<bf>(S.Td, RS16, 0, 0), O::from_acc_half(Rt[0]));
-          const frag d0 = O::from_acc_half(D0);
-          f32x4 Y = Rt[1];
-          {
-            const frag a10 = load_cb_half<bf>(S.A10, RS16, 0, 0);
-            O::mma(Y, DECAY != 0 ? a10 : O::neg(a10), d0);
-          }
-          O::mma(D1, load_cb_half<bf>(S.Td + 16 * RS16, RS16, 0, 0), O::from_acc_half(Y));
-          frag Df = d0;   // slots 0..3 from D0, 4..7 from D1
-  #pragma unroll
-          for (int jj = 0; jj < 4; ++jj) Df[4 + jj] = (bf)D1[jj];
-          // O^T = Qs^T + (M Dl)^T = Qs^T + Dl^T M^T
-          f32x4 O0 = Qs[0], O1 = Qs[1];
-          O::mma(O0, d0, load_cb_half<bf>(S.M, RSL, 0, 0));
-          O::mma(O1, Df, load_cb<bf>(S.M, RSL, 16, 0));
-          const bf16x4 ox0 = {(bf)O0[0], (bf)O0[1], (bf)O0[2], (bf)O0[3]};
-          const bf16x4 ox1 = {(bf)O1[0], (bf)O1[1], (bf)O1[2], (bf)O1[3]};
           if constexpr (CONTENT) {
-            // window sums of the fp32 outputs (tokens past T contribute zero);
-            // at a window's last block its per-channel mean goes to LDS, to be
-            // read by the solve of the next window's first block
-  #pragma unroll
-            for (int jj = 0; jj < 4; ++jj) colsum[jj] += O0[jj] + O1[jj];
-          }
-          // S <- S Gamma_L + Dl^T K- = (S + Dl^T Kh) Gamma_L, since K- = Kh Gamma_L
-          // column-wise (per channel, or per rotation pair)
-  #pragma unroll
-          for (int ct = 0; ct < NCT; ++ct) {
-            O::mma(Sacc[ct], load_cb<bf>(A.KhT, RSL, 16 * ct, 0), Df);
-            const f32x4 z4 = *(const f32x4*)(A.GL + 8 * ct + 2 * g);   // channels 16ct+4g..+3
-  #pragma unroll
-            for (int jj = 0; jj < 4; jj += 2) {
-              const f32x2 z = {z4[jj], z4[jj + 1]};
-              const float x0 = Sacc[ct][jj], x1 = Sacc[ct][jj + 1];
-              if constexpr (DECAY == 0) {
-                Sacc[ct][jj] = x0 * z.x;
-                Sacc[ct][jj + 1] = x1 * z.y;
-              } else {
-                Sacc[ct][jj] = z.x * x0 + z.y * x1;
-                Sacc[ct][jj + 1] = -z.y * x0 + z.x * x1;
-              }
-            }
-          }
-          {   // o stores last, off the chain from the barrier to the state update
-            typedef __attribute__((ext_vector_type(2))) unsigned u32x2;
-            __builtin_amdgcn_raw_buffer_store_b64(*(const u32x2*)&ox0, ro, olane, c0 * so, 0);
-            __builtin_amdgcn_raw_buffer_store_b64(*(const u32x2*)&ox1, ro, olane, (c0 + 16) * so, 0);
-          }
-          }
-          if constexpr (CONTENT) {
-            // at a window's last block its per-channel mean goes to LDS, to be
-            // read by the solve of the next window's first block
-            if (i % SPC == SPC - 1) {
-  #pragma unroll
-              for (int jj = 0; jj < 4; ++jj) {
-                float sum = colsum[jj];
-  #pragma unroll
+            if (i % SPC == SPC - 1) {   // a window's last block
+              const float inv = 1.f / (float)(SPC * L);
+              if constexpr (XW) {
+                // its signal, for the solve of the next window's first block
+                float sum = colsum[0];
+#pragma unroll
                 for (int off = 1; off < 16; off <<= 1) sum += __shfl_xor(sum, off);
-                if (n == 0) sMean[16 * cw + 4 * g + jj] = sum * (1.f / (float)(SPC * L));
-                colsum[jj] = 0.f;
+                sum += __shfl_xor(sum, 16);
+                sum += __shfl_xor(sum, 32);
+                if (l == 0) sS[0] = sum * inv;
+                colsum[0] = 0.f;
+              } else {
+#pragma unroll
+                for (int jj = 0; jj < 4; ++jj) {
+                  float sum = colsum[jj];
+#pragma unroll
+                  for (int off = 1; off < 16; off <<= 1) sum += __shfl_xor(sum, off);
+                  wmean[jj] = sum * inv;
+                  colsum[jj] = 0.f;
+                }
               }
             }
           }
@@ -958,37 +1069,44 @@ __global__ __launch_bounds__((NWP + NWS + TV / 16) * 64) void gdr_fwd_pipe_kerne
           token_next = __builtin_amdgcn_readfirstlane(f.x | f.y | f.z | f.w);
         }
         lds_barrier();
-    };
-    if constexpr (!ROBUST) {
-      for (int it = 0; it < nsteps; ++it) step(it, std::false_type{});
-    } else {
-      // the flag read in step it is that of the chunk consumed in step it + 1
-      int it = 0;
-      while (it < nsteps) {
-        for (; it < nsteps && token_next == 0; ++it) step(it, std::false_type{});
-        if (it < nsteps) {
-          step(it, std::true_type{});
-          ++it;
+      };
+      if constexpr (!ROBUST) {
+        for (int it = 0; it < nsteps; ++it) step(it, std::false_type{});
+      } else {
+        // the flag read in step it is that of the chunk consumed in step it + 1
+        int it = 0;
+        while (it < nsteps) {
+          for (; it < nsteps && token_next == 0; ++it) step(it, std::false_type{});
+          if (it < nsteps) {
+            step(it, std::true_type{});
+            ++it;
+          }
         }
       }
-    }
-      };
-    consumer_role(std::false_type{});
-    if (redo_needed(0)) {
-      reset_for_pass2();
-      consumer_role(std::true_type{});
-    }
-    const int cw = wv - NWP - NWS;
-    if (p.S_out) {
-      const size_t srow = ((size_t)(b * H + h) * DV + v0 + 16 * cw + n) * DK;
+    };
+    if (CONTENT && cw == NWC) {
+      consumer_role(std::false_type{}, std::true_type{});
+      if (redo_needed(0)) {
+        reset_for_pass2();
+        consumer_role(std::true_type{}, std::true_type{});
+      }
+    } else {
+      consumer_role(std::false_type{}, std::false_type{});
+      if (redo_needed(0)) {
+        reset_for_pass2();
+        consumer_role(std::true_type{}, std::false_type{});
+      }
+      if (p.S_out) {
+        const size_t srow = ((size_t)(b * H + h) * DV + v0 + 16 * cw + n) * DK;
 #pragma unroll
-      for (int ct = 0; ct < NCT; ++ct) *(f32x4*)(p.S_out + srow + 16 * ct + 4 * g) = Sacc[ct];
-    }
-    if constexpr (CONTENT) {   // the last window's mean (T is a multiple of the window)
-      if (p.m_carry && n == 0) {
+        for (int ct = 0; ct < NCT; ++ct) *(f32x4*)(p.S_out + srow + 16 * ct + 4 * g) = Sacc[ct];
+      }
+      if constexpr (CONTENT) {   // the last window's mean (T is a multiple of the window)
+        if (p.m_carry && n == 0) {
 #pragma unroll
-        for (int jj = 0; jj < 4; ++jj)
-          p.m_carry[(size_t)(b * H + h) * DV + 16 * cw + 4 * g + jj] = sMean[16 * cw + 4 * g + jj];
+          for (int jj = 0; jj < 4; ++jj)
+            p.m_carry[(size_t)(b * H + h) * DV + v0 + 16 * cw + 4 * g + jj] = wmean[jj];
+        }
       }
     }
   }
@@ -1000,8 +1118,9 @@ hipError_t launch(const FwdParams& p0, hipStream_t s) {
   p.n_vt = p.DV / TV;
   p.n_units = p.B * p.H;
   const int groups = (p.n_units + 7) / 8;
+  // content-aware: one more wave carries the projected row u_h^T S
   hipLaunchKernelGGL((gdr_fwd_pipe_kernel<DK, TV, DECAY, CONTENT>), dim3(groups * 8 * p.n_vt),
-                     dim3(Cfg<DK, TV>::NT), 0, s, p);
+                     dim3(Cfg<DK, TV>::NT + (CONTENT ? 64 : 0)), 0, s, p);
   return hipGetLastError();
 }
 
@@ -1017,9 +1136,11 @@ bool fwd_pipe_supported(const FwdParams& p) {
 
 hipError_t launch_fwd_pipe(const FwdParams& p, hipStream_t s) {
   const bool rot = p.decay != 0;
-  if (p.beta_logit != nullptr) {   // content-aware: one workgroup covers all value channels
-    if (p.DK == 128) return rot ? pipe::launch<128, 128, 1, true>(p, s) : pipe::launch<128, 128, 0, true>(p, s);
-    return rot ? pipe::launch<64, 64, 1, true>(p, s) : pipe::launch<64, 64, 0, true>(p, s);
+  if (p.beta_logit != nullptr) {
+    // content-aware: 16-channel value tiles, each workgroup with its own
+    // projection wave (few heads, long sequences: spread over more CUs)
+    if (p.DK == 128) return rot ? pipe::launch<128, 16, 1, true>(p, s) : pipe::launch<128, 16, 0, true>(p, s);
+    return rot ? pipe::launch<64, 16, 1, true>(p, s) : pipe::launch<64, 16, 0, true>(p, s);
   }
   if (p.DK == 128) {
     if ((long)p.B * p.H * 2 >= 192) {

@@ -62,12 +62,12 @@ __device__ inline float sum_over_g(float x) {
 //   tr [ntok][DK] fp32: DIAG alpha per channel; ROT2 (gamma cos, gamma sin) per
 //                       channel pair, pair p at channels 2p, 2p + 1
 //   kr, qr [ntok][ldk]: raw keys and queries (io type)
-//   vr: value row n of this wave at token t is vr[t * ldv]
+//   vval(t): value of row n of this wave at token t, as float
 //   beta[t], bw[t]: erase strength and beta * w
 // emit(t, o) is called on every lane with o = o_t[n] (the same on all four g).
-template <int DK, int DECAY, typename T, typename Emit>
+template <int DK, int DECAY, typename T, typename Val, typename Emit>
 __device__ inline void token_steps(f32x4 (&Sacc)[DK / 16], const float* tr, const T* kr,
-                                   const T* qr, int ldk, const T* vr, int ldv,
+                                   const T* qr, int ldk, Val vval,
                                    const float* beta, const float* bw, int ntok, Emit emit) {
   constexpr int NCT = DK / 16;
   const int g = (threadIdx.x & 63) >> 4;
@@ -94,7 +94,7 @@ __device__ inline void token_steps(f32x4 (&Sacc)[DK / 16], const float* tr, cons
       for (int j = 0; j < 4; ++j) part += Sacc[ct][j] * k4[j];
     }
     const float y = sum_over_g(part);
-    const float vn = (float)vr[t * ldv];
+    const float vn = vval(t);
     const float d = bw[t] * vn - beta[t] * y;   // beta (w v - y)
     const T* qp = qr + t * ldk + 4 * g;
     float op = 0.f;
