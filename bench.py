@@ -39,7 +39,7 @@ MFMA_BF16_PEAK_TFS = 2500.0    # dense bf16 matrix peak
 MFMA_F32_PEAK_TFS = 157.3
 TRAFFIC_FILE = os.path.join(ROOT, "profiles", "gdr_fwd_pipe_kernel_layer_traffic.txt")
 KERNEL_SRCS = [os.path.join(ROOT, "recurrent_state_memory_amd", "csrc", f)
-               for f in ("gdr_fwd_pipe.hip", "gdr_mfma.h", "gdr_kernels.h")]
+               for f in ("gdr_fwd_pipe.hip", "gdr_mfma.h", "gdr_kernels.h", "gdr_token.h")]
 
 
 def algorithmic_bytes(wl, s0: bool = False) -> int:
