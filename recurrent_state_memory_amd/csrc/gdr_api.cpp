@@ -23,9 +23,12 @@ gdr_status check_fwd(const gdr_fwd_args* a) {
     return GDR_ERR_SHAPE;
   if (!supported_d(a->dk) || a->dv != a->dk) return GDR_ERR_UNSUPPORTED;
   if (!supported_chunk(a->chunk)) return GDR_ERR_UNSUPPORTED;
-  // element counts must stay within 32-bit row indexing of the kernels
-  const long long rows = (long long)a->B * a->T * a->H;
-  if (rows * a->dk >= (1LL << 40) || (long long)a->B * a->T >= (1LL << 31)) return GDR_ERR_SHAPE;
+  // element counts must stay within 32-bit row indexing of the kernels; each
+  // product is bounded before the next one is formed, so none can overflow
+  const long long bt = (long long)a->B * a->T;   // < 2^62
+  if (bt >= (1LL << 31)) return GDR_ERR_SHAPE;
+  const long long rows = bt * a->H;              // < 2^62
+  if (rows >= (1LL << 40) / a->dk) return GDR_ERR_SHAPE;
   if (!a->q || !a->k || !a->v || !a->alpha || !a->w || !a->o) return GDR_ERR_NULL;
   const bool content = a->beta_logit != nullptr;
   if (content) {
@@ -77,6 +80,15 @@ gdr_status check_step(const gdr_step_args* a) {
 }
 
 }  // namespace
+
+namespace gdr {
+// WY block length of the sequential-stage kernel: the chunk, at most 64, and
+// at most 32 for fp32 operands at d_k = 128 (LDS of one CU).
+int fwd_block_len(int dk, int chunk, bool io_bf16) {
+  const int lmax = (!io_bf16 && dk == 128) ? 32 : 64;
+  return chunk < lmax ? chunk : lmax;
+}
+}  // namespace gdr
 
 extern "C" {
 

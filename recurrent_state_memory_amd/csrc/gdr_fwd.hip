@@ -716,9 +716,4 @@ hipError_t launch_fwd(const FwdParams& p, hipStream_t stream) {
   return pick_variant<float>(p, stream);
 }
 
-int fwd_block_len(int dk, int chunk, bool io_bf16) {
-  const int lmax = (!io_bf16 && dk == 128) ? 32 : 64;
-  return chunk < lmax ? chunk : lmax;
-}
-
 }  // namespace gdr

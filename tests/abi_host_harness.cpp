@@ -1,0 +1,106 @@
+// abi_host_harness.cpp -- the host half of libgdr (argument checks and parameter
+// marshalling in gdr_api.cpp) under AddressSanitizer and UndefinedBehaviorSanitizer.
+// The kernel launchers are replaced by recorders, so nothing touches a GPU; the
+// pointers are fake and never dereferenced.  Built and run by tests/test_abi.py.
+#include <cstdio>
+#include <cstdlib>
+#include <cstring>
+
+#include "gdr.h"
+#include "gdr_kernels.h"
+
+namespace gdr {
+static FwdParams g_fwd;
+static StepParams g_step;
+static int g_nfwd = 0, g_nstep = 0;
+hipError_t launch_fwd(const FwdParams& p, hipStream_t) {
+  g_fwd = p;
+  ++g_nfwd;
+  return hipSuccess;
+}
+hipError_t launch_step(const StepParams& p, hipStream_t) {
+  g_step = p;
+  ++g_nstep;
+  return hipSuccess;
+}
+}  // namespace gdr
+
+static int g_fail = 0;
+#define CHECK(c)                                                     \
+  do {                                                               \
+    if (!(c)) {                                                      \
+      std::fprintf(stderr, "%s:%d: check failed: %s\n", __FILE__, __LINE__, #c); \
+      ++g_fail;                                                      \
+    }                                                                \
+  } while (0)
+
+// 16 MiB apart: no two fake buffers overlap for the sizes used here
+static void* fake(unsigned k) { return (void*)((uintptr_t)0x1000000u * (k + 1)); }
+
+static gdr_fwd_args good_fwd() {
+  gdr_fwd_args a;
+  std::memset(&a, 0, sizeof a);
+  a.B = 2; a.T = 100; a.H = 4; a.dk = 128; a.dv = 128; a.chunk = 64;
+  a.io_dtype = GDR_BF16; a.decay = GDR_DECAY_DIAG;
+  a.q = fake(1); a.k = fake(2); a.v = fake(3); a.alpha = (const float*)fake(4);
+  a.beta = (const float*)fake(5); a.w = (const float*)fake(6); a.o = fake(7);
+  return a;
+}
+
+int main() {
+  // valid call: reaches the launcher with every field marshalled
+  gdr_fwd_args a = good_fwd();
+  a.S0 = (const float*)fake(8); a.S_out = (float*)fake(9);
+  CHECK(gdr_chunk_fwd(&a, nullptr) == GDR_OK);
+  CHECK(gdr::g_nfwd == 1);
+  CHECK(gdr::g_fwd.B == 2 && gdr::g_fwd.T == 100 && gdr::g_fwd.H == 4);
+  CHECK(gdr::g_fwd.DK == 128 && gdr::g_fwd.DV == 128 && gdr::g_fwd.io_bf16 == 1);
+  CHECK(gdr::g_fwd.block == 64 && gdr::g_fwd.window == 64);
+  CHECK(gdr::g_fwd.q == a.q && gdr::g_fwd.S0 == a.S0 && gdr::g_fwd.S_out == a.S_out);
+  // fp32 at d = 128 runs 32-token blocks
+  a.io_dtype = GDR_F32;
+  CHECK(gdr_chunk_fwd(&a, nullptr) == GDR_OK && gdr::g_fwd.block == 32);
+  // content-aware call
+  a = good_fwd();
+  a.beta = nullptr; a.beta_logit = (const float*)fake(10); a.ub_down = (const float*)fake(11);
+  a.ub_up = (const float*)fake(12); a.ub_rank = 16; a.chunk = 128; a.T = 256;
+  a.m_carry = (float*)fake(13);
+  CHECK(gdr_chunk_fwd(&a, nullptr) == GDR_OK && gdr::g_fwd.window == 128 && gdr::g_fwd.ub_rank == 16);
+
+  // rejected before any launch
+  const int before = gdr::g_nfwd;
+  CHECK(gdr_chunk_fwd(nullptr, nullptr) == GDR_ERR_NULL);
+  a = good_fwd(); a.B = 0; CHECK(gdr_chunk_fwd(&a, nullptr) == GDR_ERR_SHAPE);
+  a = good_fwd(); a.T = -5; CHECK(gdr_chunk_fwd(&a, nullptr) == GDR_ERR_SHAPE);
+  a = good_fwd(); a.dk = a.dv = 96; CHECK(gdr_chunk_fwd(&a, nullptr) == GDR_ERR_UNSUPPORTED);
+  a = good_fwd(); a.chunk = 48; CHECK(gdr_chunk_fwd(&a, nullptr) == GDR_ERR_UNSUPPORTED);
+  a = good_fwd(); a.io_dtype = 9; CHECK(gdr_chunk_fwd(&a, nullptr) == GDR_ERR_DTYPE);
+  a = good_fwd(); a.q = (const void*)((const char*)a.q + 4); CHECK(gdr_chunk_fwd(&a, nullptr) == GDR_ERR_ALIGN);
+  a = good_fwd(); a.theta = (const float*)fake(20); CHECK(gdr_chunk_fwd(&a, nullptr) == GDR_ERR_ARG);
+  a = good_fwd(); a.S0 = (const float*)fake(30); a.S_out = (float*)((char*)fake(30) + 64);
+  CHECK(gdr_chunk_fwd(&a, nullptr) == GDR_ERR_ARG);
+  a = good_fwd(); a.workspace_bytes = 64; CHECK(gdr_chunk_fwd(&a, nullptr) == GDR_ERR_WORKSPACE);
+  // extreme sizes: the element-count checks must not overflow
+  a = good_fwd(); a.B = 0x7fffffff; a.T = 0x7fffffff; a.H = 0x7fffffff;
+  CHECK(gdr_chunk_fwd(&a, nullptr) == GDR_ERR_SHAPE);
+  a = good_fwd(); a.T = 1 << 30; a.B = 4; CHECK(gdr_chunk_fwd(&a, nullptr) == GDR_ERR_SHAPE);
+  CHECK(gdr::g_nfwd == before);
+
+  // decode
+  gdr_step_args s;
+  std::memset(&s, 0, sizeof s);
+  s.N = 256; s.H = 16; s.dk = 128; s.dv = 128; s.io_dtype = GDR_BF16; s.decay = GDR_DECAY_ROT2;
+  s.q = fake(1); s.k = fake(2); s.v = fake(3); s.alpha = (const float*)fake(4);
+  s.theta = (const float*)fake(5); s.beta = (const float*)fake(6); s.w = (const float*)fake(7);
+  s.S = (float*)fake(8); s.o = fake(9);
+  CHECK(gdr_step_decode(&s, nullptr) == GDR_OK && gdr::g_nstep == 1 && gdr::g_step.decay == 1);
+  s.N = 0x7fffffff; s.H = 0x7fffffff; CHECK(gdr_step_decode(&s, nullptr) == GDR_ERR_SHAPE);
+  CHECK(gdr_step_decode(nullptr, nullptr) == GDR_ERR_NULL);
+
+  for (int st = -1; st < 12; ++st) CHECK(gdr_status_str((gdr_status)st) != nullptr);
+  CHECK(gdr_abi_version() == GDR_ABI_VERSION);
+  CHECK(gdr_chunk_fwd_workspace(nullptr) == 0);
+  if (g_fail) return 1;
+  std::printf("ABI_HARNESS_OK\n");
+  return 0;
+}
