@@ -141,3 +141,40 @@ def decode_step(S, q, k, v, beta, w, alpha, theta=None, decay="diag"):
     """One token for N independent states [N,H,d_v,d_k]; returns (S', o)."""
     return delta_step(_f64(S), _f64(q), _f64(k), _f64(v), _f64(beta), _f64(w),
                       _f64(alpha), _f64(theta), decay)
+
+
+# ----------------------------------------------------------------------------
+# Gate activation and q/k normalisation inside the forward (CARVE technical
+# summary, section 2.3: the decay activation is computed where it is used).
+# ----------------------------------------------------------------------------
+L2NORM_EPS = 1e-6   # q / sqrt(sum q^2 + eps): the pages give no epsilon; a reading
+
+
+def softplus(x):
+    """log(1 + e^x) in a form that neither overflows nor loses small values."""
+    x = np.asarray(x, dtype=np.float64)
+    return np.maximum(x, 0.0) + np.log1p(np.exp(-np.abs(x)))
+
+
+def gated_decay(x, a):
+    """Decay from its pre-activation: exp(-a_h softplus(x)), a_h per head.
+
+    x [..., H, C] (C = d_k, or d_k/2 block magnitudes); a [H] with a_h >= 0."""
+    x = np.asarray(x, dtype=np.float64)
+    a = np.asarray(a, dtype=np.float64)
+    return np.exp(-a[:, None] * softplus(x))
+
+
+def l2_normalise(x, eps=L2NORM_EPS):
+    """x / sqrt(sum x^2 + eps) over the last axis (one token of one head)."""
+    x = np.asarray(x, dtype=np.float64)
+    return x / np.sqrt(np.sum(x * x, axis=-1, keepdims=True) + eps)
+
+
+def forward_gated(q_raw, k_raw, v, w, x, a, beta, theta=None, decay="diag", S0=None,
+                  qk_l2norm=True):
+    """The forward with the decay given as a pre-activation and, optionally, raw q
+    and k normalised per token: forward(l2(q), l2(k), v, w, exp(-a softplus(x)))."""
+    q = l2_normalise(q_raw) if qk_l2norm else _f64(q_raw)
+    k = l2_normalise(k_raw) if qk_l2norm else _f64(k_raw)
+    return forward(q, k, v, w, gated_decay(x, a), beta=beta, theta=theta, decay=decay, S0=S0)

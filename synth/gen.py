@@ -240,3 +240,42 @@ def generate_decode(wl: Workload = WORKLOADS["rot"], N: int = DECODE_N,
         _sigmoid(b_logit), _sigmoid(w_logit),
         np.exp(np.float32(-wl.decay_scale) * _softplus(a_noise)).astype(np.float32),
         theta)
+
+
+@dataclasses.dataclass
+class GatedInputs:
+    """Inputs of the gated forward: raw (unnormalised) q and k, and the decay as
+    its pre-activation x with a per-head scale a (decay = exp(-a softplus(x)))."""
+    wl: Workload
+    q: np.ndarray          # [B,T,H,dk] bf16-valued, not normalised
+    k: np.ndarray
+    v: np.ndarray          # [B,T,H,dv]
+    beta: np.ndarray       # [B,T,H]
+    w: np.ndarray          # [B,T,H]
+    x: np.ndarray          # diag: [B,T,H,dk]; rot2: [B,T,H,dk/2], bf16-valued
+    a: np.ndarray          # [H] fp32
+    theta: Optional[np.ndarray]
+
+
+def generate_gated(wl: Workload, T: Optional[int] = None) -> GatedInputs:
+    """The recipe's draws in the recipe's order, passed on before the transforms
+    that the gated forward applies itself: q, k and the decay noise are rounded
+    to bf16 as drawn; a_h is the recipe's decay scale for every head."""
+    if T is not None:
+        wl = wl.replace(T=T)
+    rng = np.random.default_rng(wl.seed)
+    Bn, Tn, H, dk, dv = wl.B, wl.T, wl.H, wl.dk, wl.dv
+    q = rng.standard_normal((Bn, Tn, H, dk), dtype=np.float32)
+    k = rng.standard_normal((Bn, Tn, H, dk), dtype=np.float32)
+    v = rng.standard_normal((Bn, Tn, H, dv), dtype=np.float32)
+    b_logit = rng.standard_normal((Bn, Tn, H), dtype=np.float32)
+    w_logit = rng.standard_normal((Bn, Tn, H), dtype=np.float32)
+    theta = None
+    if wl.decay == "diag":
+        noise = rng.standard_normal((Bn, Tn, H, dk), dtype=np.float32)
+    else:
+        theta = rng.uniform(-math.pi, math.pi, (Bn, Tn, H, dk // 2)).astype(np.float32)
+        noise = rng.standard_normal((Bn, Tn, H, dk // 2), dtype=np.float32)
+    return GatedInputs(wl, bf16_round(q), bf16_round(k), _io_cast(v, "bf16"), _sigmoid(b_logit),
+                       _sigmoid(w_logit), bf16_round(noise),
+                       np.full((H,), wl.decay_scale, dtype=np.float32), theta)

@@ -447,3 +447,53 @@ def test_strong_decay_closed_form():
     scale = np.einsum("bhvk,bthk,bthk->bthv", np.abs(S0), G, np.abs(q))   # sum of |terms|
     assert np.all(np.abs(o - o_ref) <= 1e-13 * scale)
     np.testing.assert_allclose(S, S0 * G[:, -1, :, None, :], rtol=1e-12, atol=0)
+
+
+# ---------------------------------------------------------------- gated forward
+def test_gated_decay_closed_forms():
+    """softplus(0) = ln 2, so a = 1 gives a decay of exactly 1/2; a = 0 gives 1 for
+    any x; x -> -inf gives 1; x = 50 gives e^{-50 a} (softplus(x) = x + log1p(e^-x));
+    x = 1000 does not overflow: e^{-1000 a}."""
+    x = np.array([[0.0, 0.0], [-1000.0, 50.0], [1000.0, 3.0]])
+    d = seq.gated_decay(x[None], np.array([1.0, 0.0, 0.1]))[0]
+    assert d[0, 0] == 0.5 and d[0, 1] == 0.5
+    assert d[1, 0] == 1.0 and d[1, 1] == 1.0          # a = 0
+    assert d[2, 0] == pytest.approx(np.exp(-100.0), rel=1e-13)
+    assert d[2, 1] == pytest.approx(np.exp(-0.1 * (3.0 + np.log1p(np.exp(-3.0)))), rel=1e-15)
+    d50 = seq.gated_decay(np.array([[[50.0]]]), np.array([0.1]))
+    assert d50[0, 0, 0] == pytest.approx(np.exp(-5.0), rel=1e-14)
+    assert seq.gated_decay(np.array([[[-1000.0]]]), np.array([3.0]))[0, 0, 0] == 1.0
+
+
+def test_l2_normalise_hand_values():
+    """(3, 4) -> (0.6, 0.8) up to the epsilon; scale-invariant; a zero vector stays
+    zero (the epsilon keeps it finite)."""
+    v = seq.l2_normalise(np.array([3.0, 4.0, 0.0]), eps=0.0)
+    assert list(v) == [0.6, 0.8, 0.0]
+    v = seq.l2_normalise(np.array([3.0, 4.0]))
+    np.testing.assert_allclose(v, [0.6, 0.8], rtol=1e-7)
+    np.testing.assert_array_equal(seq.l2_normalise(np.zeros(4)), np.zeros(4))
+
+
+def test_forward_gated_matches_explicit_inputs():
+    """With x = 0 and a = 1 (decay exactly 1/2) and raw keys/queries that are
+    multiples of unit vectors, the gated forward equals the plain forward on the
+    unit vectors and alpha = 1/2 -- values fixed without the activation's formula."""
+    rng = np.random.default_rng(8)
+    B, T, H, dk, dv = 2, 12, 3, 8, 6
+    qu = rng.standard_normal((B, T, H, dk)); qu /= np.linalg.norm(qu, axis=-1, keepdims=True)
+    ku = rng.standard_normal((B, T, H, dk)); ku /= np.linalg.norm(ku, axis=-1, keepdims=True)
+    sq = rng.uniform(0.5, 4.0, (B, T, H, 1)); sk = rng.uniform(0.5, 4.0, (B, T, H, 1))
+    v = rng.standard_normal((B, T, H, dv))
+    w = rng.uniform(0, 1, (B, T, H)); beta = rng.uniform(0, 1, (B, T, H))
+    o1, S1 = seq.forward_gated(qu * sq, ku * sk, v, w, np.zeros((B, T, H, dk)), np.ones(H), beta)
+    o2, S2 = seq.forward(qu, ku, v, w, np.full((B, T, H, dk), 0.5), beta=beta)
+    np.testing.assert_allclose(o1, o2, rtol=0, atol=1e-6)   # eps = 1e-6 against norms >= 0.5
+    np.testing.assert_allclose(S1, S2, rtol=0, atol=1e-6)
+    # rotation blocks: the pre-activation drives the block magnitude
+    x = np.zeros((B, T, H, dk // 2))
+    th = rng.uniform(-np.pi, np.pi, (B, T, H, dk // 2))
+    o1, _ = seq.forward_gated(qu * sq, ku * sk, v, w, x, np.ones(H), beta, theta=th, decay="rot2")
+    o2, _ = seq.forward(qu, ku, v, w, np.full((B, T, H, dk // 2), 0.5), beta=beta, theta=th,
+                        decay="rot2")
+    np.testing.assert_allclose(o1, o2, rtol=0, atol=1e-6)
