@@ -42,11 +42,14 @@ KERNEL_SRCS = [os.path.join(ROOT, "recurrent_state_memory_amd", "csrc", f)
                for f in ("gdr_fwd_pipe.hip", "gdr_mfma.h", "gdr_kernels.h", "gdr_token.h")]
 
 
-def algorithmic_bytes(wl, s0: bool = False) -> int:
+def algorithmic_bytes(wl, s0: bool = False, gated: bool = False) -> int:
     """Bytes the forward must move at least once: q, k, v, transition, beta, w
-    in; o out; S_out (and S0 when given)."""
+    in; o out; S_out (and S0 when given).  Gated forward: the decay as a bf16
+    pre-activation (2 bytes per channel, or per block beside the fp32 angle)."""
     s_in = 2 if wl.io == "bf16" else 4
     trans = 4 * wl.dk  # alpha [dk] fp32, or theta + gamma [dk/2] each
+    if gated:
+        trans = 2 * wl.dk if wl.decay == "diag" else (2 + 4) * (wl.dk // 2)
     per_th = (2 * wl.dk + wl.dv) * s_in + trans + 8 + wl.dv * s_in
     state = 4 * wl.dv * wl.dk * wl.B * wl.H
     return per_th * wl.B * wl.T * wl.H + state * (2 if s0 else 1)
@@ -131,6 +134,25 @@ def _fwd_closure(wl):
     return step, x
 
 
+def _gated_closure(wl):
+    """The gated forward on the workload's raw draws: decay from its bf16
+    pre-activation, q and k normalised in the kernel."""
+    import torch
+    import recurrent_state_memory_amd as gdr
+    from synth.gen import generate_gated
+    x = generate_gated(wl)
+    bf = torch.bfloat16
+    q, k, v, xx = (_to_dev(t, bf) for t in (x.q, x.k, x.v, x.x))
+    a, theta, beta, w = map(_to_dev, (x.a, x.theta, x.beta, x.w))
+    o = torch.empty((wl.B, wl.T, wl.H, wl.dv), dtype=bf, device="cuda")
+    S = torch.empty((wl.B, wl.H, wl.dv, wl.dk), dtype=torch.float32, device="cuda")
+
+    def step():
+        gdr.gdr_chunk_fwd_gated(q, k, v, xx, a, w, beta, theta=theta, qk_l2norm=True,
+                                chunk=wl.chunk, o=o, S_out=S)
+    return step, x
+
+
 def _decode_closure():
     import torch
     import recurrent_state_memory_amd as gdr
@@ -195,7 +217,7 @@ def _cpu_model() -> str:
     return "unknown"
 
 
-def cpu_baseline(wl, x, budget_s: float = 15.0):
+def cpu_baseline(wl, x, budget_s: float = 15.0, gated: bool = False):
     """Time the fp64 oracle on this host's cores: one worker thread per group of
     batch rows (numpy releases the interpreter lock inside its array operations),
     BLAS single-threaded in each, all B*H heads over a prefix of the sequence
@@ -216,9 +238,12 @@ def cpu_baseline(wl, x, budget_s: float = 15.0):
     def run(part, T_s):
         b, h0, h1 = part
         sl = (slice(b, b + 1), slice(0, T_s), slice(h0, h1))
+        th = None if x.theta is None else x.theta[sl]
+        if gated:
+            return seq.forward_gated(x.q[sl], x.k[sl], x.v[sl], x.w[sl], x.x[sl], x.a[h0:h1],
+                                     x.beta[sl], theta=th, decay=wl.decay)[0]
         return seq.forward(x.q[sl], x.k[sl], x.v[sl], x.w[sl], x.alpha[sl],
-                           beta=x.beta[sl], decay=wl.decay,
-                           theta=None if x.theta is None else x.theta[sl])[0]
+                           beta=x.beta[sl], decay=wl.decay, theta=th)[0]
 
     with threadpool_limits(limits=1), cf.ThreadPoolExecutor(max_workers=workers) as ex:
         # probe the per-token cost on a short prefix, then size the sample
@@ -246,6 +271,8 @@ def main(argv=None):
     ap.add_argument("--workload", default="layer",
                     choices=["layer", "small", "rot", "long", "tiny", "decode", "copy"])
     ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--gated", action="store_true",
+                    help="gdr_chunk_fwd_gated: bf16 decay pre-activation, q/k normalised in the kernel")
     a = ap.parse_args(argv)
     if a.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) != 1:
         print("bench.py measures one GPU only: the forward runs independent (b, h) units "
@@ -284,19 +311,23 @@ def main(argv=None):
         return 0
 
     wl = WORKLOADS[a.workload]
-    step, x = _fwd_closure(wl)
-    flush = algorithmic_bytes(wl) < MALL_BYTES
+    gated = a.gated
+    if gated and (wl.content or wl.io != "bf16" or wl.dk not in (64, 128)):
+        print("--gated runs the bf16 plain-erase workloads with d in {64, 128}", file=sys.stderr)
+        return 2
+    step, x = _gated_closure(wl) if gated else _fwd_closure(wl)
+    flush = algorithmic_bytes(wl, gated=gated) < MALL_BYTES
     secs, wall = _time(step, a.steps, a.warmup, flush=flush)
     per = secs / a.steps
     tokens = wl.B * wl.T
     value = tokens / per
     from recurrent_state_memory_amd.build import ARCH  # noqa: F401  (built for gfx950)
-    nbytes = algorithmic_bytes(wl)
+    nbytes = algorithmic_bytes(wl, gated=gated)
     L_eff = wy_block(wl)
     flops = algorithmic_flops(wl, L_eff)
     achieved = nbytes / per / 1e9
     mfma_peak = MFMA_BF16_PEAK_TFS if wl.io == "bf16" else MFMA_F32_PEAK_TFS
-    traffic = _traffic() if a.workload == "layer" else None
+    traffic = _traffic() if a.workload == "layer" and not gated else None
     out = {
         "metric": METRIC,
         "value": round(value, 1),
@@ -309,12 +340,16 @@ def main(argv=None):
         "scaling": "weak",
         "vs_baseline": None,
         "dtype": wl.io,
-        "data": "synthetic (seeded; q,k L2-normalised, gates from the stated distributions)",
+        "data": ("synthetic (seeded; q,k L2-normalised, gates from the stated distributions)"
+                 if not gated else
+                 "synthetic (seeded; raw q,k and decay pre-activations from the stated distributions)"),
         "config": {
             "workload": (f"{wl.name}: B={wl.B} H={wl.H} T={wl.T} d_k=d_v={wl.dk} chunk={wl.chunk} "
                          f"({L_eff}-token WY blocks{', MALL flushed between launches' if flush else ''}) "
-                         f"{wl.io} q/k/v, fp32 gates and state, "
-                         f"{'2x2 rotation-decay' if wl.decay == 'rot2' else 'per-channel decay'}"
+                         + (f"{wl.io} q/k/v, fp32 gates and state, " if not gated else
+                            "gated: bf16 raw q/k (L2-normalised in the kernel), bf16 v, bf16 decay "
+                            "pre-activation exp(-a softplus(x)), fp32 beta/w/state, ")
+                         + f"{'2x2 rotation-decay' if wl.decay == 'rot2' else 'per-channel decay'}"
                          f"{', content-aware erase' if wl.content else ''}"),
             "global_batch": wl.B, "seq_len": wl.T, "parallelism": "single GPU",
         },
@@ -333,7 +368,7 @@ def main(argv=None):
         "wall_s_timed_region": round(wall, 4),
     }
     if not a.no_cpu_baseline and a.workload in ("layer", "small", "rot", "tiny"):
-        out["cpu_baseline"] = cpu_baseline(wl, x)
+        out["cpu_baseline"] = cpu_baseline(wl, x, gated=gated)
     print(json.dumps(out))
     return 0
 

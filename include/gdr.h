@@ -134,6 +134,36 @@ size_t gdr_chunk_fwd_workspace(const gdr_fwd_args *a);
 gdr_status gdr_chunk_fwd(const gdr_fwd_args *a, void *hip_stream);
 
 /* ------------------------------------------------------------------------ */
+/* Forward with the gate activation and the q/k normalisation in the kernel. */
+/* ------------------------------------------------------------------------ */
+/* CARVE technical summary, section 2.3: the decay activation is computed in
+ * the kernel from its pre-activation instead of being stored for the whole
+ * sequence.  Here
+ *
+ *     decay_t = exp(-a_h * softplus(x_t)),   softplus(x) = log(1 + e^x),
+ *
+ * per key channel (DIAG) or per 2x2 block magnitude (ROT2, with the angles in
+ * gdr_fwd_args.theta as before), so every decay lies in (0, 1] for a_h >= 0.
+ * With qk_l2norm, q and k are raw and each token's q and k are divided by
+ * sqrt(sum of squares over d_k + 1e-6) in the kernel.  The result equals
+ * gdr_chunk_fwd on the activated, normalised inputs up to rounding.  The
+ * decay pre-activation in bf16 halves the decay's bytes (2 instead of 4 per
+ * channel and token).
+ *
+ * Supported: io_dtype BF16, dk == dv in {64, 128}, the plain erase (beta given,
+ * no content-aware arguments), T * H * dk < 2^29; otherwise
+ * GDR_ERR_UNSUPPORTED.  gdr_fwd_args.alpha must be NULL (the decay comes from
+ * decay_x); every other field keeps its meaning. */
+typedef struct gdr_gate_args {
+  const void *decay_x;  /* bf16 pre-activation: DIAG [B,T,H,dk], ROT2 [B,T,H,dk/2] */
+  const float *decay_a; /* [H] per-head scale a_h >= 0 (fp32)                      */
+  int32_t qk_l2norm;    /* nonzero: normalise each token's q and k in the kernel   */
+  int32_t reserved;     /* must be 0                                               */
+} gdr_gate_args;
+
+gdr_status gdr_chunk_fwd_gated(const gdr_fwd_args *a, const gdr_gate_args *g, void *hip_stream);
+
+/* ------------------------------------------------------------------------ */
 /* Single-token decode step on N independent states, in place.               */
 /* ------------------------------------------------------------------------ */
 typedef struct gdr_step_args {

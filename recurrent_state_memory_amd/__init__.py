@@ -9,6 +9,8 @@ If the library has not been built, every call raises ``RuntimeError``.
 Entry points (same names as the C ABI):
 
 * ``gdr_chunk_fwd``   -- chunked forward over a sequence, returns (o, S_out)
+* ``gdr_chunk_fwd_gated`` -- the same with the decay activation (and optionally
+  the q/k L2 normalisation) computed in the kernel from raw inputs
 * ``gdr_step_decode`` -- one token on a batch of states, in place, returns o
 """
 from __future__ import annotations
@@ -43,6 +45,11 @@ class FwdArgs(ctypes.Structure):
     ]
 
 
+class GateArgs(ctypes.Structure):
+    """Mirror of ``gdr_gate_args``."""
+    _fields_ = [("decay_x", _vp), ("decay_a", _vp), ("qk_l2norm", _i32), ("reserved", _i32)]
+
+
 class StepArgs(ctypes.Structure):
     """Mirror of ``gdr_step_args``."""
     _fields_ = [
@@ -74,6 +81,8 @@ def load_library(path: Optional[str] = None) -> ctypes.CDLL:
     lib = ctypes.CDLL(p)
     lib.gdr_chunk_fwd.argtypes = [ctypes.POINTER(FwdArgs), _vp]
     lib.gdr_chunk_fwd.restype = ctypes.c_int
+    lib.gdr_chunk_fwd_gated.argtypes = [ctypes.POINTER(FwdArgs), ctypes.POINTER(GateArgs), _vp]
+    lib.gdr_chunk_fwd_gated.restype = ctypes.c_int
     lib.gdr_chunk_fwd_workspace.argtypes = [ctypes.POINTER(FwdArgs)]
     lib.gdr_chunk_fwd_workspace.restype = ctypes.c_size_t
     lib.gdr_step_decode.argtypes = [ctypes.POINTER(StepArgs), _vp]
@@ -144,6 +153,14 @@ def call_chunk_fwd(args: FwdArgs, stream=None) -> int:
     s = stream if isinstance(stream, ctypes.c_void_p) else (
         ctypes.c_void_p(0) if stream is None else _stream(stream))
     return lib.gdr_chunk_fwd(ctypes.byref(args), s)
+
+
+def call_chunk_fwd_gated(args: FwdArgs, gate: GateArgs, stream=None) -> int:
+    """Raw call with filled ``FwdArgs`` and ``GateArgs``; returns the status code."""
+    lib = load_library()
+    s = stream if isinstance(stream, ctypes.c_void_p) else (
+        ctypes.c_void_p(0) if stream is None else _stream(stream))
+    return lib.gdr_chunk_fwd_gated(ctypes.byref(args), ctypes.byref(gate), s)
 
 
 def call_step_decode(args: StepArgs, stream=None) -> int:
@@ -217,6 +234,60 @@ def gdr_chunk_fwd(q, k, v, alpha, w, beta=None, *, theta=None, S0=None, chunk=64
     a.S0, a.o, a.S_out = _ptr(S0), _ptr(o), _ptr(S_out)
     a.workspace, a.workspace_bytes = None, 0
     _check(call_chunk_fwd(a, _stream(stream)))
+    return o, S_out
+
+
+def gdr_chunk_fwd_gated(q, k, v, decay_x, decay_a, w, beta, *, theta=None, qk_l2norm=True,
+                        S0=None, chunk=64, o=None, S_out=None, return_state=True, stream=None):
+    """Forward with the decay activation in the kernel (``gdr_chunk_fwd_gated`` in
+    include/gdr.h): decay = exp(-decay_a[h] * softplus(decay_x)).
+
+    q, k [B,T,H,dk], v [B,T,H,dv] bf16 (raw q, k when ``qk_l2norm``); decay_x
+    bf16 [B,T,H,dk] (per-channel decay) or [B,T,H,dk/2] with ``theta`` fp32 of
+    the same shape (2x2 rotation-decay blocks); decay_a fp32 [H]; beta, w fp32
+    [B,T,H].  Returns (o [B,T,H,dv] bf16, S_out [B,H,dv,dk] fp32 or None).
+    Shapes, dtypes and contiguity are checked first.
+    """
+    import torch
+    if q.dim() != 4 or k.dim() != 4 or v.dim() != 4:
+        raise ValueError("gdr: q, k and v must be [B,T,H,d]")
+    B, T, H, dk = q.shape
+    dv = v.shape[-1]
+    bf, f32 = torch.bfloat16, torch.float32
+    _expect(q, "q", (B, T, H, dk), bf)
+    _expect(k, "k", (B, T, H, dk), bf)
+    _expect(v, "v", (B, T, H, dv), bf)
+    rot = theta is not None
+    if rot and dk % 2:
+        raise ValueError("gdr: rotation-decay blocks need an even d_k")
+    gshape = (B, T, H, dk // 2) if rot else (B, T, H, dk)
+    _expect(decay_x, "decay_x", gshape, bf)
+    _expect(theta, "theta", gshape, f32, required=False)
+    _expect(decay_a, "decay_a", (H,), f32)
+    _expect(w, "w", (B, T, H), f32)
+    _expect(beta, "beta", (B, T, H), f32)
+    _expect(S0, "S0", (B, H, dv, dk), f32, required=False)
+    if o is None:
+        o = torch.empty((B, T, H, dv), dtype=bf, device=q.device)
+    _expect(o, "o", (B, T, H, dv), bf)
+    if S_out is None and return_state:
+        S_out = torch.empty((B, H, dv, dk), dtype=f32, device=q.device)
+    _expect(S_out, "S_out", (B, H, dv, dk), f32, required=False)
+    a = FwdArgs()
+    a.B, a.T, a.H, a.dk, a.dv, a.chunk = B, T, H, dk, dv, chunk
+    a.io_dtype = GDR_BF16
+    a.decay = GDR_DECAY_ROT2 if rot else GDR_DECAY_DIAG
+    a.q, a.k, a.v, a.theta = map(_ptr, (q, k, v, theta))
+    a.alpha = None
+    a.beta, a.w = _ptr(beta), _ptr(w)
+    a.beta_logit = a.ub_down = a.ub_up = a.m_carry = None
+    a.ub_rank = 0
+    a.S0, a.o, a.S_out = _ptr(S0), _ptr(o), _ptr(S_out)
+    a.workspace, a.workspace_bytes = None, 0
+    g = GateArgs()
+    g.decay_x, g.decay_a = _ptr(decay_x), _ptr(decay_a)
+    g.qk_l2norm, g.reserved = int(bool(qk_l2norm)), 0
+    _check(call_chunk_fwd_gated(a, g, _stream(stream)))
     return o, S_out
 
 

@@ -88,18 +88,19 @@ int fwd_block_len(int dk, int chunk, bool io_bf16) {
   const int lmax = (!io_bf16 && dk == 128) ? 32 : 64;
   return chunk < lmax ? chunk : lmax;
 }
+
+// Whether the pipelined kernel takes the call (bf16, d_k = d_v in {64, 128}).
+bool fwd_pipe_supported(const FwdParams& p) {
+  // buffer resources address one (b, h) with 32-bit byte offsets
+  const bool fits = (unsigned long long)p.T * p.H * p.DK * 4ull < (1ull << 31);
+  // content-aware: the window must be a whole number of 32-token blocks
+  const bool content_ok = p.beta_logit == nullptr || (p.window >= 32 && p.window % 32 == 0);
+  return p.io_bf16 && content_ok && (p.DK == 64 || p.DK == 128) && p.DV == p.DK && fits;
+}
 }  // namespace gdr
 
-extern "C" {
-
-size_t gdr_chunk_fwd_workspace(const gdr_fwd_args* a) {
-  (void)a;
-  return 0;
-}
-
-gdr_status gdr_chunk_fwd(const gdr_fwd_args* a, void* hip_stream) {
-  const gdr_status st = check_fwd(a);
-  if (st != GDR_OK) return st;
+namespace {
+gdr::FwdParams fwd_params(const gdr_fwd_args* a) {
   gdr::FwdParams p{};
   p.B = a->B;
   p.T = a->T;
@@ -125,6 +126,52 @@ gdr_status gdr_chunk_fwd(const gdr_fwd_args* a, void* hip_stream) {
   p.S0 = a->S0;
   p.o = a->o;
   p.S_out = a->S_out;
+  return p;
+}
+
+// The gated forward's own conditions, on top of check_fwd's (which sees
+// decay_x in place of alpha).
+gdr_status check_gated(const gdr_fwd_args* a, const gdr_gate_args* g) {
+  if (!a || !g) return GDR_ERR_NULL;
+  if (g->reserved != 0) return GDR_ERR_ARG;
+  if (a->alpha) return GDR_ERR_ARG;
+  if (!g->decay_x || !g->decay_a) return GDR_ERR_NULL;
+  gdr_fwd_args c = *a;
+  c.alpha = static_cast<const float*>(g->decay_x);   // checked for presence and alignment only
+  const gdr_status st = check_fwd(&c);
+  if (st != GDR_OK) return st;
+  if (a->io_dtype != GDR_BF16) return GDR_ERR_UNSUPPORTED;
+  if (a->dk != 64 && a->dk != 128) return GDR_ERR_UNSUPPORTED;
+  if (a->beta_logit) return GDR_ERR_UNSUPPORTED;
+  // 32-bit byte offsets of the kernel's buffer resources (T * H * dk < 2^29)
+  if ((long long)a->T * a->H >= (1LL << 29) / a->dk) return GDR_ERR_UNSUPPORTED;
+  if ((reinterpret_cast<uintptr_t>(g->decay_a) & 3u) != 0) return GDR_ERR_ALIGN;
+  return GDR_OK;
+}
+}  // namespace
+
+extern "C" {
+
+size_t gdr_chunk_fwd_workspace(const gdr_fwd_args* a) {
+  (void)a;
+  return 0;
+}
+
+gdr_status gdr_chunk_fwd(const gdr_fwd_args* a, void* hip_stream) {
+  const gdr_status st = check_fwd(a);
+  if (st != GDR_OK) return st;
+  const hipError_t e = gdr::launch_fwd(fwd_params(a), (hipStream_t)hip_stream);
+  return e == hipSuccess ? GDR_OK : GDR_ERR_HIP;
+}
+
+gdr_status gdr_chunk_fwd_gated(const gdr_fwd_args* a, const gdr_gate_args* g, void* hip_stream) {
+  const gdr_status st = check_gated(a, g);
+  if (st != GDR_OK) return st;
+  gdr::FwdParams p = fwd_params(a);
+  p.gmode = g->qk_l2norm ? 2 : 1;
+  p.gate_x = g->decay_x;
+  p.gate_a = g->decay_a;
+  if (!gdr::fwd_pipe_supported(p)) return GDR_ERR_UNSUPPORTED;
   const hipError_t e = gdr::launch_fwd(p, (hipStream_t)hip_stream);
   return e == hipSuccess ? GDR_OK : GDR_ERR_HIP;
 }

@@ -46,6 +46,17 @@ __device__ inline f32x2 conj(f32x2 a) { return f32x2{a.x, -a.y}; }
 __device__ inline f32x2 bf2_to_f2(uint32_t u) {
   return f32x2{__uint_as_float(u << 16), __uint_as_float(u & 0xffff0000u)};
 }
+// Decay from its pre-activation (gated forward): exp(-a softplus(x)), as
+// 2^(-a (max(x, 0) log2 e + log2(1 + 2^(-|x| log2 e)))): no overflow for large
+// |x|; for x below about -17 softplus(x) < 2^-24 is dropped (an error below one
+// fp32 ulp of the decay).
+__device__ inline float gate_act(float x, float a) {
+  constexpr float kLog2e = 1.44269504088896341f;
+  const float t = __builtin_amdgcn_exp2f(-__builtin_fabsf(x) * kLog2e);
+  const float sp2 = __builtin_fmaxf(x, 0.f) * kLog2e + __builtin_amdgcn_logf(1.f + t);
+  return __builtin_amdgcn_exp2f(-a * sp2);
+}
+
 __device__ inline uint32_t f2_to_bf2(f32x2 x) {
   bf16x2 v;
   v[0] = (bf)x.x;
@@ -182,10 +193,11 @@ __device__ inline rsrc_t make_rsrc(const void* base, size_t bytes) {
 
 struct Rsrc {
   rsrc_t k, q, a, th, v, beta, w;
-  int sk, sa, sv, sb;   // per-token byte strides
+  int sk, sa, sth, sv, sb;   // per-token byte strides
 };
 
-template <int DK, int TV, int DECAY>
+// GMODE > 0 (gated forward): the decay comes as a bf16 pre-activation.
+template <int DK, int TV, int DECAY, int GMODE = 0>
 __device__ inline Rsrc make_rsrcs(const FwdParams& p, int b, int h, int v0) {
   const int Tn = p.T, H = p.H, DV = p.DV;
   const size_t bh = (size_t)b * Tn * H + h;
@@ -194,13 +206,17 @@ __device__ inline Rsrc make_rsrcs(const FwdParams& p, int b, int h, int v0) {
   r.sk = H * DK * 2;
   r.k = make_rsrc((const bf*)p.k + bh * DK, rows * DK * 2);
   r.q = make_rsrc((const bf*)p.q + bh * DK, rows * DK * 2);
+  constexpr int GS = GMODE > 0 ? 2 : 4;   // bytes per decay value
+  const char* abase = GMODE > 0 ? (const char*)p.gate_x : (const char*)p.alpha;
   if constexpr (DECAY == 0) {
-    r.sa = H * DK * 4;
-    r.a = make_rsrc(p.alpha + bh * DK, rows * DK * 4);
+    r.sa = H * DK * GS;
+    r.a = make_rsrc(abase + bh * DK * GS, rows * DK * GS);
     r.th = r.a;
+    r.sth = r.sa;
   } else {
-    r.sa = H * (DK / 2) * 4;
-    r.a = make_rsrc(p.alpha + bh * (DK / 2), rows * (DK / 2) * 4);
+    r.sa = H * (DK / 2) * GS;
+    r.a = make_rsrc(abase + bh * (DK / 2) * GS, rows * (DK / 2) * GS);
+    r.sth = H * (DK / 2) * 4;
     r.th = make_rsrc(p.theta + bh * (DK / 2), rows * (DK / 2) * 4);
   }
   r.sv = H * DV * 2;
@@ -225,7 +241,7 @@ __device__ inline bf16x8 load_kq(const bf* base, int row0, int kk) {
 // in soffset.  Both count in the range check of a raw buffer (no stride), so
 // tokens at or past T still read as zero.
 // PART 0: value tile; 1: key-axis transitions; 2: keys; 3: queries.
-template <int DK, int TV, int DECAY, bool CONTENT, int PART>
+template <int DK, int TV, int DECAY, bool CONTENT, int PART, int GMODE = 0>
 __device__ inline void load_part(RawT<DK, TV, CONTENT>& R, const Rsrc& rs, int c0, int pp, int seg,
                                  int ptid) {
   using C = Cfg<DK, TV>;
@@ -245,6 +261,20 @@ __device__ inline void load_part(RawT<DK, TV, CONTENT>& R, const Rsrc& rs, int c
       const int r = idx / C::VPR, cc = idx % C::VPR;
       const auto x = __builtin_amdgcn_raw_buffer_load_b128(rs.v, r * rs.sv + cc * 16, c0 * rs.sv, 0);
       R.v[u] = uint4{x[0], x[1], x[2], x[3]};
+    }
+  } else if constexpr (PART == 1 && GMODE > 0) {
+    // bf16 pre-activations, kept as raw bits: DIAG the channel pair's two
+    // values (.x), ROT2 the block's value (.x, low half) and its angle (.y)
+    const int al = seg * C::TPS * rs.sa + (DECAY == 0 ? 4 : 2) * pp;
+    const int tl = seg * C::TPS * rs.sth + 4 * pp;
+#pragma unroll
+    for (int r = 0; r < C::TPS; ++r) {
+      if constexpr (DECAY == 0) {
+        R.a[r] = f32x2{__uint_as_float(__builtin_amdgcn_raw_buffer_load_b32(rs.a, al, (c0 + r) * rs.sa, 0)), 0.f};
+      } else {
+        R.a[r] = f32x2{__uint_as_float((uint32_t)__builtin_amdgcn_raw_buffer_load_b16(rs.a, al, (c0 + r) * rs.sa, 0)),
+                       __uint_as_float(__builtin_amdgcn_raw_buffer_load_b32(rs.th, tl, (c0 + r) * rs.sth, 0))};
+      }
     }
   } else if constexpr (PART == 1) {
     const int al = seg * C::TPS * rs.sa + (DECAY == 0 ? 8 : 4) * pp;
@@ -270,13 +300,28 @@ __device__ inline void load_part(RawT<DK, TV, CONTENT>& R, const Rsrc& rs, int c
   }
 }
 
-template <int DK, int TV, int DECAY, bool CONTENT>
+template <int DK, int TV, int DECAY, bool CONTENT, int GMODE = 0>
 __device__ inline void load_raw(RawT<DK, TV, CONTENT>& R, const Rsrc& rs, int c0, int pp, int seg,
                                 int ptid) {
-  load_part<DK, TV, DECAY, CONTENT, 0>(R, rs, c0, pp, seg, ptid);
-  load_part<DK, TV, DECAY, CONTENT, 1>(R, rs, c0, pp, seg, ptid);
-  load_part<DK, TV, DECAY, CONTENT, 2>(R, rs, c0, pp, seg, ptid);
-  load_part<DK, TV, DECAY, CONTENT, 3>(R, rs, c0, pp, seg, ptid);
+  load_part<DK, TV, DECAY, CONTENT, 0, GMODE>(R, rs, c0, pp, seg, ptid);
+  load_part<DK, TV, DECAY, CONTENT, 1, GMODE>(R, rs, c0, pp, seg, ptid);
+  load_part<DK, TV, DECAY, CONTENT, 2, GMODE>(R, rs, c0, pp, seg, ptid);
+  load_part<DK, TV, DECAY, CONTENT, 3, GMODE>(R, rs, c0, pp, seg, ptid);
+}
+
+// Value of the partner lane across bit d (d in {8, 4, 2, 1}) of a 16-lane row,
+// by a DPP move inside the row: row mirror (lane i <-> 15 - i), half-row
+// mirror (i <-> 7 - i within each 8), then quad swaps (i ^ 2, i ^ 1).  Each
+// pairs the lanes of the two halves of the current 2d-lane group, which is all
+// a reduce-scatter needs, with no LDS instruction and no wait on one.
+__device__ inline float row_partner(float v, int d) {
+  const int x = __float_as_int(v);
+  int r;
+  if (d == 8) r = __builtin_amdgcn_mov_dpp(x, 0x140, 0xf, 0xf, false);
+  else if (d == 4) r = __builtin_amdgcn_mov_dpp(x, 0x141, 0xf, 0xf, false);
+  else if (d == 2) r = __builtin_amdgcn_mov_dpp(x, 0x4e, 0xf, 0xf, false);
+  else r = __builtin_amdgcn_mov_dpp(x, 0xb1, 0xf, 0xf, false);
+  return __int_as_float(r);
 }
 
 // Value held by lane l ^ (PPW * d) (d = 1, 2, 4; PPW * d in {8, 16, 32}):
@@ -299,30 +344,45 @@ __device__ inline float xor_lanes(float v, int d, int l) {
 // With NEXT, the raw loads of the chunk at token cn go into Rn, spread over the
 // step in four groups so that the prep waves do not all stall on a full
 // vector-memory queue at the start of every step.
-template <int DK, int TV, int DECAY, bool CONTENT, bool NEXT, bool ROBUST>
+// Gated forward (GMODE > 0): the transitions come as bf16 pre-activations with
+// the head's scale ga.  With q/k normalisation (GMODE == 2) k and q stay raw
+// here: the norms are folded into beta, beta*w and an output scale.
+template <int DK, int TV, int DECAY, bool CONTENT, bool NEXT, bool ROBUST, int GMODE = 0>
 __device__ __forceinline__ void prep_chunk(Shared<DK, TV>& sh, const RawT<DK, TV, CONTENT>& R,
                                            RawT<DK, TV, CONTENT>& Rn, const Rsrc& rs, int cn,
                                            int it, int vs, int Tn, int pw, int l, int pl,
                                            int seg, int pp, int ptid, int& any_out,
-                                           const float (&uh)[8], int vc0) {
+                                           const float (&uh)[8], int vc0, float ga = 0.f) {
   using C = Cfg<DK, TV>;
   constexpr int PPW = C::PPW, NSEG = C::NSEG, TPS = C::TPS, RSK = C::RSK, RSV = C::RSV,
                 VPR = C::VPR;
   SlotA<DK, TV>& A = sh.a[vs % 3];
   bf* Kh = sh.Kh[vs & 1];
   const int c0 = it * L;
-  if constexpr (NEXT) load_part<DK, TV, DECAY, CONTENT, 0>(Rn, rs, cn, pp, seg, ptid);
+  if constexpr (NEXT) load_part<DK, TV, DECAY, CONTENT, 0, GMODE>(Rn, rs, cn, pp, seg, ptid);
   // transitions of this lane's token segment (identity past the end)
+  f32x2 ain[TPS];
+#pragma unroll
+  for (int r = 0; r < TPS; ++r) {
+    if constexpr (GMODE == 0) {
+      ain[r] = R.a[r];
+    } else if constexpr (DECAY == 0) {
+      const f32x2 x = bf2_to_f2(__float_as_uint(R.a[r].x));
+      ain[r] = f32x2{gate_act(x.x, ga), gate_act(x.y, ga)};
+    } else {
+      ain[r] = f32x2{gate_act(__uint_as_float(__float_as_uint(R.a[r].x) << 16), ga), R.a[r].y};
+    }
+  }
   f32x2 d[TPS];
   if (c0 + L <= Tn) {
 #pragma unroll
-    for (int r = 0; r < TPS; ++r) d[r] = R.a[r];
+    for (int r = 0; r < TPS; ++r) d[r] = ain[r];
   } else {
 #pragma unroll
     for (int r = 0; r < TPS; ++r) {
       const bool ok = c0 + seg * TPS + r < Tn;
-      d[r].x = ok ? R.a[r].x : 1.f;
-      d[r].y = ok ? R.a[r].y : (DECAY == 0 ? 1.f : 0.f);
+      d[r].x = ok ? ain[r].x : 1.f;
+      d[r].y = ok ? ain[r].y : (DECAY == 0 ? 1.f : 0.f);
     }
   }
   if constexpr (DECAY != 0) {
@@ -339,7 +399,7 @@ __device__ __forceinline__ void prep_chunk(Shared<DK, TV>& sh, const RawT<DK, TV
   const f32x2 one = {1.f, DECAY == 0 ? 1.f : 0.f};
   if constexpr (NEXT) {
     __builtin_amdgcn_sched_barrier(0);
-    load_part<DK, TV, DECAY, CONTENT, 1>(Rn, rs, cn, pp, seg, ptid);
+    load_part<DK, TV, DECAY, CONTENT, 1, GMODE>(Rn, rs, cn, pp, seg, ptid);
   }
   f32x2 run = d[0];
 #pragma unroll
@@ -398,7 +458,7 @@ __device__ __forceinline__ void prep_chunk(Shared<DK, TV>& sh, const RawT<DK, TV
   }
   if constexpr (NEXT) {
     __builtin_amdgcn_sched_barrier(0);
-    load_part<DK, TV, DECAY, CONTENT, 2>(Rn, rs, cn, pp, seg, ptid);
+    load_part<DK, TV, DECAY, CONTENT, 2, GMODE>(Rn, rs, cn, pp, seg, ptid);
   }
   f32x2 ig;   // Gamma_L^{-T} per channel (pair)
   if constexpr (DECAY == 0) {
@@ -434,7 +494,7 @@ __device__ __forceinline__ void prep_chunk(Shared<DK, TV>& sh, const RawT<DK, TV
   for (int r4 = 0; r4 < TPS; r4 += 4) {
     if (NEXT && r4 == (TPS > 4 ? 4 : 0)) {
       __builtin_amdgcn_sched_barrier(0);
-      load_part<DK, TV, DECAY, CONTENT, 3>(Rn, rs, cn, pp, seg, ptid);
+      load_part<DK, TV, DECAY, CONTENT, 3, GMODE>(Rn, rs, cn, pp, seg, ptid);
     }
 #pragma unroll
     for (int u = 0; u < 4; ++u) {
@@ -489,9 +549,13 @@ __device__ __forceinline__ void prep_chunk(Shared<DK, TV>& sh, const RawT<DK, TV
 // waves (lane id ix in 0..255: token ix / 8, channels (ix % 8) * DK / 8 ...):
 // the transition as fp32 per channel (ROT2: gamma cos theta, gamma sin theta
 // per pair), then the raw keys and queries.  Tokens past T read as zero.
-template <int DK, int TV, int DECAY>
-__device__ inline void stage_raw(SlotA<DK, TV>& A, const Rsrc& rs, int c0, int ix) {
+// Gated forward: the transition from its pre-activation (scale ga), and with
+// GMODE == 2 queries divided by their norms (sums of squares reduced over the
+// 8 lanes that hold a token).
+template <int DK, int TV, int DECAY, int GMODE = 0>
+__device__ inline void stage_raw(SlotA<DK, TV>& A, const Rsrc& rs, int c0, int ix, float ga = 0.f) {
   constexpr int CPL = DK / 8;   // channels per lane
+  constexpr int NP8 = CPL / 8;  // 16-byte pieces of keys (or queries) per lane
   static_assert(NWS * 64 == 8 * L, "one solve lane per (token, channel block)");
   char* raw = (char*)A.Kp;
   float* ra = (float*)raw;
@@ -499,32 +563,91 @@ __device__ inline void stage_raw(SlotA<DK, TV>& A, const Rsrc& rs, int c0, int i
   bf* rq = rk + L * DK;
   const int t = ix >> 3, c = (ix & 7) * CPL;
   const int tok = c0 + t;
+  uint4 kk[NP8], qq[NP8];
 #pragma unroll
-  for (int u = 0; u < CPL; u += 8) {
-    const auto xk = __builtin_amdgcn_raw_buffer_load_b128(rs.k, (c + u) * 2, tok * rs.sk, 0);
-    const auto xq = __builtin_amdgcn_raw_buffer_load_b128(rs.q, (c + u) * 2, tok * rs.sk, 0);
-    *(uint4*)(rk + t * DK + c + u) = uint4{xk[0], xk[1], xk[2], xk[3]};
-    *(uint4*)(rq + t * DK + c + u) = uint4{xq[0], xq[1], xq[2], xq[3]};
+  for (int u = 0; u < NP8; ++u) {
+    const auto xk = __builtin_amdgcn_raw_buffer_load_b128(rs.k, (c + 8 * u) * 2, tok * rs.sk, 0);
+    const auto xq = __builtin_amdgcn_raw_buffer_load_b128(rs.q, (c + 8 * u) * 2, tok * rs.sk, 0);
+    kk[u] = uint4{xk[0], xk[1], xk[2], xk[3]};
+    qq[u] = uint4{xq[0], xq[1], xq[2], xq[3]};
   }
-  if constexpr (DECAY == 0) {
+  if constexpr (GMODE == 2) {
+    // queries divided by their norms; keys stay raw (their norms are folded
+    // into the block's beta and beta*w, which the token path uses too)
+    float sq = 0.f;
+#pragma unroll
+    for (int u = 0; u < NP8; ++u) {
+      const uint32_t wq[4] = {qq[u].x, qq[u].y, qq[u].z, qq[u].w};
+#pragma unroll
+      for (int e = 0; e < 4; ++e) {
+        const bf16x2 q2 = __builtin_bit_cast(bf16x2, wq[e]);
+        sq = __builtin_amdgcn_fdot2_f32_bf16(q2, q2, sq, false);
+      }
+    }
+#pragma unroll
+    for (int d = 4; d >= 1; d >>= 1) sq += row_partner(sq, d);
+    const float fq = __builtin_amdgcn_rsqf(sq + 1e-6f);
+#pragma unroll
+    for (int u = 0; u < NP8; ++u) {
+      uint32_t wq[4] = {qq[u].x, qq[u].y, qq[u].z, qq[u].w};
+#pragma unroll
+      for (int e = 0; e < 4; ++e) {
+        const f32x2 b2 = bf2_to_f2(wq[e]);
+        wq[e] = f2_to_bf2(f32x2{b2.x * fq, b2.y * fq});
+      }
+      qq[u] = uint4{wq[0], wq[1], wq[2], wq[3]};
+    }
+  }
+#pragma unroll
+  for (int u = 0; u < NP8; ++u) {
+    *(uint4*)(rk + t * DK + c + 8 * u) = kk[u];
+    *(uint4*)(rq + t * DK + c + 8 * u) = qq[u];
+  }
+  if constexpr (DECAY == 0 && GMODE == 0) {
 #pragma unroll
     for (int u = 0; u < CPL; u += 4) {
       const auto x = __builtin_amdgcn_raw_buffer_load_b128(rs.a, (c + u) * 4, tok * rs.sa, 0);
       *(uint4*)(ra + t * DK + c + u) = uint4{x[0], x[1], x[2], x[3]};
     }
+  } else if constexpr (DECAY == 0) {
+#pragma unroll
+    for (int u = 0; u < CPL; u += 8) {   // 8 bf16 pre-activations -> 8 decays
+      const auto x = __builtin_amdgcn_raw_buffer_load_b128(rs.a, (c + u) * 2, tok * rs.sa, 0);
+      f32x4 lo, hi;
+#pragma unroll
+      for (int e = 0; e < 4; ++e) {
+        const f32x2 v2 = bf2_to_f2(x[e]);
+        (e < 2 ? lo : hi)[2 * (e & 1)] = gate_act(v2.x, ga);
+        (e < 2 ? lo : hi)[2 * (e & 1) + 1] = gate_act(v2.y, ga);
+      }
+      *(f32x4*)(ra + t * DK + c + u) = lo;
+      *(f32x4*)(ra + t * DK + c + u + 4) = hi;
+    }
   } else {
 #pragma unroll
     for (int u = 0; u < CPL / 2; u += 4) {   // pairs c/2 + u .. c/2 + u + 3
-      const auto xg = __builtin_amdgcn_raw_buffer_load_b128(rs.a, (c / 2 + u) * 4, tok * rs.sa, 0);
-      const auto xt = __builtin_amdgcn_raw_buffer_load_b128(rs.th, (c / 2 + u) * 4, tok * rs.sa, 0);
+      float gm4[4];
+      if constexpr (GMODE == 0) {
+        const auto xg = __builtin_amdgcn_raw_buffer_load_b128(rs.a, (c / 2 + u) * 4, tok * rs.sa, 0);
+#pragma unroll
+        for (int e = 0; e < 4; ++e) gm4[e] = __uint_as_float(xg[e]);
+      } else {
+        const auto xg = __builtin_amdgcn_raw_buffer_load_b64(rs.a, (c / 2 + u) * 2, tok * rs.sa, 0);
+#pragma unroll
+        for (int e = 0; e < 2; ++e) {
+          const f32x2 v2 = bf2_to_f2(xg[e]);
+          gm4[2 * e] = gate_act(v2.x, ga);
+          gm4[2 * e + 1] = gate_act(v2.y, ga);
+        }
+      }
+      const auto xt = __builtin_amdgcn_raw_buffer_load_b128(rs.th, (c / 2 + u) * 4, tok * rs.sth, 0);
       f32x4 lo, hi;
 #pragma unroll
       for (int e = 0; e < 4; ++e) {
         float sn, cs;
         __sincosf(__uint_as_float(xt[e]), &sn, &cs);
-        const float gm = __uint_as_float(xg[e]);
-        (e < 2 ? lo : hi)[2 * (e & 1)] = gm * cs;
-        (e < 2 ? lo : hi)[2 * (e & 1) + 1] = gm * sn;
+        (e < 2 ? lo : hi)[2 * (e & 1)] = gm4[e] * cs;
+        (e < 2 ? lo : hi)[2 * (e & 1) + 1] = gm4[e] * sn;
       }
       *(f32x4*)(ra + t * DK + c + 2 * u) = lo;
       *(f32x4*)(ra + t * DK + c + 2 * u + 4) = hi;
@@ -532,9 +655,10 @@ __device__ inline void stage_raw(SlotA<DK, TV>& A, const Rsrc& rs, int c0, int i
   }
 }
 
-template <int DK, int TV, int DECAY, bool CONTENT>
+template <int DK, int TV, int DECAY, bool CONTENT, int GMODE = 0>
 __global__ __launch_bounds__((NWP + NWS + TV / 16 + (CONTENT ? 1 : 0)) * 64) void gdr_fwd_pipe_kernel(
     FwdParams p) {
+  static_assert(GMODE == 0 || !CONTENT, "the gated forward has the plain erase");
   using C = Cfg<DK, TV>;
   using O = Op<bf>;
   using frag = O::frag;
@@ -580,6 +704,15 @@ __global__ __launch_bounds__((NWP + NWS + TV / 16 + (CONTENT ? 1 : 0)) * 64) voi
   constexpr int NWC = C::NWC;
   __shared__ __attribute__((aligned(16))) float sU[CONTENT ? DK : 1], sMean[CONTENT ? DK : 1];
   __shared__ float sS[1];
+  // Gated forward with q/k normalisation.  Dividing k_t by its norm |k_t|
+  // (sqrt of the sum of squares + 1e-6) turns the erase beta_t k^ k^T into
+  // (beta_t / |k_t|^2) k k^T and the write beta_t w_t v k^T into
+  // (beta_t w_t / |k_t|) v k^T, so a block runs on raw k with those two
+  // strengths in place of beta and beta*w, exactly; and o_t = S_t q_t / |q_t|.
+  // The solve waves form both norms from raw k and q, and sNq holds 1 / |q_t|
+  // of a block (one per prep slot) for the consumer.
+  constexpr bool GNORM = GMODE == 2;
+  __shared__ __attribute__((aligned(16))) float sNq[GNORM ? 3 : 1][GNORM ? L : 1];
   // content-aware: beta and beta*w of a block, computed by the solve for the
   // consumer (one per prep slot)
   __shared__ __attribute__((aligned(16))) float sBc[CONTENT ? 3 : 1][CONTENT ? 2 : 1][L];
@@ -637,7 +770,8 @@ __global__ __launch_bounds__((NWP + NWS + TV / 16 + (CONTENT ? 1 : 0)) * 64) voi
     if constexpr (CONTENT) __builtin_amdgcn_s_setprio(1);
     const int pl = l % PPW, seg = l / PPW, pp = pw * PPW + pl;
     const int ptid = tid;                       // 0 .. NWP*64-1
-    const Rsrc rs = make_rsrcs<DK, TV, DECAY>(p, b, h, CONTENT ? 0 : v0);
+    const Rsrc rs = make_rsrcs<DK, TV, DECAY, GMODE>(p, b, h, CONTENT ? 0 : v0);
+    const float ga = GMODE > 0 ? p.gate_a[h] : 0.f;   // gated forward: the head's decay scale
     const int clast = (nchunks - 1) * L;
     // content-aware: u_h over the 8 value channels of this lane's row piece
     float uh[8] = {0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f};
@@ -651,6 +785,7 @@ __global__ __launch_bounds__((NWP + NWS + TV / 16 + (CONTENT ? 1 : 0)) * 64) voi
     };
     int it = 0;
     if constexpr (C::NT > 12 * 64) {
+      static_assert(GMODE == 0, "the gated forward runs the three-register-set prep");
       // 16 waves leave 128 VGPRs per wave: one chunk ahead, two register sets
       RawT<DK, TV, CONTENT> R0, R1;
       load_raw<DK, TV, DECAY, CONTENT>(R0, rs, 0, pp, seg, ptid);
@@ -672,33 +807,33 @@ __global__ __launch_bounds__((NWP + NWS + TV / 16 + (CONTENT ? 1 : 0)) * 64) voi
       }
     } else {
     RawT<DK, TV, CONTENT> R0, R1, R2;
-    load_raw<DK, TV, DECAY, CONTENT>(R0, rs, 0, pp, seg, ptid);
-    load_raw<DK, TV, DECAY, CONTENT>(R1, rs, min(L, clast), pp, seg, ptid);
+    load_raw<DK, TV, DECAY, CONTENT, GMODE>(R0, rs, 0, pp, seg, ptid);
+    load_raw<DK, TV, DECAY, CONTENT, GMODE>(R1, rs, min(L, clast), pp, seg, ptid);
     for (; it + 2 < nchunks; it += 3) {
-      prep_chunk<DK, TV, DECAY, CONTENT, true, ROBUST>(sh, R0, R2, rs, (it + 2) * L, it, vstep(it), Tn, pw, l, pl,
-                                      seg, pp, ptid, any_bad, uh, v0);
+      prep_chunk<DK, TV, DECAY, CONTENT, true, ROBUST, GMODE>(sh, R0, R2, rs, (it + 2) * L, it, vstep(it), Tn, pw, l, pl,
+                                      seg, pp, ptid, any_bad, uh, v0, ga);
       lds_barrier();
       idle_after(it);
-      prep_chunk<DK, TV, DECAY, CONTENT, true, ROBUST>(sh, R1, R0, rs, min((it + 3) * L, clast), it + 1,
-                                      vstep(it + 1), Tn, pw, l, pl, seg, pp, ptid, any_bad, uh, v0);
+      prep_chunk<DK, TV, DECAY, CONTENT, true, ROBUST, GMODE>(sh, R1, R0, rs, min((it + 3) * L, clast), it + 1,
+                                      vstep(it + 1), Tn, pw, l, pl, seg, pp, ptid, any_bad, uh, v0, ga);
       lds_barrier();
       idle_after(it + 1);
-      prep_chunk<DK, TV, DECAY, CONTENT, true, ROBUST>(sh, R2, R1, rs, min((it + 4) * L, clast), it + 2,
-                                      vstep(it + 2), Tn, pw, l, pl, seg, pp, ptid, any_bad, uh, v0);
+      prep_chunk<DK, TV, DECAY, CONTENT, true, ROBUST, GMODE>(sh, R2, R1, rs, min((it + 4) * L, clast), it + 2,
+                                      vstep(it + 2), Tn, pw, l, pl, seg, pp, ptid, any_bad, uh, v0, ga);
       lds_barrier();
       idle_after(it + 2);
     }
     // one or two chunks left: they are in R0 and R1
     if (it < nchunks) {
-      prep_chunk<DK, TV, DECAY, CONTENT, false, ROBUST>(sh, R0, R2, rs, 0, it, vstep(it), Tn, pw, l, pl, seg, pp,
-                                       ptid, any_bad, uh, v0);
+      prep_chunk<DK, TV, DECAY, CONTENT, false, ROBUST, GMODE>(sh, R0, R2, rs, 0, it, vstep(it), Tn, pw, l, pl, seg, pp,
+                                       ptid, any_bad, uh, v0, ga);
       lds_barrier();
       idle_after(it);
       ++it;
     }
     if (it < nchunks) {
-      prep_chunk<DK, TV, DECAY, CONTENT, false, ROBUST>(sh, R1, R2, rs, 0, it, vstep(it), Tn, pw, l, pl, seg, pp,
-                                       ptid, any_bad, uh, v0);
+      prep_chunk<DK, TV, DECAY, CONTENT, false, ROBUST, GMODE>(sh, R1, R2, rs, 0, it, vstep(it), Tn, pw, l, pl, seg, pp,
+                                       ptid, any_bad, uh, v0, ga);
       lds_barrier();
       ++it;
     }
@@ -723,15 +858,70 @@ __global__ __launch_bounds__((NWP + NWS + TV / 16 + (CONTENT ? 1 : 0)) * 64) voi
     const rsrc_t rw = make_rsrc(p.w + ((size_t)b * Tn * H + h), ((size_t)(Tn - 1) * H + 1) * 4);
     const int tb = (l < L ? l : L - 1) * H * 4;
     float nbt = 0.f, nwt = 0.f;
-    if (sw == NWS - 1) {
+    if (!GNORM && sw == NWS - 1) {
       nbt = __uint_as_float(__builtin_amdgcn_raw_buffer_load_b32(rb, tb, 0, 0));
       nwt = __uint_as_float(__builtin_amdgcn_raw_buffer_load_b32(rw, tb, 0, 0));
     }
     float s_win = 0.f;   // content-aware: s_c = u_h . m_c of the current window
-    const Rsrc rss = make_rsrcs<DK, TV, DECAY>(p, b, h, v0);
-    for (int it = 0; it < nsteps; ++it) {
+    const Rsrc rss = make_rsrcs<DK, TV, DECAY, GMODE>(p, b, h, v0);
+    const float ga = GMODE > 0 ? p.gate_a[h] : 0.f;
+    // Normalised gated: lane ix = 64 sw + l holds token ix / 8 of a block and
+    // its key and query channels (ix % 8) * DK / 8 ..., loaded two steps before
+    // the block's prep step (two register sets, the loop unrolled by two); in
+    // that step the 8 lanes of a token reduce the sums of squares, and the
+    // first of them stages the block's strengths beta / |k|^2 and
+    // beta w / |k| and the output scale 1 / |q|.
+    constexpr int NPC = GNORM ? DK / 64 : 1;   // 16-byte pieces of k (and of q) per lane
+    struct GSet {
+      uint4 k[NPC], q[NPC];
+      float b, w;
+    };
+    const int ntk = (sw * 64 + l) >> 3;
+    const int nvo = ntk * rss.sk + ((sw * 64 + l) & 7) * (DK / 8) * 2;
+    auto gnorm_load = [&](GSet& G, int c) {   // block c (tokens past T read as zero)
+      const int so = c * L * rss.sk;
+#pragma unroll
+      for (int u = 0; u < NPC; ++u) {
+        const auto xk = __builtin_amdgcn_raw_buffer_load_b128(rss.k, nvo + 16 * u, so, 0);
+        const auto xq = __builtin_amdgcn_raw_buffer_load_b128(rss.q, nvo + 16 * u, so, 0);
+        G.k[u] = uint4{xk[0], xk[1], xk[2], xk[3]};
+        G.q[u] = uint4{xq[0], xq[1], xq[2], xq[3]};
+      }
+      G.b = __uint_as_float(__builtin_amdgcn_raw_buffer_load_b32(rb, ntk * H * 4, c * L * H * 4, 0));
+      G.w = __uint_as_float(__builtin_amdgcn_raw_buffer_load_b32(rw, ntk * H * 4, c * L * H * 4, 0));
+    };
+    auto gnorm_stage = [&](const GSet& G, int it) {
+      float sk = 0.f, sq = 0.f;
+#pragma unroll
+      for (int u = 0; u < NPC; ++u) {
+        const uint32_t wk[4] = {G.k[u].x, G.k[u].y, G.k[u].z, G.k[u].w};
+        const uint32_t wq[4] = {G.q[u].x, G.q[u].y, G.q[u].z, G.q[u].w};
+#pragma unroll
+        for (int e = 0; e < 4; ++e) {
+          const bf16x2 k2 = __builtin_bit_cast(bf16x2, wk[e]), q2 = __builtin_bit_cast(bf16x2, wq[e]);
+          sk = __builtin_amdgcn_fdot2_f32_bf16(k2, k2, sk, false);
+          sq = __builtin_amdgcn_fdot2_f32_bf16(q2, q2, sq, false);
+        }
+      }
+#pragma unroll
+      for (int d = 4; d >= 1; d >>= 1) {   // all 8 lanes of the token end with the sums
+        sk += row_partner(sk, d);
+        sq += row_partner(sq, d);
+      }
+      if ((l & 7) == 0) {
+        const float k2 = sk + 1e-6f;
+        sh.a[it % 3].beta[ntk] = G.b * __builtin_amdgcn_rcpf(k2);
+        sh.a[it % 3].bw[ntk] = G.b * G.w * __builtin_amdgcn_rsqf(k2);
+        sNq[it % 3][ntk] = __builtin_amdgcn_rsqf(sq + 1e-6f);
+      }
+    };
+    // one solve step; G holds block it (normalised gated) and takes block it + 2
+    auto solve_step = [&](int it, GSet& G) {
       const int jp = CONTENT ? block_at(it) : it;
-      if (sw == NWS - 1 && (CONTENT ? (jp >= 0 && jp < nchunks) : (it < nchunks))) {
+      if constexpr (GNORM) {
+        if (it < nchunks) gnorm_stage(G, it);
+        if (it + 2 < nchunks) gnorm_load(G, it + 2);
+      } else if (sw == NWS - 1 && (CONTENT ? (jp >= 0 && jp < nchunks) : (it < nchunks))) {
         const float bt = nbt, wt = nwt;
         const int cn = min(jp + 1, nchunks - 1) * L * H * 4;   // uniform
         nbt = __uint_as_float(__builtin_amdgcn_raw_buffer_load_b32(rb, tb, cn, 0));
@@ -845,10 +1035,23 @@ __global__ __launch_bounds__((NWP + NWS + TV / 16 + (CONTENT ? 1 : 0)) * 64) voi
         if (ROBUST && __builtin_amdgcn_readfirstlane(rflag.x | rflag.y | rflag.z | rflag.w) != 0) {
           // the other solve waves may still be reading K+ / Q+ of this slot for
           // their Gram tiles; those results are discarded for this chunk
-          stage_raw<DK, TV, DECAY>(sh.a[vj % 3], rss, j * L, sw * 64 + l);
+          stage_raw<DK, TV, DECAY, GMODE>(sh.a[vj % 3], rss, j * L, sw * 64 + l, ga);
         }
       }
       lds_barrier();
+    };
+    GSet g0, g1;
+    if constexpr (GNORM) {
+      gnorm_load(g0, 0);
+      gnorm_load(g1, min(1, nchunks - 1));
+      int it = 0;
+      for (; it + 1 < nsteps; it += 2) {
+        solve_step(it, g0);
+        solve_step(it + 1, g1);
+      }
+      if (it < nsteps) solve_step(it, g0);
+    } else {
+      for (int it = 0; it < nsteps; ++it) solve_step(it, g0);
     }
     };
     solve_role(std::false_type{});
@@ -999,6 +1202,10 @@ __global__ __launch_bounds__((NWP + NWS + TV / 16 + (CONTENT ? 1 : 0)) * 64) voi
                     f32x4 O0 = Qs[0], O1 = Qs[1];
                     O::mma(O0, d0, load_cb_half<bf>(S.M, RSL, 0, 0));
                     O::mma(O1, Df, load_cb<bf>(S.M, RSL, 16, 0));
+                    if constexpr (GNORM) {   // o_t = (S_t q_t) / |q_t|: tokens n and 16 + n
+                      O0 *= sNq[vi % 3][n];
+                      O1 *= sNq[vi % 3][16 + n];
+                    }
                     const bf16x4 ox0 = {(bf)O0[0], (bf)O0[1], (bf)O0[2], (bf)O0[3]};
                     const bf16x4 ox1 = {(bf)O1[0], (bf)O1[1], (bf)O1[2], (bf)O1[3]};
                     if constexpr (CONTENT) {
@@ -1112,27 +1319,38 @@ __global__ __launch_bounds__((NWP + NWS + TV / 16 + (CONTENT ? 1 : 0)) * 64) voi
   }
 }
 
-template <int DK, int TV, int DECAY, bool CONTENT = false>
+template <int DK, int TV, int DECAY, bool CONTENT = false, int GMODE = 0>
 hipError_t launch(const FwdParams& p0, hipStream_t s) {
   FwdParams p = p0;
   p.n_vt = p.DV / TV;
   p.n_units = p.B * p.H;
   const int groups = (p.n_units + 7) / 8;
   // content-aware: one more wave carries the projected row u_h^T S
-  hipLaunchKernelGGL((gdr_fwd_pipe_kernel<DK, TV, DECAY, CONTENT>), dim3(groups * 8 * p.n_vt),
+  hipLaunchKernelGGL((gdr_fwd_pipe_kernel<DK, TV, DECAY, CONTENT, GMODE>), dim3(groups * 8 * p.n_vt),
                      dim3(Cfg<DK, TV>::NT + (CONTENT ? 64 : 0)), 0, s, p);
   return hipGetLastError();
 }
 
 }  // namespace pipe
 
-bool fwd_pipe_supported(const FwdParams& p) {
-  // buffer resources address one (b, h) with 32-bit byte offsets
-  const bool fits = (unsigned long long)p.T * p.H * p.DK * 4ull < (1ull << 31);
-  // content-aware: the window must be a whole number of 32-token blocks
-  const bool content_ok = p.beta_logit == nullptr || (p.window >= 32 && p.window % 32 == 0);
-  return p.io_bf16 && content_ok && (p.DK == 64 || p.DK == 128) && p.DV == p.DK && fits;
+namespace {
+// gated forward (decay from its pre-activation; gmode 2 also normalises q, k)
+template <int DK, int TV>
+hipError_t launch_gated(const FwdParams& p, hipStream_t s) {
+  const bool rot = p.decay != 0;
+  if (p.gmode == 2) return rot ? pipe::launch<DK, TV, 1, false, 2>(p, s) : pipe::launch<DK, TV, 0, false, 2>(p, s);
+  return rot ? pipe::launch<DK, TV, 1, false, 1>(p, s) : pipe::launch<DK, TV, 0, false, 1>(p, s);
 }
+
+hipError_t launch_fwd_gated(const FwdParams& p, hipStream_t s) {
+  if (p.DK == 128) {
+    if ((long)p.B * p.H * 2 >= 192) return launch_gated<128, 64>(p, s);
+    return launch_gated<128, 32>(p, s);
+  }
+  if (p.DK == 64) return launch_gated<64, 32>(p, s);
+  return hipErrorInvalidValue;
+}
+}  // namespace
 
 hipError_t launch_fwd_pipe(const FwdParams& p, hipStream_t s) {
   const bool rot = p.decay != 0;
@@ -1142,6 +1360,7 @@ hipError_t launch_fwd_pipe(const FwdParams& p, hipStream_t s) {
     if (p.DK == 128) return rot ? pipe::launch<128, 16, 1, true>(p, s) : pipe::launch<128, 16, 0, true>(p, s);
     return rot ? pipe::launch<64, 16, 1, true>(p, s) : pipe::launch<64, 16, 0, true>(p, s);
   }
+  if (p.gmode != 0) return launch_fwd_gated(p, s);
   if (p.DK == 128) {
     if ((long)p.B * p.H * 2 >= 192) {
       return rot ? pipe::launch<128, 64, 1>(p, s) : pipe::launch<128, 64, 0>(p, s);

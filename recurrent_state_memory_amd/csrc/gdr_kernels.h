@@ -29,6 +29,11 @@ struct FwdParams {
   float* S_out;
   int n_vt;      // value tiles per (b, h); set by the launcher
   int n_units;   // B * H; set by the launcher
+  // gated forward: 0 off; 1 decay from the bf16 pre-activation gate_x with the
+  // per-head scale gate_a; 2 also L2-normalises each token's q and k
+  int gmode;
+  const void* gate_x;
+  const float* gate_a;
 };
 
 struct StepParams {

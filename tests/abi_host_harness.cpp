@@ -86,6 +86,38 @@ int main() {
   a = good_fwd(); a.T = 1 << 30; a.B = 4; CHECK(gdr_chunk_fwd(&a, nullptr) == GDR_ERR_SHAPE);
   CHECK(gdr::g_nfwd == before);
 
+  // gated forward: marshalled with its gate mode, decay from decay_x
+  gdr_gate_args g;
+  std::memset(&g, 0, sizeof g);
+  g.decay_x = fake(14); g.decay_a = (const float*)fake(15); g.qk_l2norm = 1;
+  a = good_fwd(); a.alpha = nullptr;
+  CHECK(gdr_chunk_fwd_gated(&a, &g, nullptr) == GDR_OK);
+  CHECK(gdr::g_fwd.gmode == 2 && gdr::g_fwd.gate_x == g.decay_x && gdr::g_fwd.gate_a == g.decay_a);
+  CHECK(gdr::g_fwd.alpha == nullptr && gdr::g_fwd.q == a.q);
+  g.qk_l2norm = 0; a.decay = GDR_DECAY_ROT2; a.theta = (const float*)fake(16); a.dk = a.dv = 64;
+  CHECK(gdr_chunk_fwd_gated(&a, &g, nullptr) == GDR_OK && gdr::g_fwd.gmode == 1 && gdr::g_fwd.decay == 1);
+  const int before_g = gdr::g_nfwd;
+  a = good_fwd(); a.alpha = nullptr;
+  CHECK(gdr_chunk_fwd_gated(nullptr, &g, nullptr) == GDR_ERR_NULL);
+  CHECK(gdr_chunk_fwd_gated(&a, nullptr, nullptr) == GDR_ERR_NULL);
+  {
+    gdr_gate_args h = g; h.reserved = 1; CHECK(gdr_chunk_fwd_gated(&a, &h, nullptr) == GDR_ERR_ARG);
+    h = g; h.decay_x = nullptr; CHECK(gdr_chunk_fwd_gated(&a, &h, nullptr) == GDR_ERR_NULL);
+    h = g; h.decay_a = nullptr; CHECK(gdr_chunk_fwd_gated(&a, &h, nullptr) == GDR_ERR_NULL);
+    h = g; h.decay_x = (const char*)fake(14) + 2; CHECK(gdr_chunk_fwd_gated(&a, &h, nullptr) == GDR_ERR_ALIGN);
+    h = g; h.decay_a = (const float*)((const char*)fake(15) + 2);
+    CHECK(gdr_chunk_fwd_gated(&a, &h, nullptr) == GDR_ERR_ALIGN);
+  }
+  gdr_fwd_args b = a; b.alpha = (const float*)fake(4); CHECK(gdr_chunk_fwd_gated(&b, &g, nullptr) == GDR_ERR_ARG);
+  b = a; b.io_dtype = GDR_F32; CHECK(gdr_chunk_fwd_gated(&b, &g, nullptr) == GDR_ERR_UNSUPPORTED);
+  b = a; b.dk = b.dv = 32; CHECK(gdr_chunk_fwd_gated(&b, &g, nullptr) == GDR_ERR_UNSUPPORTED);
+  b = a; b.beta = nullptr; b.beta_logit = (const float*)fake(10); b.ub_down = (const float*)fake(11);
+  b.ub_up = (const float*)fake(12); b.ub_rank = 16;
+  CHECK(gdr_chunk_fwd_gated(&b, &g, nullptr) == GDR_ERR_UNSUPPORTED);
+  b = a; b.T = 1 << 22; b.H = 1; CHECK(gdr_chunk_fwd_gated(&b, &g, nullptr) == GDR_ERR_UNSUPPORTED);
+  b = a; b.beta = nullptr; CHECK(gdr_chunk_fwd_gated(&b, &g, nullptr) == GDR_ERR_NULL);
+  CHECK(gdr::g_nfwd == before_g);
+
   // decode
   gdr_step_args s;
   std::memset(&s, 0, sizeof s);

@@ -25,8 +25,8 @@ def _declared():
 def test_library_loads_and_exports_header_symbols():
     lib = gdr.load_library()
     names = _declared()
-    assert {"gdr_chunk_fwd", "gdr_step_decode", "gdr_chunk_fwd_workspace",
-            "gdr_status_str", "gdr_abi_version"} <= set(names)
+    assert {"gdr_chunk_fwd", "gdr_chunk_fwd_gated", "gdr_step_decode",
+            "gdr_chunk_fwd_workspace", "gdr_status_str", "gdr_abi_version"} <= set(names)
     for nm in names:
         assert hasattr(lib, nm), nm
     out = subprocess.run(["nm", "-D", "--defined-only", gdr.LIB_PATH], capture_output=True,
@@ -91,6 +91,47 @@ def test_fwd_rejects_before_any_hip_call(kw, status):
     assert gdr.call_chunk_fwd(_good_fwd(**kw)) == status
 
 
+def _good_gate(**kw):
+    g = gdr.GateArgs()
+    g.decay_x, g.decay_a, g.qk_l2norm, g.reserved = FAKE, FAKE, 1, 0
+    for f, val in kw.items():
+        setattr(g, f, val)
+    return g
+
+
+GATE_CASES = [
+    (dict(), dict(reserved=1), gdr.GDR_ERR_ARG),
+    (dict(), dict(decay_x=None), gdr.GDR_ERR_NULL),
+    (dict(), dict(decay_a=None), gdr.GDR_ERR_NULL),
+    (dict(), dict(decay_x=FAKE + 2), gdr.GDR_ERR_ALIGN),
+    (dict(), dict(decay_a=FAKE + 2), gdr.GDR_ERR_ALIGN),
+    (dict(alpha=FAKE), dict(), gdr.GDR_ERR_ARG),              # decay comes from decay_x
+    (dict(io_dtype=gdr.GDR_F32), dict(), gdr.GDR_ERR_UNSUPPORTED),
+    (dict(dk=32, dv=32), dict(), gdr.GDR_ERR_UNSUPPORTED),
+    (dict(beta=None, beta_logit=FAKE, ub_down=FAKE, ub_up=FAKE, ub_rank=16), dict(),
+     gdr.GDR_ERR_UNSUPPORTED),
+    (dict(T=1 << 23, H=1), dict(), gdr.GDR_ERR_UNSUPPORTED),  # T * H * dk >= 2^29
+    (dict(beta=None), dict(), gdr.GDR_ERR_NULL),
+    (dict(decay=gdr.GDR_DECAY_ROT2), dict(), gdr.GDR_ERR_NULL),  # rot2 without theta
+    (dict(B=0), dict(), gdr.GDR_ERR_SHAPE),
+]
+
+
+@pytest.mark.parametrize("kw,gkw,status", GATE_CASES)
+def test_gated_fwd_rejects_before_any_hip_call(kw, gkw, status):
+    a = _good_fwd(alpha=None, **{k: v for k, v in kw.items() if k != "alpha"})
+    if "alpha" in kw:
+        a.alpha = kw["alpha"]
+    assert gdr.call_chunk_fwd_gated(a, _good_gate(**gkw)) == status
+
+
+def test_gated_fwd_null_structs():
+    lib = gdr.load_library()
+    g = _good_gate()
+    assert lib.gdr_chunk_fwd_gated(None, ctypes.byref(g), None) == gdr.GDR_ERR_NULL
+    assert lib.gdr_chunk_fwd_gated(ctypes.byref(_good_fwd(alpha=None)), None, None) == gdr.GDR_ERR_NULL
+
+
 def test_fwd_null_args():
     lib = gdr.load_library()
     assert lib.gdr_chunk_fwd(None, None) == gdr.GDR_ERR_NULL
@@ -128,7 +169,8 @@ def test_step_rejects_before_any_hip_call(kw, status):
 
 def test_struct_layout_matches_header(tmp_path):
     """Field offsets of the ctypes mirrors equal the C compiler's offsetof()."""
-    fields = {"gdr_fwd_args": gdr.FwdArgs, "gdr_step_args": gdr.StepArgs}
+    fields = {"gdr_fwd_args": gdr.FwdArgs, "gdr_step_args": gdr.StepArgs,
+              "gdr_gate_args": gdr.GateArgs}
     lines = ["#include <stdio.h>", "#include <stddef.h>", f'#include "{HEADER}"',
              "int main(void) {"]
     for cname, cls in fields.items():
@@ -224,6 +266,42 @@ def test_binding_rejects_bad_content_and_rotation_arguments():
     a["m_carry"] = torch.zeros(2, 3, 8)
     with pytest.raises(ValueError, match="content-aware"):
         gdr.gdr_chunk_fwd(**a)
+
+
+def _cpu_gated_args(B=2, T=5, H=3, d=8, rot=False):
+    import torch
+    bf, f32 = torch.bfloat16, torch.float32
+    g = d // 2 if rot else d
+    a = dict(q=torch.zeros(B, T, H, d, dtype=bf), k=torch.zeros(B, T, H, d, dtype=bf),
+             v=torch.zeros(B, T, H, d, dtype=bf), decay_x=torch.zeros(B, T, H, g, dtype=bf),
+             decay_a=torch.ones(H, dtype=f32), w=torch.zeros(B, T, H, dtype=f32),
+             beta=torch.zeros(B, T, H, dtype=f32))
+    if rot:
+        a["theta"] = torch.zeros(B, T, H, g, dtype=f32)
+    return a
+
+
+def test_gated_binding_checks():
+    """Good shapes pass every check (then the CPU device is refused); each bad
+    argument is named."""
+    import torch
+    for rot in (False, True):
+        with pytest.raises(ValueError, match="GPU"):
+            gdr.gdr_chunk_fwd_gated(**_cpu_gated_args(rot=rot))
+    bad = [("decay_x", torch.zeros(2, 5, 3, 8)),                     # fp32, not bf16
+           ("decay_x", torch.zeros(2, 5, 3, 4, dtype=torch.bfloat16)),
+           ("decay_a", torch.ones(2)), ("decay_a", torch.ones(3, dtype=torch.bfloat16)),
+           ("q", torch.zeros(2, 5, 3, 8)), ("v", torch.zeros(2, 5, 3, 8)),
+           ("beta", torch.zeros(2, 5)), ("w", torch.zeros(2, 5, 3, dtype=torch.bfloat16))]
+    for name, val in bad:
+        a = _cpu_gated_args()
+        a[name] = val
+        with pytest.raises(ValueError, match=name):
+            gdr.gdr_chunk_fwd_gated(**a)
+    a = _cpu_gated_args(rot=True)
+    a["theta"] = torch.zeros(2, 5, 3, 8)
+    with pytest.raises(ValueError, match="theta"):
+        gdr.gdr_chunk_fwd_gated(**a)
 
 
 def test_decode_binding_checks():
