@@ -919,8 +919,7 @@ __global__ __launch_bounds__((NWP + NWS + TV / 16 + (CONTENT ? 1 : 0)) * 64) voi
     auto solve_step = [&](int it, GSet& G) {
       const int jp = CONTENT ? block_at(it) : it;
       if constexpr (GNORM) {
-        if (it < nchunks) gnorm_stage(G, it);
-        if (it + 2 < nchunks) gnorm_load(G, it + 2);
+        // (after this step's solve work below)
       } else if (sw == NWS - 1 && (CONTENT ? (jp >= 0 && jp < nchunks) : (it < nchunks))) {
         const float bt = nbt, wt = nwt;
         const int cn = min(jp + 1, nchunks - 1) * L * H * 4;   // uniform
@@ -1037,6 +1036,10 @@ __global__ __launch_bounds__((NWP + NWS + TV / 16 + (CONTENT ? 1 : 0)) * 64) voi
           // their Gram tiles; those results are discarded for this chunk
           stage_raw<DK, TV, DECAY, GMODE>(sh.a[vj % 3], rss, j * L, sw * 64 + l, ga);
         }
+      }
+      if constexpr (GNORM) {   // off the start of the solve's chain
+        if (it < nchunks) gnorm_stage(G, it);
+        if (it + 2 < nchunks) gnorm_load(G, it + 2);
       }
       lds_barrier();
     };
