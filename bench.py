@@ -38,6 +38,7 @@ HBM_PEAK_GBS = 8000.0          # MI355X HBM3E
 MFMA_BF16_PEAK_TFS = 2500.0    # dense bf16 matrix peak
 MFMA_F32_PEAK_TFS = 157.3
 TRAFFIC_FILE = os.path.join(ROOT, "profiles", "gdr_fwd_pipe_kernel_layer_traffic.txt")
+TRAFFIC_FILE_GATED = os.path.join(ROOT, "profiles", "gdr_fwd_pipe_kernel_layer_gated_traffic.txt")
 KERNEL_SRCS = [os.path.join(ROOT, "recurrent_state_memory_amd", "csrc", f)
                for f in ("gdr_fwd_pipe.hip", "gdr_mfma.h", "gdr_kernels.h", "gdr_token.h")]
 
@@ -90,13 +91,13 @@ def _kernel_hash() -> str:
     return h.hexdigest()[:16]
 
 
-def _traffic():
+def _traffic(path=TRAFFIC_FILE):
     """Per-launch HBM bytes (FETCH_SIZE + WRITE_SIZE, each scaled by what the
     counter reads for a copy of known size) from the committed rocprofv3
     summary, if it was taken on the current kernel source (else None)."""
     try:
         vals = {}
-        for ln in open(TRAFFIC_FILE):
+        for ln in open(path):
             if ":" in ln and not ln.startswith("#"):
                 k, v = ln.split(":", 1)
                 vals[k.strip()] = v.strip()
@@ -327,7 +328,9 @@ def main(argv=None):
     flops = algorithmic_flops(wl, L_eff)
     achieved = nbytes / per / 1e9
     mfma_peak = MFMA_BF16_PEAK_TFS if wl.io == "bf16" else MFMA_F32_PEAK_TFS
-    traffic = _traffic() if a.workload == "layer" and not gated else None
+    traffic = None
+    if a.workload == "layer":
+        traffic = _traffic(TRAFFIC_FILE_GATED if gated else TRAFFIC_FILE)
     out = {
         "metric": METRIC,
         "value": round(value, 1),

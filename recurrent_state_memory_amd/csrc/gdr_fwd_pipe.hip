@@ -866,11 +866,12 @@ __global__ __launch_bounds__((NWP + NWS + TV / 16 + (CONTENT ? 1 : 0)) * 64) voi
     const Rsrc rss = make_rsrcs<DK, TV, DECAY, GMODE>(p, b, h, v0);
     const float ga = GMODE > 0 ? p.gate_a[h] : 0.f;
     // Normalised gated: lane ix = 64 sw + l holds token ix / 8 of a block and
-    // its key and query channels (ix % 8) * DK / 8 ..., loaded two steps before
-    // the block's prep step (two register sets, the loop unrolled by two); in
-    // that step the 8 lanes of a token reduce the sums of squares, and the
-    // first of them stages the block's strengths beta / |k|^2 and
-    // beta w / |k| and the output scale 1 / |q|.
+    // its key and query channels (ix % 8) * DK / 8 ..., loaded at the end of
+    // the step before the block's prep step; at the end of that step the 8
+    // lanes of a token reduce the sums of squares, and the first of them
+    // stages the block's strengths beta / |k|^2 and beta w / |k| and the
+    // output scale 1 / |q|.  (A second register set, two steps ahead, would
+    // need the solve loop unrolled by two, which slows the plain launches.)
     constexpr int NPC = GNORM ? DK / 64 : 1;   // 16-byte pieces of k (and of q) per lane
     struct GSet {
       uint4 k[NPC], q[NPC];
@@ -915,12 +916,12 @@ __global__ __launch_bounds__((NWP + NWS + TV / 16 + (CONTENT ? 1 : 0)) * 64) voi
         sNq[it % 3][ntk] = __builtin_amdgcn_rsqf(sq + 1e-6f);
       }
     };
-    // one solve step; G holds block it (normalised gated) and takes block it + 2
-    auto solve_step = [&](int it, GSet& G) {
+    GSet G;   // normalised gated: block it during step it
+    if constexpr (GNORM) gnorm_load(G, 0);
+    for (int it = 0; it < nsteps; ++it) {
       const int jp = CONTENT ? block_at(it) : it;
-      if constexpr (GNORM) {
-        // (after this step's solve work below)
-      } else if (sw == NWS - 1 && (CONTENT ? (jp >= 0 && jp < nchunks) : (it < nchunks))) {
+      // (normalised gated: the block's strengths are staged at the end of the step)
+      if (!GNORM && sw == NWS - 1 && (CONTENT ? (jp >= 0 && jp < nchunks) : (it < nchunks))) {
         const float bt = nbt, wt = nwt;
         const int cn = min(jp + 1, nchunks - 1) * L * H * 4;   // uniform
         nbt = __uint_as_float(__builtin_amdgcn_raw_buffer_load_b32(rb, tb, cn, 0));
@@ -1039,22 +1040,9 @@ __global__ __launch_bounds__((NWP + NWS + TV / 16 + (CONTENT ? 1 : 0)) * 64) voi
       }
       if constexpr (GNORM) {   // off the start of the solve's chain
         if (it < nchunks) gnorm_stage(G, it);
-        if (it + 2 < nchunks) gnorm_load(G, it + 2);
+        if (it + 1 < nchunks) gnorm_load(G, it + 1);
       }
       lds_barrier();
-    };
-    GSet g0, g1;
-    if constexpr (GNORM) {
-      gnorm_load(g0, 0);
-      gnorm_load(g1, min(1, nchunks - 1));
-      int it = 0;
-      for (; it + 1 < nsteps; it += 2) {
-        solve_step(it, g0);
-        solve_step(it + 1, g1);
-      }
-      if (it < nsteps) solve_step(it, g0);
-    } else {
-      for (int it = 0; it < nsteps; ++it) solve_step(it, g0);
     }
     };
     solve_role(std::false_type{});

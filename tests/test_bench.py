@@ -23,11 +23,25 @@ def test_kernel_hash_ignores_comment_edits(tmp_path, monkeypatch):
 
 
 def test_traffic_summary_parses():
-    """The committed traffic summary has the fields the bench line reads."""
-    vals = {}
-    for ln in open(bench.TRAFFIC_FILE):
-        if ":" in ln and not ln.startswith("#"):
-            k, v = ln.split(":", 1)
-            vals[k.strip()] = v.strip()
-    assert float(vals["hbm_bytes_per_launch"]) > float(vals["algorithmic_bytes_per_launch"]) * 0.9
-    assert len(vals["kernel_source_sha256_16"]) == 16
+    """The committed traffic summaries (plain and gated layer) have the fields the
+    bench line reads."""
+    for path in (bench.TRAFFIC_FILE, bench.TRAFFIC_FILE_GATED):
+        vals = {}
+        for ln in open(path):
+            if ":" in ln and not ln.startswith("#"):
+                k, v = ln.split(":", 1)
+                vals[k.strip()] = v.strip()
+        assert float(vals["hbm_bytes_per_launch"]) > float(vals["algorithmic_bytes_per_launch"]) * 0.9
+        assert len(vals["kernel_source_sha256_16"]) == 16
+
+
+def test_gated_algorithmic_bytes():
+    """The gated forward reads the decay as a bf16 pre-activation: 2 bytes per
+    channel (diag) or 2 + 4 per block with the fp32 angle (rot2)."""
+    from synth.gen import WORKLOADS
+    L = WORKLOADS["layer"]
+    per_th = (bench.algorithmic_bytes(L) - bench.algorithmic_bytes(L, gated=True)) / (L.B * L.T * L.H)
+    assert per_th == 4 * L.dk - 2 * L.dk
+    R = WORKLOADS["rot"]
+    per_th = (bench.algorithmic_bytes(R) - bench.algorithmic_bytes(R, gated=True)) / (R.B * R.T * R.H)
+    assert per_th == 4 * R.dk - 6 * (R.dk // 2)
