@@ -164,6 +164,55 @@ typedef struct gdr_gate_args {
 gdr_status gdr_chunk_fwd_gated(const gdr_fwd_args *a, const gdr_gate_args *g, void *hip_stream);
 
 /* ------------------------------------------------------------------------ */
+/* Backward of the forward (plain erase).                                     */
+/* ------------------------------------------------------------------------ */
+/* The gradients that training needs (the CARVE technical summary reports
+ * training throughput; its section 3 item 5 concerns gradient norms): for a
+ * scalar loss L with dL/do = grad_o and dL/dS_T = grad_S (NULL: zero), the
+ * call writes dL/dq, dL/dk, dL/dv, dL/d(decay) -- alpha (DIAG), or gamma and
+ * theta (ROT2) -- dL/dbeta, dL/dw and dL/dS0.  The pages give no backward
+ * algorithm; this one is the adjoint of the chunk (WY) form of the forward.
+ *
+ * It recomputes the forward (storing the state at the start of every 32-token
+ * block in the workspace), then runs the blocks in reverse.  Products use
+ * fp32 operands; the block-start states come from the forward's bf16 matrix
+ * products, so the gradients carry the forward's rounding.
+ *
+ * Supported: BF16 q, k, v and grad_o; dk == dv in {64, 128}; T * H * dk <
+ * 2^29; otherwise GDR_ERR_UNSUPPORTED.  Range: every 32-token block must keep
+ * each key channel's (or pair's) decay product >= e^-40 (the forward has a
+ * token path for such blocks, the backward does not); a head with a block
+ * outside that range gets non-finite gradients.
+ *
+ * Layouts (fp32 gradients, same shapes as the inputs):
+ *   grad_q, grad_k [B,T,H,dk]; grad_v [B,T,H,dv]; grad_alpha as alpha
+ *   ([B,T,H,dk] DIAG, [B,T,H,dk/2] ROT2); grad_theta as theta (ROT2, else
+ *   NULL); grad_beta, grad_w [B,T,H]; grad_S0 [B,H,dv,dk] (may be NULL).
+ * workspace: device memory of at least gdr_chunk_bwd_workspace(a) bytes,
+ * 256-byte aligned; its contents on entry do not matter. */
+typedef struct gdr_bwd_args {
+  int32_t B, T, H, dk, dv;
+  gdr_decay decay;
+  const void *q, *k, *v;        /* bf16, as gdr_fwd_args                      */
+  const float *alpha, *theta;   /* as gdr_fwd_args                            */
+  const float *beta, *w;        /* [B,T,H]                                    */
+  const float *S0;              /* [B,H,dv,dk] or NULL (zeros)                */
+  const void *grad_o;           /* [B,T,H,dv] bf16                            */
+  const float *grad_S;          /* [B,H,dv,dk] or NULL (zeros)                */
+  float *grad_q, *grad_k, *grad_v;
+  float *grad_alpha, *grad_theta;
+  float *grad_beta, *grad_w;
+  float *grad_S0;               /* or NULL                                    */
+  void *workspace;
+  size_t workspace_bytes;
+} gdr_bwd_args;
+
+/* Bytes of workspace the call needs (0 when the arguments are invalid). */
+size_t gdr_chunk_bwd_workspace(const gdr_bwd_args *a);
+
+gdr_status gdr_chunk_bwd(const gdr_bwd_args *a, void *hip_stream);
+
+/* ------------------------------------------------------------------------ */
 /* Single-token decode step on N independent states, in place.               */
 /* ------------------------------------------------------------------------ */
 typedef struct gdr_step_args {

@@ -11,6 +11,7 @@ Entry points (same names as the C ABI):
 * ``gdr_chunk_fwd``   -- chunked forward over a sequence, returns (o, S_out)
 * ``gdr_chunk_fwd_gated`` -- the same with the decay activation (and optionally
   the q/k L2 normalisation) computed in the kernel from raw inputs
+* ``gdr_chunk_bwd``   -- gradients of the plain-erase forward (recomputes it)
 * ``gdr_step_decode`` -- one token on a batch of states, in place, returns o
 """
 from __future__ import annotations
@@ -50,6 +51,18 @@ class GateArgs(ctypes.Structure):
     _fields_ = [("decay_x", _vp), ("decay_a", _vp), ("qk_l2norm", _i32), ("reserved", _i32)]
 
 
+class BwdArgs(ctypes.Structure):
+    """Mirror of ``gdr_bwd_args``."""
+    _fields_ = [
+        ("B", _i32), ("T", _i32), ("H", _i32), ("dk", _i32), ("dv", _i32), ("decay", _i32),
+        ("q", _vp), ("k", _vp), ("v", _vp), ("alpha", _vp), ("theta", _vp),
+        ("beta", _vp), ("w", _vp), ("S0", _vp), ("grad_o", _vp), ("grad_S", _vp),
+        ("grad_q", _vp), ("grad_k", _vp), ("grad_v", _vp), ("grad_alpha", _vp),
+        ("grad_theta", _vp), ("grad_beta", _vp), ("grad_w", _vp), ("grad_S0", _vp),
+        ("workspace", _vp), ("workspace_bytes", ctypes.c_size_t),
+    ]
+
+
 class StepArgs(ctypes.Structure):
     """Mirror of ``gdr_step_args``."""
     _fields_ = [
@@ -83,6 +96,10 @@ def load_library(path: Optional[str] = None) -> ctypes.CDLL:
     lib.gdr_chunk_fwd.restype = ctypes.c_int
     lib.gdr_chunk_fwd_gated.argtypes = [ctypes.POINTER(FwdArgs), ctypes.POINTER(GateArgs), _vp]
     lib.gdr_chunk_fwd_gated.restype = ctypes.c_int
+    lib.gdr_chunk_bwd.argtypes = [ctypes.POINTER(BwdArgs), _vp]
+    lib.gdr_chunk_bwd.restype = ctypes.c_int
+    lib.gdr_chunk_bwd_workspace.argtypes = [ctypes.POINTER(BwdArgs)]
+    lib.gdr_chunk_bwd_workspace.restype = ctypes.c_size_t
     lib.gdr_chunk_fwd_workspace.argtypes = [ctypes.POINTER(FwdArgs)]
     lib.gdr_chunk_fwd_workspace.restype = ctypes.c_size_t
     lib.gdr_step_decode.argtypes = [ctypes.POINTER(StepArgs), _vp]
@@ -161,6 +178,14 @@ def call_chunk_fwd_gated(args: FwdArgs, gate: GateArgs, stream=None) -> int:
     s = stream if isinstance(stream, ctypes.c_void_p) else (
         ctypes.c_void_p(0) if stream is None else _stream(stream))
     return lib.gdr_chunk_fwd_gated(ctypes.byref(args), ctypes.byref(gate), s)
+
+
+def call_chunk_bwd(args: BwdArgs, stream=None) -> int:
+    """Raw call with a filled ``BwdArgs``; returns the status code."""
+    lib = load_library()
+    s = stream if isinstance(stream, ctypes.c_void_p) else (
+        ctypes.c_void_p(0) if stream is None else _stream(stream))
+    return lib.gdr_chunk_bwd(ctypes.byref(args), s)
 
 
 def call_step_decode(args: StepArgs, stream=None) -> int:
@@ -289,6 +314,68 @@ def gdr_chunk_fwd_gated(q, k, v, decay_x, decay_a, w, beta, *, theta=None, qk_l2
     g.qk_l2norm, g.reserved = int(bool(qk_l2norm)), 0
     _check(call_chunk_fwd_gated(a, g, _stream(stream)))
     return o, S_out
+
+
+def gdr_chunk_bwd(q, k, v, alpha, w, beta, grad_o, *, theta=None, S0=None, grad_S=None,
+                  need_grad_S0=True, workspace=None, stream=None):
+    """Gradients of the plain-erase forward (``gdr_chunk_bwd`` in include/gdr.h).
+
+    Inputs as ``gdr_chunk_fwd`` (bf16 q, k, v; fp32 alpha [and theta], beta,
+    w; optional S0) plus grad_o [B,T,H,dv] bf16 and optional grad_S
+    [B,H,dv,dk] fp32.  Returns a dict of fp32 tensors: q, k, v, alpha, beta,
+    w, theta (rotation decay only) and S0 (when ``need_grad_S0``).  The
+    workspace (``gdr_chunk_bwd_workspace`` bytes) is allocated here unless a
+    large enough uint8 CUDA tensor is passed.
+    """
+    import torch
+    if q.dim() != 4 or k.dim() != 4 or v.dim() != 4:
+        raise ValueError("gdr: q, k and v must be [B,T,H,d]")
+    B, T, H, dk = q.shape
+    dv = v.shape[-1]
+    bf, f32 = torch.bfloat16, torch.float32
+    _expect(q, "q", (B, T, H, dk), bf)
+    _expect(k, "k", (B, T, H, dk), bf)
+    _expect(v, "v", (B, T, H, dv), bf)
+    rot = theta is not None
+    if rot and dk % 2:
+        raise ValueError("gdr: rotation-decay blocks need an even d_k")
+    gshape = (B, T, H, dk // 2) if rot else (B, T, H, dk)
+    _expect(alpha, "alpha", gshape, f32)
+    _expect(theta, "theta", gshape, f32, required=False)
+    _expect(w, "w", (B, T, H), f32)
+    _expect(beta, "beta", (B, T, H), f32)
+    _expect(S0, "S0", (B, H, dv, dk), f32, required=False)
+    _expect(grad_o, "grad_o", (B, T, H, dv), bf)
+    _expect(grad_S, "grad_S", (B, H, dv, dk), f32, required=False)
+    dev = q.device
+    g = {"q": torch.empty((B, T, H, dk), dtype=f32, device=dev),
+         "k": torch.empty((B, T, H, dk), dtype=f32, device=dev),
+         "v": torch.empty((B, T, H, dv), dtype=f32, device=dev),
+         "alpha": torch.empty(gshape, dtype=f32, device=dev),
+         "beta": torch.empty((B, T, H), dtype=f32, device=dev),
+         "w": torch.empty((B, T, H), dtype=f32, device=dev)}
+    if rot:
+        g["theta"] = torch.empty(gshape, dtype=f32, device=dev)
+    if need_grad_S0:
+        g["S0"] = torch.empty((B, H, dv, dk), dtype=f32, device=dev)
+    a = BwdArgs()
+    a.B, a.T, a.H, a.dk, a.dv = B, T, H, dk, dv
+    a.decay = GDR_DECAY_ROT2 if rot else GDR_DECAY_DIAG
+    a.q, a.k, a.v, a.alpha, a.theta = map(_ptr, (q, k, v, alpha, theta))
+    a.beta, a.w, a.S0, a.grad_o, a.grad_S = map(_ptr, (beta, w, S0, grad_o, grad_S))
+    a.grad_q, a.grad_k, a.grad_v = _ptr(g["q"]), _ptr(g["k"]), _ptr(g["v"])
+    a.grad_alpha, a.grad_theta = _ptr(g["alpha"]), _ptr(g.get("theta"))
+    a.grad_beta, a.grad_w, a.grad_S0 = _ptr(g["beta"]), _ptr(g["w"]), _ptr(g.get("S0"))
+    need = load_library().gdr_chunk_bwd_workspace(ctypes.byref(a))
+    if need == 0:
+        _check(call_chunk_bwd(a, _stream(stream)))   # reports why the arguments are invalid
+    if workspace is None:
+        workspace = torch.empty(need, dtype=torch.uint8, device=dev)
+    if workspace.dtype != torch.uint8 or workspace.numel() < need:
+        raise ValueError(f"gdr: workspace must be a uint8 tensor of at least {need} bytes")
+    a.workspace, a.workspace_bytes = _ptr(workspace), workspace.numel()
+    _check(call_chunk_bwd(a, _stream(stream)))
+    return g
 
 
 def gdr_step_decode(S, q, k, v, alpha, beta, w, *, theta=None, o=None, stream=None):

@@ -148,6 +148,52 @@ gdr_status check_gated(const gdr_fwd_args* a, const gdr_gate_args* g) {
   if ((reinterpret_cast<uintptr_t>(g->decay_a) & 3u) != 0) return GDR_ERR_ALIGN;
   return GDR_OK;
 }
+// Backward: the workspace holds the block-start states of the forward
+// recompute, its output o (not returned) and the per-value-tile partial sums,
+// each region 256-byte aligned.
+struct BwdLayout {
+  size_t ckpt, o, part, total;
+};
+
+size_t round256(size_t x) { return (x + 255) & ~(size_t)255; }
+
+BwdLayout bwd_layout(const gdr_bwd_args* a) {
+  const size_t nc = (size_t)(a->T + gdr::kBwdBlock - 1) / gdr::kBwdBlock;
+  const size_t bth = (size_t)a->B * a->T * a->H;
+  BwdLayout w;
+  w.ckpt = 0;
+  w.o = round256((size_t)a->B * a->H * nc * a->dv * a->dk * sizeof(float));
+  w.part = w.o + round256(bth * a->dv * 2);
+  w.total = w.part + round256(gdr::bwd_part_floats(a->B, a->T, a->H, a->dk, a->dv) * sizeof(float));
+  return w;
+}
+
+// Everything but the workspace size.
+gdr_status check_bwd_args(const gdr_bwd_args* a) {
+  if (!a) return GDR_ERR_NULL;
+  if (a->decay != GDR_DECAY_DIAG && a->decay != GDR_DECAY_ROT2) return GDR_ERR_DTYPE;
+  if (a->B <= 0 || a->T <= 0 || a->H <= 0 || a->dk <= 0 || a->dv <= 0) return GDR_ERR_SHAPE;
+  if ((a->dk != 64 && a->dk != 128) || a->dv != a->dk) return GDR_ERR_UNSUPPORTED;
+  if ((long long)a->B * a->T >= (1LL << 31)) return GDR_ERR_SHAPE;
+  // 32-bit byte offsets of the forward's buffer resources (T * H * dk < 2^29)
+  if ((long long)a->T * a->H >= (1LL << 29) / a->dk) return GDR_ERR_UNSUPPORTED;
+  if ((long long)a->B * a->T * a->H >= (1LL << 40) / a->dk) return GDR_ERR_SHAPE;
+  const void* need[] = {a->q, a->k, a->v, a->alpha, a->beta, a->w, a->grad_o, a->grad_q,
+                        a->grad_k, a->grad_v, a->grad_alpha, a->grad_beta, a->grad_w};
+  for (const void* p : need)
+    if (!p) return GDR_ERR_NULL;
+  if (a->decay == GDR_DECAY_ROT2) {
+    if (!a->theta || !a->grad_theta) return GDR_ERR_NULL;
+  } else if (a->theta || a->grad_theta) {
+    return GDR_ERR_ARG;
+  }
+  const void* vec[] = {a->q, a->k, a->v, a->alpha, a->theta, a->beta, a->w, a->S0, a->grad_o,
+                       a->grad_S, a->grad_q, a->grad_k, a->grad_v, a->grad_alpha, a->grad_theta,
+                       a->grad_beta, a->grad_w, a->grad_S0, a->workspace};
+  for (const void* p : vec)
+    if (p && !aligned16(p)) return GDR_ERR_ALIGN;
+  return GDR_OK;
+}
 }  // namespace
 
 extern "C" {
@@ -173,6 +219,72 @@ gdr_status gdr_chunk_fwd_gated(const gdr_fwd_args* a, const gdr_gate_args* g, vo
   p.gate_a = g->decay_a;
   if (!gdr::fwd_pipe_supported(p)) return GDR_ERR_UNSUPPORTED;
   const hipError_t e = gdr::launch_fwd(p, (hipStream_t)hip_stream);
+  return e == hipSuccess ? GDR_OK : GDR_ERR_HIP;
+}
+
+size_t gdr_chunk_bwd_workspace(const gdr_bwd_args* a) {
+  if (check_bwd_args(a) != GDR_OK) return 0;
+  return bwd_layout(a).total;
+}
+
+gdr_status gdr_chunk_bwd(const gdr_bwd_args* a, void* hip_stream) {
+  const gdr_status st = check_bwd_args(a);
+  if (st != GDR_OK) return st;
+  const BwdLayout lay = bwd_layout(a);
+  if (!a->workspace || a->workspace_bytes < lay.total) return GDR_ERR_WORKSPACE;
+  char* ws = (char*)a->workspace;
+  // forward recompute with block-start checkpoints
+  gdr::FwdParams f{};
+  f.B = a->B;
+  f.T = a->T;
+  f.H = a->H;
+  f.DK = a->dk;
+  f.DV = a->dv;
+  f.io_bf16 = 1;
+  f.block = gdr::kBwdBlock;
+  f.window = gdr::kBwdBlock;
+  f.decay = a->decay;
+  f.q = a->q;
+  f.k = a->k;
+  f.v = a->v;
+  f.alpha = a->alpha;
+  f.theta = a->theta;
+  f.beta = a->beta;
+  f.w = a->w;
+  f.S0 = a->S0;
+  f.o = ws + lay.o;
+  f.S_out = nullptr;
+  f.ckpt = (float*)(ws + lay.ckpt);
+  if (!gdr::fwd_pipe_supported(f)) return GDR_ERR_UNSUPPORTED;
+  hipError_t e = gdr::launch_fwd(f, (hipStream_t)hip_stream);
+  if (e != hipSuccess) return GDR_ERR_HIP;
+  gdr::BwdParams p{};
+  p.B = a->B;
+  p.T = a->T;
+  p.H = a->H;
+  p.DK = a->dk;
+  p.DV = a->dv;
+  p.decay = a->decay;
+  p.q = a->q;
+  p.k = a->k;
+  p.v = a->v;
+  p.alpha = a->alpha;
+  p.theta = a->theta;
+  p.beta = a->beta;
+  p.w = a->w;
+  p.grad_o = a->grad_o;
+  p.grad_S = a->grad_S;
+  p.grad_q = a->grad_q;
+  p.grad_k = a->grad_k;
+  p.grad_v = a->grad_v;
+  p.grad_alpha = a->grad_alpha;
+  p.grad_theta = a->grad_theta;
+  p.grad_beta = a->grad_beta;
+  p.grad_w = a->grad_w;
+  p.grad_S0 = a->grad_S0;
+  p.ckpt = (const float*)(ws + lay.ckpt);
+  p.part = (float*)(ws + lay.part);
+  e = gdr::launch_bwd(p, (hipStream_t)hip_stream);
   return e == hipSuccess ? GDR_OK : GDR_ERR_HIP;
 }
 

@@ -1,0 +1,526 @@
+// gdr_bwd.hip -- backward of the chunked gated delta rule (plain erase), gfx950.
+//
+// The forward (CARVE technical summary, sections 1 and 2.3; SFDA technical
+// summary, core architecture) is, per head and token,
+//     S_t = S_{t-1} D_t + beta_t (w_t v_t - S_{t-1} D_t k_t) k_t^T,  o_t = S_t q_t.
+// For a 32-token block with start state S and cumulative transitions
+// P_r = D_1 ... D_r, with Kp_r = P_r k_r, Qp_r = P_r q_r, Kh_r = P_r^{-T} k_r,
+// the deltas Dl (one row per token) solve (I + Diag(beta) N) Dl = Diag(beta)
+// (Diag(w) V - Kp S^T) with N = strict_lower(Kp Kh^T); then
+// O = Qp S^T + M Dl (M = lower(Qp Kh^T)) and S_end = (S + Dl^T Kh) P_L.
+// The backward runs the adjoint of these expressions block by block, last
+// block first, carrying G = dL/dS_end:
+//     dY = G P_L^T,  dDl = M^T dO + Kh dY^T,  dR = T^T dDl  (T = (I + Diag(beta) N)^{-1}),
+//     dA = -dR Dl^T,  dM = lower(dO Dl^T),  dN = strict_lower(Diag(beta) dA),
+//     dQp = dO S + dM Kh,  dKp = dN Kh - Diag(beta) dR S,
+//     dKh = Dl dY + dM^T Qp + dN^T Kp,
+//     dS = dY + dO^T Qp - (Diag(beta) dR)^T Kp   (the G of the previous block),
+// and the gradients of q, k, the decay, beta, w and v follow elementwise.
+//
+// One workgroup (4 waves) per (b, h, 32-channel value tile).  Every product
+// runs on the matrix cores with fp32 operands (v_mfma_f32_16x16x4_f32) from
+// LDS; G stays in accumulator registers across blocks.  Sums over value
+// channels (dq, dk, the decay's log-gradient, dbeta, dw) are written per value
+// tile to a partial-sum area and added by bwd_reduce_kernel, which also turns
+// the per-token log-gradients into decay gradients by a reverse prefix sum over
+// each block.  The state at the start of every block comes from the forward
+// recompute (checkpoints).
+//
+// Range: like the forward's split form, the block form divides by the running
+// decay, so every block must keep each channel's product P_L >= e^-40; a block
+// that does not gives non-finite gradients for its head (the forward's token
+// path has no counterpart here).
+#include <hip/hip_runtime.h>
+
+#include "gdr_kernels.h"
+#include "gdr_mfma.h"
+
+namespace gdr {
+namespace bwd {
+
+constexpr int L = kBwdBlock;   // tokens per block
+constexpr int TV = kBwdTile;   // value channels per workgroup
+constexpr int NT = 256;        // 4 waves
+
+using F = Op<float>;
+
+template <int DK>
+struct Smem {
+  static constexpr int PK = DK + 4, PV = TV + 4, PL = L + 4;
+  float Kp[L * PK], Qp[L * PK], Kh[L * PK], Gam[L * PK];
+  float S[TV * PK], DY[TV * PK];
+  float V[L * PV], DO[L * PV], In[L * PV], Dl[L * PV], DDl[L * PV], DR[L * PV], Din[L * PV];
+  float N[L * PL], M[L * PL], T[L * PL], DA[L * PL], DM[L * PL];
+  float beta[L], w[L];
+  float gl[DK];       // DIAG: P_L per channel; ROT2: (re, im) of P_L per pair
+  float dl_end[DK];   // block-end term of the decay's log-gradient
+  float red[6][L];    // per-token row sums from the waves (dw, dbeta)
+};
+
+__device__ inline float bf2f(const __bf16* p, size_t i) { return (float)p[i]; }
+
+// acc += A B over K, 16x16 output tile at rows r0, columns c0, with
+// A(r, k) = a[r * ARS + k * ACS] and B(k, c) = b[k * BRS + c * BCS].
+template <int ARS, int ACS, int BRS, int BCS, int K>
+__device__ inline void mm(f32x4& acc, const float* a, int r0, const float* b, int c0) {
+  const int l = lane_id(), n = l & 15, g = l >> 4;
+#pragma unroll
+  for (int k0 = 0; k0 < K; k0 += 32) {
+    f32x8 fa, fb;
+#pragma unroll
+    for (int s = 0; s < 8; ++s) {
+      fa[s] = a[(r0 + n) * ARS + (k0 + 8 * g + s) * ACS];
+      fb[s] = b[(k0 + 8 * g + s) * BRS + (c0 + n) * BCS];
+    }
+    F::mma(acc, fa, fb);
+  }
+}
+
+// Sum over the 16 lanes that share g (columns n of one accumulator row).
+__device__ inline float sum16(float x) {
+#pragma unroll
+  for (int off = 1; off < 16; off <<= 1) x += __shfl_xor(x, off);
+  return x;
+}
+
+template <int DK, int DECAY>
+__global__ __launch_bounds__(NT) void bwd_kernel(BwdParams p) {
+  using Sm = Smem<DK>;
+  constexpr int PK = Sm::PK, PV = Sm::PV, PL = Sm::PL;
+  constexpr int NCT = DK / 16, CPW = NCT / 4;   // column tiles of a DK-wide matrix per wave
+  __shared__ __attribute__((aligned(16))) Sm sm;
+  const int tid = threadIdx.x, l = tid & 63;
+  const int wv = __builtin_amdgcn_readfirstlane(tid >> 6);
+  const int n = l & 15, g = l >> 4;
+  const int H = p.H, Tn = p.T, DV = p.DV;
+  const int vt = blockIdx.x % p.n_vt, unit = blockIdx.x / p.n_vt;
+  const int b = unit / H, h = unit % H;
+  const int v0 = vt * TV;
+  const int nc = (Tn + L - 1) / L;
+  const size_t bh = (size_t)b * Tn * H + h;   // token-head row of token t: bh + t * H
+  const size_t BTH = (size_t)p.B * Tn * H;
+  const __bf16* q = (const __bf16*)p.q;
+  const __bf16* k = (const __bf16*)p.k;
+  const __bf16* v = (const __bf16*)p.v;
+  const __bf16* dO = (const __bf16*)p.grad_o;
+  float* Pq = p.part;
+  float* Pk = Pq + (size_t)p.n_vt * BTH * DK;
+  float* Pl = Pk + (size_t)p.n_vt * BTH * DK;
+  float* Pb = Pl + (size_t)p.n_vt * BTH * DK;
+  float* Pw = Pb + (size_t)p.n_vt * BTH;
+  const int ti2 = wv >> 1, tj2 = wv & 1;   // tile of a 32x32 matrix owned by this wave
+
+  // G = dL/dS at the end of the current block: rows v0 + 16 ti + 4g + j,
+  // columns 16 (wv * CPW + c) + n
+  f32x4 G[2][CPW];
+#pragma unroll
+  for (int ti = 0; ti < 2; ++ti)
+#pragma unroll
+    for (int c = 0; c < CPW; ++c)
+#pragma unroll
+      for (int j = 0; j < 4; ++j) {
+        const int row = v0 + 16 * ti + 4 * g + j, col = 16 * (wv * CPW + c) + n;
+        G[ti][c][j] = p.grad_S ? p.grad_S[((size_t)(b * H + h) * DV + row) * DK + col] : 0.f;
+      }
+
+  for (int c = nc - 1; c >= 0; --c) {
+    const int t0 = c * L, nt = min(L, Tn - t0);
+    // ---------------------------------------------------------------- loads
+    if (tid < L) {
+      const bool ok = tid < nt;
+      const size_t row = bh + (size_t)(t0 + tid) * H;
+      sm.beta[tid] = ok ? p.beta[row] : 0.f;
+      sm.w[tid] = ok ? p.w[row] : 0.f;
+    }
+    for (int e = tid; e < L * TV; e += NT) {
+      const int r = e / TV, i = e % TV;
+      const bool ok = r < nt;
+      const size_t src = (bh + (size_t)(t0 + r) * H) * DV + v0 + i;
+      sm.V[r * PV + i] = ok ? bf2f(v, src) : 0.f;
+      sm.DO[r * PV + i] = ok ? bf2f(dO, src) : 0.f;
+    }
+    {
+      const float* ck = p.ckpt + ((size_t)(b * H + h) * nc + c) * DV * DK;
+      for (int e = tid; e < TV * DK / 4; e += NT) {
+        const int i = e / (DK / 4), j4 = e % (DK / 4);
+        *(f32x4*)(sm.S + i * PK + 4 * j4) = *(const f32x4*)(ck + (size_t)(v0 + i) * DK + 4 * j4);
+      }
+    }
+    // cumulative transitions and the decayed key/query forms
+    if constexpr (DECAY == 0) {
+      if (tid < DK) {
+        const int j = tid;
+        float gam = 1.f;
+        for (int r = 0; r < L; ++r) {
+          const bool ok = r < nt;
+          const size_t row = bh + (size_t)(t0 + r) * H;
+          gam *= ok ? p.alpha[row * DK + j] : 1.f;
+          const float kk = ok ? bf2f(k, row * DK + j) : 0.f;
+          const float qq = ok ? bf2f(q, row * DK + j) : 0.f;
+          sm.Gam[r * PK + j] = gam;
+          sm.Kp[r * PK + j] = gam * kk;
+          sm.Qp[r * PK + j] = gam * qq;
+          sm.Kh[r * PK + j] = kk / gam;
+        }
+        sm.gl[j] = gam;
+      }
+    } else {
+      if (tid < DK / 2) {
+        const int pr = tid;
+        float zr = 1.f, zi = 0.f;
+        for (int r = 0; r < L; ++r) {
+          const bool ok = r < nt;
+          const size_t row = bh + (size_t)(t0 + r) * H;
+          const float gm = ok ? p.alpha[row * (DK / 2) + pr] : 1.f;
+          const float th = ok ? p.theta[row * (DK / 2) + pr] : 0.f;
+          float sn, cs;
+          __sincosf(th, &sn, &cs);
+          const float dr = gm * cs, di = gm * sn;
+          const float nr = zr * dr - zi * di, ni = zr * di + zi * dr;
+          zr = nr;
+          zi = ni;
+          const float k0 = ok ? bf2f(k, row * DK + 2 * pr) : 0.f;
+          const float k1 = ok ? bf2f(k, row * DK + 2 * pr + 1) : 0.f;
+          const float q0 = ok ? bf2f(q, row * DK + 2 * pr) : 0.f;
+          const float q1 = ok ? bf2f(q, row * DK + 2 * pr + 1) : 0.f;
+          const float iz = 1.f / (zr * zr + zi * zi);
+          const float hr = zr * iz, hi = zi * iz;   // P^{-T} on a pair: z / |z|^2
+          sm.Gam[r * PK + 2 * pr] = zr;
+          sm.Gam[r * PK + 2 * pr + 1] = zi;
+          sm.Kp[r * PK + 2 * pr] = zr * k0 - zi * k1;
+          sm.Kp[r * PK + 2 * pr + 1] = zr * k1 + zi * k0;
+          sm.Qp[r * PK + 2 * pr] = zr * q0 - zi * q1;
+          sm.Qp[r * PK + 2 * pr + 1] = zr * q1 + zi * q0;
+          sm.Kh[r * PK + 2 * pr] = hr * k0 - hi * k1;
+          sm.Kh[r * PK + 2 * pr + 1] = hr * k1 + hi * k0;
+        }
+        sm.gl[2 * pr] = zr;
+        sm.gl[2 * pr + 1] = zi;
+      }
+    }
+    lds_barrier();
+    // ------------------------------------------- N, M and inner = w v - Kp S^T
+    {
+      f32x4 an = {0.f, 0.f, 0.f, 0.f}, am = an, ai = an;
+      mm<PK, 1, 1, PK, DK>(an, sm.Kp, 16 * ti2, sm.Kh, 16 * tj2);
+      mm<PK, 1, 1, PK, DK>(am, sm.Qp, 16 * ti2, sm.Kh, 16 * tj2);
+      mm<PK, 1, 1, PK, DK>(ai, sm.Kp, 16 * ti2, sm.S, 16 * tj2);
+#pragma unroll
+      for (int j = 0; j < 4; ++j) {
+        const int r = 16 * ti2 + 4 * g + j, s = 16 * tj2 + n;
+        sm.N[r * PL + s] = s < r ? an[j] : 0.f;
+        sm.M[r * PL + s] = s <= r ? am[j] : 0.f;
+        sm.In[r * PV + s] = sm.w[r] * sm.V[r * PV + s] - ai[j];
+      }
+    }
+    lds_barrier();
+    // ------------------- T = (I + Diag(beta) N)^{-1}, and T Diag(beta) in DA
+    if (wv == 0 && l < L) {
+      float x[L];
+#pragma unroll
+      for (int i = 0; i < L; ++i) {
+        float acc = i == l ? 1.f : 0.f;
+        float dot = 0.f;
+#pragma unroll
+        for (int s = 0; s < i; ++s) dot += sm.N[i * PL + s] * x[s];
+        acc -= sm.beta[i] * dot;
+        x[i] = acc;
+        sm.T[i * PL + l] = acc;
+        sm.DA[i * PL + l] = acc * sm.beta[l];
+      }
+    }
+    lds_barrier();
+    // ----------------------------------------------- Dl = T Diag(beta) inner
+    {
+      f32x4 acc = {0.f, 0.f, 0.f, 0.f};
+      mm<PL, 1, PV, 1, L>(acc, sm.DA, 16 * ti2, sm.In, 16 * tj2);
+#pragma unroll
+      for (int j = 0; j < 4; ++j) sm.Dl[(16 * ti2 + 4 * g + j) * PV + 16 * tj2 + n] = acc[j];
+    }
+    lds_barrier();
+    // ---- Y = S + Dl^T Kh, S_end = Y P_L, dY = G P_L^T, block-end decay term
+    f32x4 dYr[2][CPW];
+    {
+      float te[CPW][2];   // per column tile: DIAG sum_i G S_end; ROT2 (da, dphi) of the pair
+#pragma unroll
+      for (int cc = 0; cc < CPW; ++cc) te[cc][0] = te[cc][1] = 0.f;
+#pragma unroll
+      for (int ti = 0; ti < 2; ++ti) {
+#pragma unroll
+        for (int cc = 0; cc < CPW; ++cc) {
+          const int col0 = 16 * (wv * CPW + cc), ch = col0 + n;
+          f32x4 y;
+#pragma unroll
+          for (int j = 0; j < 4; ++j) y[j] = sm.S[(16 * ti + 4 * g + j) * PK + ch];
+          mm<1, PV, PK, 1, L>(y, sm.Dl, 16 * ti, sm.Kh, col0);
+          if constexpr (DECAY == 0) {
+            const float z = sm.gl[ch];
+#pragma unroll
+            for (int j = 0; j < 4; ++j) {
+              te[cc][0] += G[ti][cc][j] * (y[j] * z);
+              dYr[ti][cc][j] = G[ti][cc][j] * z;
+            }
+          } else {
+            const bool even = (n & 1) == 0;
+            const float zr = sm.gl[ch & ~1], zi = sm.gl[ch | 1];
+#pragma unroll
+            for (int j = 0; j < 4; ++j) {
+              const float yo = __shfl_xor(y[j], 1), go = __shfl_xor(G[ti][cc][j], 1);
+              const float y0 = even ? y[j] : yo, y1 = even ? yo : y[j];
+              const float g0 = even ? G[ti][cc][j] : go, g1 = even ? go : G[ti][cc][j];
+              // a state row is multiplied by conj(z) (the transition acts on
+              // the right), the adjoint row by z
+              const float s0 = y0 * zr + y1 * zi, s1 = y1 * zr - y0 * zi;   // S_end pair
+              const float d0 = g0 * zr - g1 * zi, d1 = g0 * zi + g1 * zr;   // dY pair
+              dYr[ti][cc][j] = even ? d0 : d1;
+              if (even) {   // d/da of conj(z) is conj(z), d/dphi is -i conj(z)
+                te[cc][0] += g0 * s0 + g1 * s1;
+                te[cc][1] += g0 * s1 - g1 * s0;
+              }
+            }
+          }
+#pragma unroll
+          for (int j = 0; j < 4; ++j) sm.DY[(16 * ti + 4 * g + j) * PK + ch] = dYr[ti][cc][j];
+        }
+      }
+#pragma unroll
+      for (int cc = 0; cc < CPW; ++cc) {
+        const int ch = 16 * (wv * CPW + cc) + n;
+#pragma unroll
+        for (int e = 0; e < 2; ++e) {
+          te[cc][e] += __shfl_xor(te[cc][e], 16);
+          te[cc][e] += __shfl_xor(te[cc][e], 32);
+        }
+        if (g == 0) {
+          if constexpr (DECAY == 0) {
+            sm.dl_end[ch] = te[cc][0];
+          } else if ((n & 1) == 0) {
+            sm.dl_end[ch >> 1] = te[cc][0];
+            sm.dl_end[DK / 2 + (ch >> 1)] = te[cc][1];
+          }
+        }
+      }
+    }
+    lds_barrier();
+    // ------------------------------------------ dDl = M^T dO + Kh dY^T  [L x TV]
+    {
+      f32x4 acc = {0.f, 0.f, 0.f, 0.f};
+      mm<1, PL, PV, 1, L>(acc, sm.M, 16 * ti2, sm.DO, 16 * tj2);
+      mm<PK, 1, 1, PK, DK>(acc, sm.Kh, 16 * ti2, sm.DY, 16 * tj2);
+#pragma unroll
+      for (int j = 0; j < 4; ++j) sm.DDl[(16 * ti2 + 4 * g + j) * PV + 16 * tj2 + n] = acc[j];
+    }
+    lds_barrier();
+    // ------------ dR = T^T dDl; dinner = beta dR; grad_v; dw and dbeta row sums
+    {
+      f32x4 acc = {0.f, 0.f, 0.f, 0.f};
+      mm<1, PL, PV, 1, L>(acc, sm.T, 16 * ti2, sm.DDl, 16 * tj2);
+#pragma unroll
+      for (int j = 0; j < 4; ++j) {
+        const int r = 16 * ti2 + 4 * g + j, i = 16 * tj2 + n;
+        const float din = sm.beta[r] * acc[j];
+        sm.DR[r * PV + i] = acc[j];
+        sm.Din[r * PV + i] = din;
+        if (r < nt) p.grad_v[(bh + (size_t)(t0 + r) * H) * DV + v0 + i] = sm.w[r] * din;
+        const float pw = sum16(din * sm.V[r * PV + i]);
+        const float pb = sum16(acc[j] * sm.In[r * PV + i]);
+        if (n == 0) {
+          sm.red[tj2][r] = pw;
+          sm.red[2 + tj2][r] = pb;
+        }
+      }
+    }
+    lds_barrier();
+    // --------------------- dA = -dR Dl^T -> dN; dM = lower(dO Dl^T); dbeta part
+    {
+      f32x4 da = {0.f, 0.f, 0.f, 0.f}, dm = da;
+      mm<PV, 1, 1, PV, TV>(da, sm.DR, 16 * ti2, sm.Dl, 16 * tj2);
+      mm<PV, 1, 1, PV, TV>(dm, sm.DO, 16 * ti2, sm.Dl, 16 * tj2);
+#pragma unroll
+      for (int j = 0; j < 4; ++j) {
+        const int r = 16 * ti2 + 4 * g + j, s = 16 * tj2 + n;
+        const float a = -da[j];
+        const float pb = sum16(s < r ? a * sm.N[r * PL + s] : 0.f);
+        if (n == 0) sm.red[4 + tj2][r] = pb;
+        sm.DA[r * PL + s] = s < r ? sm.beta[r] * a : 0.f;   // dN
+        sm.DM[r * PL + s] = s <= r ? dm[j] : 0.f;
+      }
+    }
+    lds_barrier();
+    // ------------------------- dQp, dKp, dKh [L x DK] and the per-tile partials
+    if (tid < L && tid < nt) {
+      const size_t row = bh + (size_t)(t0 + tid) * H;
+      Pw[(size_t)vt * BTH + row] = sm.red[0][tid] + sm.red[1][tid];
+      Pb[(size_t)vt * BTH + row] = sm.red[2][tid] + sm.red[3][tid] + sm.red[4][tid] + sm.red[5][tid];
+    }
+#pragma unroll 1
+    for (int ti = 0; ti < 2; ++ti) {
+#pragma unroll 1
+      for (int cc = 0; cc < CPW; ++cc) {
+        const int col0 = 16 * (wv * CPW + cc), ch = col0 + n;
+        f32x4 dq = {0.f, 0.f, 0.f, 0.f}, dkp = dq, dkp2 = dq, dkh = dq;
+        mm<PV, 1, PK, 1, TV>(dq, sm.DO, 16 * ti, sm.S, col0);
+        mm<PL, 1, PK, 1, L>(dq, sm.DM, 16 * ti, sm.Kh, col0);
+        mm<PL, 1, PK, 1, L>(dkp, sm.DA, 16 * ti, sm.Kh, col0);
+        mm<PV, 1, PK, 1, TV>(dkp2, sm.Din, 16 * ti, sm.S, col0);
+        mm<PV, 1, PK, 1, TV>(dkh, sm.Dl, 16 * ti, sm.DY, col0);
+        mm<1, PL, PK, 1, L>(dkh, sm.DM, 16 * ti, sm.Qp, col0);
+        mm<1, PL, PK, 1, L>(dkh, sm.DA, 16 * ti, sm.Kp, col0);
+#pragma unroll
+        for (int j = 0; j < 4; ++j) {
+          const int r = 16 * ti + 4 * g + j;
+          const float gq = dq[j], gkp = dkp[j] - dkp2[j], gkh = dkh[j];
+          const float kp = sm.Kp[r * PK + ch], qp = sm.Qp[r * PK + ch], kh = sm.Kh[r * PK + ch];
+          const size_t row = bh + (size_t)(t0 + r) * H;
+          const size_t o = ((size_t)vt * BTH + row) * DK;
+          if constexpr (DECAY == 0) {
+            const float gam = sm.Gam[r * PK + ch];
+            float dl = kp * gkp - kh * gkh + qp * gq;
+            if (r == nt - 1) dl += sm.dl_end[ch];
+            if (r < nt) {
+              Pq[o + ch] = gam * gq;
+              Pk[o + ch] = gam * gkp + gkh / gam;
+              Pl[o + ch] = dl;
+            }
+          } else {
+            // pairs (2p, 2p + 1) sit in adjacent lanes
+            const bool even = (n & 1) == 0;
+            const float zr = sm.Gam[r * PK + (ch & ~1)], zi = sm.Gam[r * PK + (ch | 1)];
+            const float o_q = __shfl_xor(gq, 1), o_kp = __shfl_xor(gkp, 1), o_kh = __shfl_xor(gkh, 1);
+            const float x_kp = __shfl_xor(kp, 1), x_qp = __shfl_xor(qp, 1), x_kh = __shfl_xor(kh, 1);
+            // components 0 and 1 of each pair
+            const float q0 = even ? gq : o_q, q1 = even ? o_q : gq;
+            const float a0 = even ? gkp : o_kp, a1 = even ? o_kp : gkp;
+            const float h0 = even ? gkh : o_kh, h1 = even ? o_kh : gkh;
+            const float Kp0 = even ? kp : x_kp, Kp1 = even ? x_kp : kp;
+            const float Qp0 = even ? qp : x_qp, Qp1 = even ? x_qp : qp;
+            const float Kh0 = even ? kh : x_kh, Kh1 = even ? x_kh : kh;
+            // dq = conj(z) dQp; dk = conj(z) dKp + conj(z) / |z|^2 dKh
+            const float iz = 1.f / (zr * zr + zi * zi);
+            const float dq0 = zr * q0 + zi * q1, dq1 = zr * q1 - zi * q0;
+            const float dk0 = zr * a0 + zi * a1 + iz * (zr * h0 + zi * h1);
+            const float dk1 = zr * a1 - zi * a0 + iz * (zr * h1 - zi * h0);
+            // log-magnitude and angle gradients of the pair's running product
+            float da = Kp0 * a0 + Kp1 * a1 - (Kh0 * h0 + Kh1 * h1) + Qp0 * q0 + Qp1 * q1;
+            float dphi = (-a0 * Kp1 + a1 * Kp0) + (-h0 * Kh1 + h1 * Kh0) + (-q0 * Qp1 + q1 * Qp0);
+            const int pr = ch >> 1;
+            if (r == nt - 1) {
+              da += sm.dl_end[pr];
+              dphi += sm.dl_end[DK / 2 + pr];
+            }
+            if (r < nt) {
+              Pq[o + ch] = even ? dq0 : dq1;
+              Pk[o + ch] = even ? dk0 : dk1;
+              Pl[o + (even ? pr : DK / 2 + pr)] = even ? da : dphi;
+            }
+          }
+        }
+      }
+    }
+    // --------------------- dS = dY + dO^T Qp - dinner^T Kp: G of the previous block
+#pragma unroll
+    for (int ti = 0; ti < 2; ++ti) {
+#pragma unroll
+      for (int cc = 0; cc < CPW; ++cc) {
+        const int col0 = 16 * (wv * CPW + cc);
+        f32x4 acc = dYr[ti][cc], acc2 = {0.f, 0.f, 0.f, 0.f};
+        mm<1, PV, PK, 1, L>(acc, sm.DO, 16 * ti, sm.Qp, col0);
+        mm<1, PV, PK, 1, L>(acc2, sm.Din, 16 * ti, sm.Kp, col0);
+        G[ti][cc] = acc - acc2;
+      }
+    }
+    lds_barrier();
+  }
+  if (p.grad_S0) {
+#pragma unroll
+    for (int ti = 0; ti < 2; ++ti)
+#pragma unroll
+      for (int cc = 0; cc < CPW; ++cc)
+#pragma unroll
+        for (int j = 0; j < 4; ++j) {
+          const int row = v0 + 16 * ti + 4 * g + j, col = 16 * (wv * CPW + cc) + n;
+          p.grad_S0[((size_t)(b * H + h) * DV + row) * DK + col] = G[ti][cc][j];
+        }
+  }
+}
+
+// Sums the value tiles' partials; turns the per-token log-gradients of the
+// running decay into gradients of each token's decay by a reverse prefix sum
+// over the block (a token's decay enters every running product from it to
+// the block's end).  One workgroup of DK threads per (b, h, block).
+template <int DK, int DECAY>
+__global__ __launch_bounds__(DK) void bwd_reduce_kernel(BwdParams p) {
+  const int H = p.H, Tn = p.T;
+  const int nc = (Tn + L - 1) / L;
+  const int c = blockIdx.x % nc, unit = blockIdx.x / nc;
+  const int b = unit / H, h = unit % H;
+  const int t0 = c * L, nt = min(L, Tn - t0);
+  const int j = threadIdx.x;
+  const size_t bh = (size_t)b * Tn * H + h;
+  const size_t BTH = (size_t)p.B * Tn * H;
+  const int nvt = p.n_vt;
+  const float* Pq = p.part;
+  const float* Pk = Pq + (size_t)nvt * BTH * DK;
+  const float* Pl = Pk + (size_t)nvt * BTH * DK;
+  const float* Pb = Pl + (size_t)nvt * BTH * DK;
+  const float* Pw = Pb + (size_t)nvt * BTH;
+  float acc0 = 0.f, acc1 = 0.f;
+  for (int r = nt - 1; r >= 0; --r) {
+    const size_t row = bh + (size_t)(t0 + r) * H;
+    float sq = 0.f, sk = 0.f, sl0 = 0.f, sl1 = 0.f;
+    for (int t = 0; t < nvt; ++t) {
+      const size_t o = ((size_t)t * BTH + row) * DK;
+      sq += Pq[o + j];
+      sk += Pk[o + j];
+      if (DECAY == 0) {
+        sl0 += Pl[o + j];
+      } else if (j < DK / 2) {
+        sl0 += Pl[o + j];
+        sl1 += Pl[o + DK / 2 + j];
+      }
+    }
+    p.grad_q[row * DK + j] = sq;
+    p.grad_k[row * DK + j] = sk;
+    if (DECAY == 0) {
+      acc0 += sl0;
+      p.grad_alpha[row * DK + j] = acc0 / p.alpha[row * DK + j];
+    } else if (j < DK / 2) {
+      acc0 += sl0;
+      acc1 += sl1;
+      p.grad_alpha[row * (DK / 2) + j] = acc0 / p.alpha[row * (DK / 2) + j];
+      p.grad_theta[row * (DK / 2) + j] = acc1;
+    }
+    if (j == 0) {
+      float sb = 0.f, sw = 0.f;
+      for (int t = 0; t < nvt; ++t) {
+        sb += Pb[(size_t)t * BTH + row];
+        sw += Pw[(size_t)t * BTH + row];
+      }
+      p.grad_beta[row] = sb;
+      p.grad_w[row] = sw;
+    }
+  }
+}
+
+template <int DK, int DECAY>
+hipError_t launch_dk(const BwdParams& p0, hipStream_t s) {
+  BwdParams p = p0;
+  p.n_vt = p.DV / TV;
+  const int nc = (p.T + L - 1) / L;
+  hipLaunchKernelGGL((bwd_kernel<DK, DECAY>), dim3(p.B * p.H * p.n_vt), dim3(NT), 0, s, p);
+  hipError_t e = hipGetLastError();
+  if (e != hipSuccess) return e;
+  hipLaunchKernelGGL((bwd_reduce_kernel<DK, DECAY>), dim3(p.B * p.H * nc), dim3(DK), 0, s, p);
+  return hipGetLastError();
+}
+
+}  // namespace bwd
+
+hipError_t launch_bwd(const BwdParams& p, hipStream_t s) {
+  const bool rot = p.decay != 0;
+  if (p.DK == 128 && p.DV == 128) return rot ? bwd::launch_dk<128, 1>(p, s) : bwd::launch_dk<128, 0>(p, s);
+  if (p.DK == 64 && p.DV == 64) return rot ? bwd::launch_dk<64, 1>(p, s) : bwd::launch_dk<64, 0>(p, s);
+  return hipErrorInvalidValue;
+}
+
+}  // namespace gdr

@@ -655,10 +655,13 @@ __device__ inline void stage_raw(SlotA<DK, TV>& A, const Rsrc& rs, int c0, int i
   }
 }
 
-template <int DK, int TV, int DECAY, bool CONTENT, int GMODE = 0>
+// CKPT: the backward's forward recompute, which also stores the state at the
+// start of every block (p.ckpt).
+template <int DK, int TV, int DECAY, bool CONTENT, int GMODE = 0, bool CKPT = false>
 __global__ __launch_bounds__((NWP + NWS + TV / 16 + (CONTENT ? 1 : 0)) * 64) void gdr_fwd_pipe_kernel(
     FwdParams p) {
   static_assert(GMODE == 0 || !CONTENT, "the gated forward has the plain erase");
+  static_assert(!CKPT || (GMODE == 0 && !CONTENT), "checkpoints are taken by the plain forward");
   using C = Cfg<DK, TV>;
   using O = Op<bf>;
   using frag = O::frag;
@@ -715,7 +718,7 @@ __global__ __launch_bounds__((NWP + NWS + TV / 16 + (CONTENT ? 1 : 0)) * 64) voi
   __shared__ __attribute__((aligned(16))) float sNq[GNORM ? 3 : 1][GNORM ? L : 1];
   // content-aware: beta and beta*w of a block, computed by the solve for the
   // consumer (one per prep slot)
-  __shared__ __attribute__((aligned(16))) float sBc[CONTENT ? 3 : 1][CONTENT ? 2 : 1][L];
+  __shared__ __attribute__((aligned(16))) float sBc[CONTENT ? 3 : 1][2][L];
   if constexpr (CONTENT) {
     if (tid < DV) {
       float acc = 0.f;
@@ -1124,6 +1127,11 @@ __global__ __launch_bounds__((NWP + NWS + TV / 16 + (CONTENT ? 1 : 0)) * 64) voi
           const SlotA<DK, TV>& A = sh.a[vi % 3];
           const SlotS& S = sh.s[vi & 1];
           const int c0 = i * L;
+          if constexpr (CKPT) {   // the state at the start of block i, for the backward
+            float* dst = p.ckpt + (((size_t)(b * H + h) * nchunks + i) * DV + v0 + 16 * cw + n) * DK + 4 * g;
+#pragma unroll
+            for (int ct = 0; ct < NCT; ++ct) *(f32x4*)(dst + 16 * ct) = Sacc[ct];
+          }
           if constexpr (TOKEN) {
             // raw transition, keys and queries staged by the solve; o_t[n] is
             // stored as one bf16 by the lanes with g == 0
@@ -1310,14 +1318,14 @@ __global__ __launch_bounds__((NWP + NWS + TV / 16 + (CONTENT ? 1 : 0)) * 64) voi
   }
 }
 
-template <int DK, int TV, int DECAY, bool CONTENT = false, int GMODE = 0>
+template <int DK, int TV, int DECAY, bool CONTENT = false, int GMODE = 0, bool CKPT = false>
 hipError_t launch(const FwdParams& p0, hipStream_t s) {
   FwdParams p = p0;
   p.n_vt = p.DV / TV;
   p.n_units = p.B * p.H;
   const int groups = (p.n_units + 7) / 8;
   // content-aware: one more wave carries the projected row u_h^T S
-  hipLaunchKernelGGL((gdr_fwd_pipe_kernel<DK, TV, DECAY, CONTENT, GMODE>), dim3(groups * 8 * p.n_vt),
+  hipLaunchKernelGGL((gdr_fwd_pipe_kernel<DK, TV, DECAY, CONTENT, GMODE, CKPT>), dim3(groups * 8 * p.n_vt),
                      dim3(Cfg<DK, TV>::NT + (CONTENT ? 64 : 0)), 0, s, p);
   return hipGetLastError();
 }
@@ -1352,6 +1360,11 @@ hipError_t launch_fwd_pipe(const FwdParams& p, hipStream_t s) {
     return rot ? pipe::launch<64, 16, 1, true>(p, s) : pipe::launch<64, 16, 0, true>(p, s);
   }
   if (p.gmode != 0) return launch_fwd_gated(p, s);
+  if (p.ckpt != nullptr) {   // the backward's forward recompute
+    if (p.DK == 128) return rot ? pipe::launch<128, 32, 1, false, 0, true>(p, s) : pipe::launch<128, 32, 0, false, 0, true>(p, s);
+    if (p.DK == 64) return rot ? pipe::launch<64, 32, 1, false, 0, true>(p, s) : pipe::launch<64, 32, 0, false, 0, true>(p, s);
+    return hipErrorInvalidValue;
+  }
   if (p.DK == 128) {
     if ((long)p.B * p.H * 2 >= 192) {
       return rot ? pipe::launch<128, 64, 1>(p, s) : pipe::launch<128, 64, 0>(p, s);

@@ -34,6 +34,37 @@ struct FwdParams {
   int gmode;
   const void* gate_x;
   const float* gate_a;
+  // backward's forward recompute: when set, the state at the start of every
+  // 32-token block, [B, H, ceil(T / 32), DV, DK] fp32
+  float* ckpt;
+};
+
+// Backward of the plain-erase forward (gdr_bwd.hip).  Inputs as the forward
+// (bf16 q, k, v, grad_o), fp32 gradients out; ckpt holds the block-start
+// states from the forward recompute, part the per-value-tile partial sums.
+struct BwdParams {
+  int B, T, H, DK, DV;
+  int decay;
+  const void* q;
+  const void* k;
+  const void* v;
+  const float* alpha;
+  const float* theta;
+  const float* beta;
+  const float* w;
+  const void* grad_o;
+  const float* grad_S;   // gradient of S_T, or null
+  float* grad_q;
+  float* grad_k;
+  float* grad_v;
+  float* grad_alpha;
+  float* grad_theta;
+  float* grad_beta;
+  float* grad_w;
+  float* grad_S0;        // or null
+  const float* ckpt;
+  float* part;           // partial sums, bwd_part_floats() floats
+  int n_vt;              // value tiles per (b, h); set by the launcher
 };
 
 struct StepParams {
@@ -56,6 +87,16 @@ hipError_t launch_fwd(const FwdParams& p, hipStream_t stream);
 bool fwd_pipe_supported(const FwdParams& p);
 hipError_t launch_fwd_pipe(const FwdParams& p, hipStream_t stream);
 hipError_t launch_step(const StepParams& p, hipStream_t stream);
+hipError_t launch_bwd(const BwdParams& p, hipStream_t stream);
+// block length of the backward (and of the forward's checkpoints) and the
+// value-tile width of the backward kernel
+constexpr int kBwdBlock = 32;
+constexpr int kBwdTile = 32;
+// floats of the partial-sum area: per value tile and token-head, dq, dk and
+// the decay's log-gradient (DK each), then dbeta and dw
+inline size_t bwd_part_floats(int B, int T, int H, int DK, int DV) {
+  return (size_t)(DV / kBwdTile) * B * T * H * (3 * (size_t)DK + 2);
+}
 int fwd_block_len(int dk, int chunk, bool io_bf16);
 
 }  // namespace gdr

@@ -12,7 +12,8 @@
 namespace gdr {
 static FwdParams g_fwd;
 static StepParams g_step;
-static int g_nfwd = 0, g_nstep = 0;
+static BwdParams g_bwd;
+static int g_nfwd = 0, g_nstep = 0, g_nbwd = 0;
 hipError_t launch_fwd(const FwdParams& p, hipStream_t) {
   g_fwd = p;
   ++g_nfwd;
@@ -21,6 +22,11 @@ hipError_t launch_fwd(const FwdParams& p, hipStream_t) {
 hipError_t launch_step(const StepParams& p, hipStream_t) {
   g_step = p;
   ++g_nstep;
+  return hipSuccess;
+}
+hipError_t launch_bwd(const BwdParams& p, hipStream_t) {
+  g_bwd = p;
+  ++g_nbwd;
   return hipSuccess;
 }
 }  // namespace gdr
@@ -117,6 +123,43 @@ int main() {
   b = a; b.T = 1 << 22; b.H = 1; CHECK(gdr_chunk_fwd_gated(&b, &g, nullptr) == GDR_ERR_UNSUPPORTED);
   b = a; b.beta = nullptr; CHECK(gdr_chunk_fwd_gated(&b, &g, nullptr) == GDR_ERR_NULL);
   CHECK(gdr::g_nfwd == before_g);
+
+  // backward: forward recompute with checkpoints in the workspace, then the
+  // backward kernels on the same workspace
+  gdr_bwd_args w;
+  std::memset(&w, 0, sizeof w);
+  w.B = 2; w.T = 100; w.H = 4; w.dk = 128; w.dv = 128; w.decay = GDR_DECAY_DIAG;
+  w.q = fake(1); w.k = fake(2); w.v = fake(3); w.alpha = (const float*)fake(4);
+  w.beta = (const float*)fake(5); w.w = (const float*)fake(6); w.grad_o = fake(7);
+  w.grad_q = (float*)fake(8); w.grad_k = (float*)fake(9); w.grad_v = (float*)fake(10);
+  w.grad_alpha = (float*)fake(11); w.grad_beta = (float*)fake(12); w.grad_w = (float*)fake(13);
+  const size_t need = gdr_chunk_bwd_workspace(&w);
+  // 4 blocks of 32: checkpoints 2*4*4*128*128*4, o 800*128*2, partials 4*800*386*4
+  CHECK(need == (size_t)2 * 4 * 4 * 128 * 128 * 4 + 800 * 128 * 2 + (size_t)4 * 800 * 386 * 4);
+  CHECK(gdr_chunk_bwd(&w, nullptr) == GDR_ERR_WORKSPACE);
+  w.workspace = fake(20); w.workspace_bytes = need - 1;
+  CHECK(gdr_chunk_bwd(&w, nullptr) == GDR_ERR_WORKSPACE);
+  w.workspace_bytes = need;
+  const int f_before = gdr::g_nfwd;
+  CHECK(gdr_chunk_bwd(&w, nullptr) == GDR_OK);
+  CHECK(gdr::g_nfwd == f_before + 1 && gdr::g_nbwd == 1);
+  CHECK(gdr::g_fwd.ckpt == (float*)w.workspace && gdr::g_fwd.S_out == nullptr && gdr::g_fwd.o != nullptr);
+  CHECK(gdr::g_bwd.ckpt == gdr::g_fwd.ckpt && gdr::g_bwd.grad_q == w.grad_q && gdr::g_bwd.grad_S0 == nullptr);
+  CHECK((char*)gdr::g_bwd.part >= (char*)gdr::g_fwd.o + 800 * 128 * 2);
+  CHECK((char*)gdr::g_bwd.part + (size_t)4 * 800 * 386 * 4 <= (char*)w.workspace + need);
+  {
+    gdr_bwd_args x = w; x.dk = x.dv = 32; CHECK(gdr_chunk_bwd(&x, nullptr) == GDR_ERR_UNSUPPORTED);
+    CHECK(gdr_chunk_bwd_workspace(&x) == 0);
+    x = w; x.grad_beta = nullptr; CHECK(gdr_chunk_bwd(&x, nullptr) == GDR_ERR_NULL);
+    x = w; x.theta = (const float*)fake(21); CHECK(gdr_chunk_bwd(&x, nullptr) == GDR_ERR_ARG);
+    x = w; x.decay = GDR_DECAY_ROT2; CHECK(gdr_chunk_bwd(&x, nullptr) == GDR_ERR_NULL);
+    x = w; x.decay = GDR_DECAY_ROT2; x.theta = (const float*)fake(21); x.grad_theta = (float*)fake(22);
+    CHECK(gdr_chunk_bwd(&x, nullptr) == GDR_OK && gdr::g_bwd.decay == 1);
+    x = w; x.grad_q = (float*)((char*)fake(8) + 4); CHECK(gdr_chunk_bwd(&x, nullptr) == GDR_ERR_ALIGN);
+    x = w; x.T = 0; CHECK(gdr_chunk_bwd(&x, nullptr) == GDR_ERR_SHAPE);
+    x = w; x.B = 0x7fffffff; x.T = 0x7fffffff; CHECK(gdr_chunk_bwd(&x, nullptr) == GDR_ERR_SHAPE);
+    CHECK(gdr_chunk_bwd(nullptr, nullptr) == GDR_ERR_NULL && gdr_chunk_bwd_workspace(nullptr) == 0);
+  }
 
   // decode
   gdr_step_args s;

@@ -25,8 +25,9 @@ def _declared():
 def test_library_loads_and_exports_header_symbols():
     lib = gdr.load_library()
     names = _declared()
-    assert {"gdr_chunk_fwd", "gdr_chunk_fwd_gated", "gdr_step_decode",
-            "gdr_chunk_fwd_workspace", "gdr_status_str", "gdr_abi_version"} <= set(names)
+    assert {"gdr_chunk_fwd", "gdr_chunk_fwd_gated", "gdr_chunk_bwd", "gdr_chunk_bwd_workspace",
+            "gdr_step_decode", "gdr_chunk_fwd_workspace", "gdr_status_str",
+            "gdr_abi_version"} <= set(names)
     for nm in names:
         assert hasattr(lib, nm), nm
     out = subprocess.run(["nm", "-D", "--defined-only", gdr.LIB_PATH], capture_output=True,
@@ -132,6 +133,51 @@ def test_gated_fwd_null_structs():
     assert lib.gdr_chunk_fwd_gated(ctypes.byref(_good_fwd(alpha=None)), None, None) == gdr.GDR_ERR_NULL
 
 
+def _good_bwd(**kw):
+    a = gdr.BwdArgs()
+    a.B, a.T, a.H, a.dk, a.dv, a.decay = 2, 100, 4, 64, 64, gdr.GDR_DECAY_DIAG
+    for f in ("q", "k", "v", "alpha", "beta", "w", "grad_o", "grad_q", "grad_k", "grad_v",
+              "grad_alpha", "grad_beta", "grad_w"):
+        setattr(a, f, FAKE)
+    for f, val in kw.items():
+        setattr(a, f, val)
+    return a
+
+
+BWD_CASES = [
+    (dict(q=None), gdr.GDR_ERR_NULL),
+    (dict(grad_o=None), gdr.GDR_ERR_NULL),
+    (dict(grad_w=None), gdr.GDR_ERR_NULL),
+    (dict(dk=32, dv=32), gdr.GDR_ERR_UNSUPPORTED),
+    (dict(dk=64, dv=128), gdr.GDR_ERR_UNSUPPORTED),
+    (dict(decay=5), gdr.GDR_ERR_DTYPE),
+    (dict(H=0), gdr.GDR_ERR_SHAPE),
+    (dict(T=1 << 23, H=1), gdr.GDR_ERR_UNSUPPORTED),
+    (dict(theta=FAKE), gdr.GDR_ERR_ARG),
+    (dict(decay=gdr.GDR_DECAY_ROT2, theta=FAKE), gdr.GDR_ERR_NULL),   # no grad_theta
+    (dict(grad_S0=MISALIGNED), gdr.GDR_ERR_ALIGN),
+    (dict(), gdr.GDR_ERR_WORKSPACE),                                  # no workspace
+    (dict(workspace=FAKE, workspace_bytes=1024), gdr.GDR_ERR_WORKSPACE),
+]
+
+
+@pytest.mark.parametrize("kw,status", BWD_CASES)
+def test_bwd_rejects_before_any_hip_call(kw, status):
+    assert gdr.call_chunk_bwd(_good_bwd(**kw)) == status
+
+
+def test_bwd_workspace_size():
+    """Checkpoints of every 32-token block, the recompute's o and the partials."""
+    lib = gdr.load_library()
+    a = _good_bwd()
+    nc = (100 + 31) // 32
+    want = 2 * 4 * nc * 64 * 64 * 4 + 2 * 100 * 4 * 64 * 2 + 2 * (2 * 100 * 4) * (3 * 64 + 2) * 4
+    rounded = sum(-(-x // 256) * 256 for x in (2 * 4 * nc * 64 * 64 * 4, 2 * 100 * 4 * 64 * 2,
+                                               2 * (2 * 100 * 4) * (3 * 64 + 2) * 4))
+    assert lib.gdr_chunk_bwd_workspace(ctypes.byref(a)) == rounded >= want
+    assert lib.gdr_chunk_bwd_workspace(ctypes.byref(_good_bwd(dk=48, dv=48))) == 0
+
+
 def test_fwd_null_args():
     lib = gdr.load_library()
     assert lib.gdr_chunk_fwd(None, None) == gdr.GDR_ERR_NULL
@@ -170,7 +216,7 @@ def test_step_rejects_before_any_hip_call(kw, status):
 def test_struct_layout_matches_header(tmp_path):
     """Field offsets of the ctypes mirrors equal the C compiler's offsetof()."""
     fields = {"gdr_fwd_args": gdr.FwdArgs, "gdr_step_args": gdr.StepArgs,
-              "gdr_gate_args": gdr.GateArgs}
+              "gdr_gate_args": gdr.GateArgs, "gdr_bwd_args": gdr.BwdArgs}
     lines = ["#include <stdio.h>", "#include <stddef.h>", f'#include "{HEADER}"',
              "int main(void) {"]
     for cname, cls in fields.items():
@@ -302,6 +348,27 @@ def test_gated_binding_checks():
     a["theta"] = torch.zeros(2, 5, 3, 8)
     with pytest.raises(ValueError, match="theta"):
         gdr.gdr_chunk_fwd_gated(**a)
+
+
+def test_bwd_binding_checks():
+    """Good shapes pass every check (then the CPU device is refused); each bad
+    argument is named."""
+    import torch
+    bf, f32 = torch.bfloat16, torch.float32
+    B, T, H, d = 2, 5, 3, 8
+    good = dict(q=torch.zeros(B, T, H, d, dtype=bf), k=torch.zeros(B, T, H, d, dtype=bf),
+                v=torch.zeros(B, T, H, d, dtype=bf), alpha=torch.ones(B, T, H, d),
+                w=torch.zeros(B, T, H), beta=torch.zeros(B, T, H),
+                grad_o=torch.zeros(B, T, H, d, dtype=bf))
+    with pytest.raises(ValueError, match="GPU"):
+        gdr.gdr_chunk_bwd(**good)
+    for name, val in (("grad_o", torch.zeros(B, T, H, d)), ("alpha", torch.ones(B, T, H, 4)),
+                      ("q", torch.zeros(B, T, H, d)), ("beta", torch.zeros(B, T)),
+                      ("grad_S", torch.zeros(B, H, d, 4)), ("S0", torch.zeros(B, H, d, d, dtype=bf))):
+        a = dict(good)
+        a[name] = val
+        with pytest.raises(ValueError, match=name):
+            gdr.gdr_chunk_bwd(**a)
 
 
 def test_decode_binding_checks():
