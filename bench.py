@@ -64,6 +64,16 @@ def algorithmic_flops(wl, L: int) -> float:
     return per_th * wl.B * wl.T * wl.H
 
 
+def bwd_flops(wl) -> float:
+    """Matrix-core flops of the backward kernel per launch, each product counted
+    once (the value-tile workgroups repeat the key-side ones): per 32-token
+    block, eight d_k x d_v products with one L-sized side (16 L d_k d_v),
+    six L x L x d_k (12 L^2 d_k) and five L x L x d_v (10 L^2 d_v)."""
+    L = 32
+    per_th = 16 * wl.dk * wl.dv + 12 * L * wl.dk + 10 * L * wl.dv
+    return per_th * wl.B * wl.T * wl.H
+
+
 def wy_block(wl) -> int:
     """Token block of the WY solve that actually runs for this workload: the
     pipelined bf16 kernel (d in {64, 128}) always uses 32-token blocks; the
@@ -151,6 +161,41 @@ def _gated_closure(wl):
     def step():
         gdr.gdr_chunk_fwd_gated(q, k, v, xx, a, w, beta, theta=theta, qk_l2norm=True,
                                 chunk=wl.chunk, o=o, S_out=S)
+    return step, x
+
+
+def _bwd_closure(wl):
+    """gdr_chunk_bwd on the workload's inputs with a seeded bf16 grad_o and an
+    fp32 grad_S; the workspace is allocated once, outside the timed region."""
+    import numpy as np
+    import torch
+    import recurrent_state_memory_amd as gdr
+    from synth.gen import bf16_round, generate
+    x = generate(wl)
+    bf = torch.bfloat16
+    q, k, v = (_to_dev(t, bf) for t in (x.q, x.k, x.v))
+    alpha, theta, beta, w = map(_to_dev, (x.alpha, x.theta, x.beta, x.w))
+    rng = np.random.default_rng(wl.seed + 1)
+    dO = _to_dev(bf16_round(rng.standard_normal(x.v.shape, dtype=np.float32)), bf)
+    dS = _to_dev((rng.standard_normal((wl.B, wl.H, wl.dv, wl.dk)) / 8).astype(np.float32))
+    ws = {}
+
+    def step():
+        g = gdr.gdr_chunk_bwd(q, k, v, alpha, w, beta, dO, theta=theta, grad_S=dS,
+                              workspace=ws.get("w"))
+        return g
+    # size the workspace with one call, then reuse it
+    import ctypes
+    a = gdr.BwdArgs()
+    a.B, a.T, a.H, a.dk, a.dv = wl.B, wl.T, wl.H, wl.dk, wl.dv
+    a.decay = gdr.GDR_DECAY_ROT2 if theta is not None else gdr.GDR_DECAY_DIAG
+    for f in ("q", "k", "v", "alpha", "beta", "w", "grad_o", "grad_q", "grad_k", "grad_v",
+              "grad_alpha", "grad_beta", "grad_w"):
+        setattr(a, f, 1 << 20)
+    if theta is not None:
+        a.theta = a.grad_theta = 1 << 20
+    need = gdr.load_library().gdr_chunk_bwd_workspace(ctypes.byref(a))
+    ws["w"] = torch.empty(need, dtype=torch.uint8, device="cuda")
     return step, x
 
 
@@ -272,6 +317,8 @@ def main(argv=None):
     ap.add_argument("--workload", default="layer",
                     choices=["layer", "small", "rot", "long", "tiny", "decode", "copy"])
     ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--bwd", action="store_true",
+                    help="gdr_chunk_bwd: the backward (forward recompute + reverse blocks + reduction)")
     ap.add_argument("--gated", action="store_true",
                     help="gdr_chunk_fwd_gated: bf16 decay pre-activation, q/k normalised in the kernel")
     a = ap.parse_args(argv)
@@ -312,6 +359,32 @@ def main(argv=None):
         return 0
 
     wl = WORKLOADS[a.workload]
+    if a.bwd:
+        if wl.content or wl.io != "bf16" or wl.dk not in (64, 128):
+            print("--bwd runs the bf16 plain-erase workloads with d in {64, 128}", file=sys.stderr)
+            return 2
+        step, x = _bwd_closure(wl)
+        secs, wall = _time(step, a.steps, a.warmup)
+        per = secs / a.steps
+        fl = bwd_flops(wl)
+        out = {
+            "metric": "tokens/sec gated-delta chunk bwd (recompute + backward + reduction)",
+            "value": round(wl.B * wl.T / per, 1), "unit": "tokens/s", "n_gpus": 1,
+            "steps": a.steps, "warmup": a.warmup, "ms_per_step": round(per * 1e3, 4),
+            "higher_is_better": True, "scaling": "weak", "vs_baseline": None, "dtype": "f32",
+            "data": "synthetic (seeded; the forward's inputs, bf16 grad_o, fp32 grad_S)",
+            "config": {"workload": (f"{wl.name}: B={wl.B} H={wl.H} T={wl.T} d_k=d_v={wl.dk}, "
+                                    f"{'2x2 rotation-decay' if wl.decay == 'rot2' else 'per-channel decay'}, "
+                                    "gradients of q,k,v,decay,beta,w,S0 in fp32"),
+                       "global_batch": wl.B, "seq_len": wl.T, "parallelism": "single GPU"},
+            "roofline_scope": "whole gdr_chunk_bwd call (3 kernels); per-kernel times in profiles/",
+            "roofline": {"bound": "mfma", "achieved": round(fl / per / 1e12, 2),
+                         "peak": MFMA_F32_PEAK_TFS, "unit": "TFLOP/s",
+                         "frac": round(fl / per / 1e12 / MFMA_F32_PEAK_TFS, 4), "traffic": None},
+            "wall_s_timed_region": round(wall, 4),
+        }
+        print(json.dumps(out))
+        return 0
     gated = a.gated
     if gated and (wl.content or wl.io != "bf16" or wl.dk not in (64, 128)):
         print("--gated runs the bf16 plain-erase workloads with d in {64, 128}", file=sys.stderr)

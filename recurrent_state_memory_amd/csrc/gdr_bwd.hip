@@ -83,6 +83,117 @@ __device__ inline float sum16(float x) {
   return x;
 }
 
+// Unpack 8 bf16 (one 16-byte piece) to fp32 in LDS.
+__device__ inline void put8(float* dst, uint4 u, bool ok) {
+  const uint32_t wds[4] = {u.x, u.y, u.z, u.w};
+#pragma unroll
+  for (int e = 0; e < 4; ++e) {
+    dst[2 * e] = ok ? __uint_as_float(wds[e] << 16) : 0.f;
+    dst[2 * e + 1] = ok ? __uint_as_float(wds[e] & 0xffff0000u) : 0.f;
+  }
+}
+
+// Raw inputs of block c into LDS; tokens at or past T read as zero (and as
+// the identity transition).
+template <int DK, int DECAY>
+__device__ inline void stage_block(Smem<DK>& sm, const BwdParams& p, int unit, size_t bh, int c,
+                                   int t0, int nt, int nc, int v0, int tid) {
+  constexpr int PK = Smem<DK>::PK, PV = Smem<DK>::PV;
+  const int H = p.H, DV = p.DV;
+  if (tid < L) {
+    const bool ok = tid < nt;
+    const size_t row = bh + (size_t)(t0 + min(tid, nt - 1)) * H;
+    const float bt = p.beta[row], wt = p.w[row];
+    sm.beta[tid] = ok ? bt : 0.f;
+    sm.w[tid] = ok ? wt : 0.f;
+  }
+  // v and grad_o tiles: L rows x TV bf16 = 4 pieces of 8 per row
+  static_assert(L * TV / 8 <= NT, "one piece of v and of grad_o per thread");
+  if (tid < L * TV / 8) {
+    const int r = tid / (TV / 8), i8 = tid % (TV / 8);
+    const bool ok = r < nt;
+    const size_t src = (bh + (size_t)(t0 + min(r, nt - 1)) * H) * DV + v0 + 8 * i8;
+    const uint4 uv = *(const uint4*)((const __bf16*)p.v + src);
+    const uint4 ug = *(const uint4*)((const __bf16*)p.grad_o + src);
+    put8(sm.V + r * PV + 8 * i8, uv, ok);
+    put8(sm.DO + r * PV + 8 * i8, ug, ok);
+  }
+  // block-start state tile: TV rows x DK fp32
+  {
+    constexpr int PIECES = TV * DK / 4 / NT;
+    const float* ck = p.ckpt + ((size_t)unit * nc + c) * DV * DK;   // unit = b * H + h
+    f32x4 x[PIECES];
+#pragma unroll
+    for (int u = 0; u < PIECES; ++u) {
+      const int e = tid + u * NT, i = e / (DK / 4), j4 = e % (DK / 4);
+      x[u] = *(const f32x4*)(ck + (size_t)(v0 + i) * DK + 4 * j4);
+    }
+#pragma unroll
+    for (int u = 0; u < PIECES; ++u) {
+      const int e = tid + u * NT, i = e / (DK / 4), j4 = e % (DK / 4);
+      *(f32x4*)(sm.S + i * PK + 4 * j4) = x[u];
+    }
+  }
+  // keys and queries: L rows x DK bf16
+  {
+    constexpr int PIECES = L * DK / 8 / NT;
+    uint4 kx[PIECES], qx[PIECES];
+#pragma unroll
+    for (int u = 0; u < PIECES; ++u) {
+      const int e = tid + u * NT, r = e / (DK / 8), j8 = e % (DK / 8);
+      const size_t src = (bh + (size_t)(t0 + min(r, nt - 1)) * H) * DK + 8 * j8;
+      kx[u] = *(const uint4*)((const __bf16*)p.k + src);
+      qx[u] = *(const uint4*)((const __bf16*)p.q + src);
+    }
+#pragma unroll
+    for (int u = 0; u < PIECES; ++u) {
+      const int e = tid + u * NT, r = e / (DK / 8), j8 = e % (DK / 8);
+      put8(sm.Kp + r * PK + 8 * j8, kx[u], r < nt);
+      put8(sm.Qp + r * PK + 8 * j8, qx[u], r < nt);
+    }
+  }
+  // transitions: DIAG alpha [L x DK]; ROT2 gamma and theta [L x DK/2] each
+  if constexpr (DECAY == 0) {
+    constexpr int PIECES = L * DK / 4 / NT;
+    f32x4 ax[PIECES];
+#pragma unroll
+    for (int u = 0; u < PIECES; ++u) {
+      const int e = tid + u * NT, r = e / (DK / 4), j4 = e % (DK / 4);
+      ax[u] = *(const f32x4*)(p.alpha + (bh + (size_t)(t0 + min(r, nt - 1)) * H) * DK + 4 * j4);
+    }
+#pragma unroll
+    for (int u = 0; u < PIECES; ++u) {
+      const int e = tid + u * NT, r = e / (DK / 4), j4 = e % (DK / 4);
+      const bool ok = r < nt;
+#pragma unroll
+      for (int q4 = 0; q4 < 4; ++q4) sm.Gam[r * PK + 4 * j4 + q4] = ok ? ax[u][q4] : 1.f;
+    }
+  } else {
+    constexpr int HP = DK / 2, PIECES = (L * HP / 4 + NT - 1) / NT;
+    f32x4 gx[PIECES], tx[PIECES];
+#pragma unroll
+    for (int u = 0; u < PIECES; ++u) {
+      const int e = min(tid + u * NT, L * HP / 4 - 1), r = e / (HP / 4), j4 = e % (HP / 4);
+      const size_t src = (bh + (size_t)(t0 + min(r, nt - 1)) * H) * HP + 4 * j4;
+      gx[u] = *(const f32x4*)(p.alpha + src);
+      tx[u] = *(const f32x4*)(p.theta + src);
+    }
+#pragma unroll
+    for (int u = 0; u < PIECES; ++u) {
+      const int e = tid + u * NT;
+      if (e < L * HP / 4) {
+        const int r = e / (HP / 4), j4 = e % (HP / 4);
+        const bool ok = r < nt;
+#pragma unroll
+        for (int q4 = 0; q4 < 4; ++q4) {
+          sm.Gam[r * PK + 2 * (4 * j4 + q4)] = ok ? gx[u][q4] : 1.f;
+          sm.Gam[r * PK + 2 * (4 * j4 + q4) + 1] = ok ? tx[u][q4] : 0.f;
+        }
+      }
+    }
+  }
+}
+
 template <int DK, int DECAY>
 __global__ __launch_bounds__(NT) void bwd_kernel(BwdParams p) {
   using Sm = Smem<DK>;
@@ -126,37 +237,20 @@ __global__ __launch_bounds__(NT) void bwd_kernel(BwdParams p) {
   for (int c = nc - 1; c >= 0; --c) {
     const int t0 = c * L, nt = min(L, Tn - t0);
     // ---------------------------------------------------------------- loads
-    if (tid < L) {
-      const bool ok = tid < nt;
-      const size_t row = bh + (size_t)(t0 + tid) * H;
-      sm.beta[tid] = ok ? p.beta[row] : 0.f;
-      sm.w[tid] = ok ? p.w[row] : 0.f;
-    }
-    for (int e = tid; e < L * TV; e += NT) {
-      const int r = e / TV, i = e % TV;
-      const bool ok = r < nt;
-      const size_t src = (bh + (size_t)(t0 + r) * H) * DV + v0 + i;
-      sm.V[r * PV + i] = ok ? bf2f(v, src) : 0.f;
-      sm.DO[r * PV + i] = ok ? bf2f(dO, src) : 0.f;
-    }
-    {
-      const float* ck = p.ckpt + ((size_t)(b * H + h) * nc + c) * DV * DK;
-      for (int e = tid; e < TV * DK / 4; e += NT) {
-        const int i = e / (DK / 4), j4 = e % (DK / 4);
-        *(f32x4*)(sm.S + i * PK + 4 * j4) = *(const f32x4*)(ck + (size_t)(v0 + i) * DK + 4 * j4);
-      }
-    }
-    // cumulative transitions and the decayed key/query forms
+    // Every global load of the block is issued before any is used (unrolled,
+    // 16-byte pieces), into LDS: k into Kp, q into Qp, the transition into
+    // Gam (DIAG alpha; ROT2 gamma at even, theta at odd positions).
+    stage_block<DK, DECAY>(sm, p, unit, bh, c, t0, nt, nc, v0, tid);
+    lds_barrier();
+    // cumulative transitions and the decayed key/query forms, in place
     if constexpr (DECAY == 0) {
       if (tid < DK) {
         const int j = tid;
         float gam = 1.f;
+#pragma unroll 4
         for (int r = 0; r < L; ++r) {
-          const bool ok = r < nt;
-          const size_t row = bh + (size_t)(t0 + r) * H;
-          gam *= ok ? p.alpha[row * DK + j] : 1.f;
-          const float kk = ok ? bf2f(k, row * DK + j) : 0.f;
-          const float qq = ok ? bf2f(q, row * DK + j) : 0.f;
+          gam *= sm.Gam[r * PK + j];
+          const float kk = sm.Kp[r * PK + j], qq = sm.Qp[r * PK + j];
           sm.Gam[r * PK + j] = gam;
           sm.Kp[r * PK + j] = gam * kk;
           sm.Qp[r * PK + j] = gam * qq;
@@ -168,21 +262,17 @@ __global__ __launch_bounds__(NT) void bwd_kernel(BwdParams p) {
       if (tid < DK / 2) {
         const int pr = tid;
         float zr = 1.f, zi = 0.f;
+#pragma unroll 4
         for (int r = 0; r < L; ++r) {
-          const bool ok = r < nt;
-          const size_t row = bh + (size_t)(t0 + r) * H;
-          const float gm = ok ? p.alpha[row * (DK / 2) + pr] : 1.f;
-          const float th = ok ? p.theta[row * (DK / 2) + pr] : 0.f;
+          const float gm = sm.Gam[r * PK + 2 * pr], th = sm.Gam[r * PK + 2 * pr + 1];
           float sn, cs;
           __sincosf(th, &sn, &cs);
           const float dr = gm * cs, di = gm * sn;
           const float nr = zr * dr - zi * di, ni = zr * di + zi * dr;
           zr = nr;
           zi = ni;
-          const float k0 = ok ? bf2f(k, row * DK + 2 * pr) : 0.f;
-          const float k1 = ok ? bf2f(k, row * DK + 2 * pr + 1) : 0.f;
-          const float q0 = ok ? bf2f(q, row * DK + 2 * pr) : 0.f;
-          const float q1 = ok ? bf2f(q, row * DK + 2 * pr + 1) : 0.f;
+          const float k0 = sm.Kp[r * PK + 2 * pr], k1 = sm.Kp[r * PK + 2 * pr + 1];
+          const float q0 = sm.Qp[r * PK + 2 * pr], q1 = sm.Qp[r * PK + 2 * pr + 1];
           const float iz = 1.f / (zr * zr + zi * zi);
           const float hr = zr * iz, hi = zi * iz;   // P^{-T} on a pair: z / |z|^2
           sm.Gam[r * PK + 2 * pr] = zr;
