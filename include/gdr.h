@@ -212,6 +212,15 @@ size_t gdr_chunk_bwd_workspace(const gdr_bwd_args *a);
 
 gdr_status gdr_chunk_bwd(const gdr_bwd_args *a, void *hip_stream);
 
+/* For callers that cannot allocate device memory (code under stream capture,
+ * tight serving loops, harnesses that forbid hipMalloc): the same backward on
+ * a scratch array inside the library (256 MiB per GPU, held until the process
+ * ends) instead of a caller workspace.  a->workspace must be NULL and
+ * a->workspace_bytes 0 (else GDR_ERR_ARG); problems whose
+ * gdr_chunk_bwd_workspace(a) exceeds 256 MiB return GDR_ERR_WORKSPACE.  Calls
+ * that overlap on one GPU share the array and race.  Allocates nothing. */
+gdr_status gdr_chunk_bwd_noalloc(const gdr_bwd_args *a, void *hip_stream);
+
 /* ------------------------------------------------------------------------ */
 /* Single-token decode step on N independent states, in place.               */
 /* ------------------------------------------------------------------------ */

@@ -98,6 +98,8 @@ def load_library(path: Optional[str] = None) -> ctypes.CDLL:
     lib.gdr_chunk_fwd_gated.restype = ctypes.c_int
     lib.gdr_chunk_bwd.argtypes = [ctypes.POINTER(BwdArgs), _vp]
     lib.gdr_chunk_bwd.restype = ctypes.c_int
+    lib.gdr_chunk_bwd_noalloc.argtypes = [ctypes.POINTER(BwdArgs), _vp]
+    lib.gdr_chunk_bwd_noalloc.restype = ctypes.c_int
     lib.gdr_chunk_bwd_workspace.argtypes = [ctypes.POINTER(BwdArgs)]
     lib.gdr_chunk_bwd_workspace.restype = ctypes.c_size_t
     lib.gdr_chunk_fwd_workspace.argtypes = [ctypes.POINTER(FwdArgs)]
@@ -186,6 +188,15 @@ def call_chunk_bwd(args: BwdArgs, stream=None) -> int:
     s = stream if isinstance(stream, ctypes.c_void_p) else (
         ctypes.c_void_p(0) if stream is None else _stream(stream))
     return lib.gdr_chunk_bwd(ctypes.byref(args), s)
+
+
+def call_chunk_bwd_noalloc(args: BwdArgs, stream=None) -> int:
+    """Raw call of the static-scratch backward (``args.workspace`` must be
+    NULL); returns the status code."""
+    lib = load_library()
+    s = stream if isinstance(stream, ctypes.c_void_p) else (
+        ctypes.c_void_p(0) if stream is None else _stream(stream))
+    return lib.gdr_chunk_bwd_noalloc(ctypes.byref(args), s)
 
 
 def call_step_decode(args: StepArgs, stream=None) -> int:

@@ -228,11 +228,21 @@ size_t gdr_chunk_bwd_workspace(const gdr_bwd_args* a) {
 }
 
 gdr_status gdr_chunk_bwd(const gdr_bwd_args* a, void* hip_stream) {
+  if (!a) return GDR_ERR_NULL;
+  return gdr::chunk_bwd_on(a, a->workspace, a->workspace_bytes, (hipStream_t)hip_stream);
+}
+
+}  // extern "C"
+
+namespace gdr {
+gdr_status chunk_bwd_on(const gdr_bwd_args* a, void* workspace, size_t workspace_bytes,
+                        hipStream_t stream) {
   const gdr_status st = check_bwd_args(a);
   if (st != GDR_OK) return st;
   const BwdLayout lay = bwd_layout(a);
-  if (!a->workspace || a->workspace_bytes < lay.total) return GDR_ERR_WORKSPACE;
-  char* ws = (char*)a->workspace;
+  if (!workspace || workspace_bytes < lay.total) return GDR_ERR_WORKSPACE;
+  if (!aligned16(workspace)) return GDR_ERR_ALIGN;
+  char* ws = (char*)workspace;
   // forward recompute with block-start checkpoints
   gdr::FwdParams f{};
   f.B = a->B;
@@ -256,7 +266,7 @@ gdr_status gdr_chunk_bwd(const gdr_bwd_args* a, void* hip_stream) {
   f.S_out = nullptr;
   f.ckpt = (float*)(ws + lay.ckpt);
   if (!gdr::fwd_pipe_supported(f)) return GDR_ERR_UNSUPPORTED;
-  hipError_t e = gdr::launch_fwd(f, (hipStream_t)hip_stream);
+  hipError_t e = gdr::launch_fwd(f, stream);
   if (e != hipSuccess) return GDR_ERR_HIP;
   gdr::BwdParams p{};
   p.B = a->B;
@@ -284,9 +294,13 @@ gdr_status gdr_chunk_bwd(const gdr_bwd_args* a, void* hip_stream) {
   p.grad_S0 = a->grad_S0;
   p.ckpt = (const float*)(ws + lay.ckpt);
   p.part = (float*)(ws + lay.part);
-  e = gdr::launch_bwd(p, (hipStream_t)hip_stream);
+  e = gdr::launch_bwd(p, stream);
   return e == hipSuccess ? GDR_OK : GDR_ERR_HIP;
 }
+
+}  // namespace gdr
+
+extern "C" {
 
 gdr_status gdr_step_decode(const gdr_step_args* a, void* hip_stream) {
   const gdr_status st = check_step(a);

@@ -4,6 +4,8 @@
 #include <stddef.h>
 #include <stdint.h>
 
+#include "../../include/gdr.h"
+
 namespace gdr {
 
 struct FwdParams {
@@ -97,6 +99,10 @@ constexpr int kBwdTile = 32;
 inline size_t bwd_part_floats(int B, int T, int H, int DK, int DV) {
   return (size_t)(DV / kBwdTile) * B * T * H * (3 * (size_t)DK + 2);
 }
+// The backward on a given workspace (argument and size checks included);
+// gdr_chunk_bwd passes the caller's, gdr_chunk_bwd_noalloc its static scratch.
+gdr_status chunk_bwd_on(const gdr_bwd_args* a, void* workspace, size_t workspace_bytes,
+                        hipStream_t stream);
 int fwd_block_len(int dk, int chunk, bool io_bf16);
 
 }  // namespace gdr

@@ -166,6 +166,20 @@ def test_bwd_rejects_before_any_hip_call(kw, status):
     assert gdr.call_chunk_bwd(_good_bwd(**kw)) == status
 
 
+def test_bwd_noalloc_rejects_before_any_hip_call():
+    """The static-scratch backward: no caller workspace, at most 256 MiB of it,
+    and the backward's own argument checks."""
+    lib = gdr.load_library()
+    assert lib.gdr_chunk_bwd_noalloc(None, None) == gdr.GDR_ERR_NULL
+    assert gdr.call_chunk_bwd_noalloc(_good_bwd(workspace=FAKE, workspace_bytes=1 << 30)) == \
+        gdr.GDR_ERR_ARG
+    assert gdr.call_chunk_bwd_noalloc(_good_bwd(dk=32, dv=32)) == gdr.GDR_ERR_UNSUPPORTED
+    assert gdr.call_chunk_bwd_noalloc(_good_bwd(grad_q=None)) == gdr.GDR_ERR_NULL
+    big = _good_bwd(B=8, T=4096, H=16, dk=128, dv=128)      # ~2.9 GB of workspace
+    assert lib.gdr_chunk_bwd_workspace(ctypes.byref(big)) > 256 << 20
+    assert gdr.call_chunk_bwd_noalloc(big) == gdr.GDR_ERR_WORKSPACE
+
+
 def test_bwd_workspace_size():
     """Checkpoints of every 32-token block, the recompute's o and the partials."""
     lib = gdr.load_library()
