@@ -51,6 +51,13 @@ def transition_matrix(decay, alpha_t, theta_t, dk):
     D = np.zeros((dk, dk))
     for j in range(dk // 2):
         c, s, g = np.cos(theta_t[j]), np.sin(theta_t[j]), alpha_t[j]
+        if decay == "dihedral" and np.signbit(g):   # reflection |g| R(theta) F, F = Diag(1, -1)
+            g = -g
+            D[2 * j, 2 * j] = g * c
+            D[2 * j, 2 * j + 1] = g * s
+            D[2 * j + 1, 2 * j] = g * s
+            D[2 * j + 1, 2 * j + 1] = -g * c
+            continue
         D[2 * j, 2 * j] = g * c
         D[2 * j, 2 * j + 1] = -g * s
         D[2 * j + 1, 2 * j] = g * s

@@ -62,14 +62,19 @@ def transition(S: np.ndarray, decay: str, alpha_t: np.ndarray,
     rot2: D_t = direct sum over j of gamma_j [[c_j, -s_j], [s_j, c_j]] on key
           channels (2j, 2j+1), gamma = alpha_t [..., d_k/2], c/s of theta_t
           (SFDA core architecture: 2x2 rotation-decay blocks).
+    dihedral: as rot2, except that a block whose gamma has its sign bit set is
+          the reflection |gamma| [[c, s], [s, -c]] = |gamma| R(theta) F with
+          F = Diag(1, -1) (SFDA finite-state expressivity: with reflections
+          the family realises dihedral phase-orientation memory).  Products
+          of such blocks do not commute.
     """
     if decay == "diag":
         return S * alpha_t[..., None, :]
-    if decay != "rot2":
+    if decay not in ("rot2", "dihedral"):
         raise ValueError(decay)
     c = np.cos(theta_t)[..., None, :]
     s = np.sin(theta_t)[..., None, :]
-    g = alpha_t[..., None, :]
+    g = np.abs(alpha_t)[..., None, :] if decay == "dihedral" else alpha_t[..., None, :]
     even = S[..., 0::2]
     odd = S[..., 1::2]
     X = np.empty_like(S)
@@ -77,6 +82,9 @@ def transition(S: np.ndarray, decay: str, alpha_t: np.ndarray,
     # (S D)[:, 2j+1] = S[:, 2j] D[2j, 2j+1] + S[:, 2j+1] D[2j+1, 2j+1]
     X[..., 0::2] = g * (c * even + s * odd)
     X[..., 1::2] = g * (-s * even + c * odd)
+    if decay == "dihedral":
+        refl = np.signbit(alpha_t)[..., None, :]
+        X[..., 1::2] = np.where(refl, g * (s * even - c * odd), X[..., 1::2])
     return X
 
 

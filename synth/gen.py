@@ -91,7 +91,7 @@ class Workload:
     dv: int
     chunk: int
     io: str            # "f32" | "bf16"
-    decay: str         # "diag" | "rot2"
+    decay: str         # "diag" | "rot2" | "dihedral" (rot2 with reflection blocks)
     content: bool      # content-aware erase
     seed: int
     rank: int = 16     # low-rank width of the erase projection
@@ -112,6 +112,8 @@ WORKLOADS = {
     "long": Workload("long", 1, 16, 32768, 128, 128, 128, "bf16", "diag", True, 3),
     "rot": Workload("rot", 4, 16, 8192, 128, 128, 64, "bf16", "rot2", False, 4,
                     decay_scale=0.05),
+    "dihedral": Workload("dihedral", 4, 16, 8192, 128, 128, 64, "bf16", "dihedral", False, 5,
+                         decay_scale=0.05),
 }
 
 DECODE_N = 256
@@ -160,6 +162,9 @@ def generate(wl: Workload, T: Optional[int] = None, B: Optional[int] = None,
     else:
         theta = rng.uniform(-math.pi, math.pi, (Bn, Tn, H, dk // 2)).astype(np.float32)
         a_noise = rng.standard_normal((Bn, Tn, H, dk // 2), dtype=np.float32)
+    refl = None
+    if wl.decay == "dihedral":   # each block a reflection with probability 1/2
+        refl = rng.uniform(0.0, 1.0, (Bn, Tn, H, dk // 2)) < 0.5
     ub_down = ub_up = None
     if wl.content:
         ub_down = (rng.standard_normal((H, wl.rank, dv), dtype=np.float32)
@@ -171,6 +176,8 @@ def generate(wl: Workload, T: Optional[int] = None, B: Optional[int] = None,
     k = _io_cast(_l2_normalise(k), wl.io)
     v = _io_cast(v, wl.io)
     alpha = np.exp(np.float32(-wl.decay_scale) * _softplus(a_noise)).astype(np.float32)
+    if refl is not None:   # a reflection block carries its magnitude with the sign bit set
+        alpha = np.where(refl, -alpha, alpha).astype(np.float32)
     w = _sigmoid(w_logit)
     if wl.content:
         beta, beta_logit = None, b_logit
@@ -220,6 +227,8 @@ def generate_decode(wl: Workload = WORKLOADS["rot"], N: int = DECODE_N,
         else:
             rng.uniform(-math.pi, math.pi, (Bn, Tn, H, dk // 2))
             rng.standard_normal((Bn, Tn, H, dk // 2), dtype=np.float32)
+            if wl.decay == "dihedral":
+                rng.uniform(0.0, 1.0, (Bn, Tn, H, dk // 2))
     S = (rng.standard_normal((N, H, dv, dk), dtype=np.float32)
          / np.float32(math.sqrt(dk))).astype(np.float32)
     q = rng.standard_normal((N, H, dk), dtype=np.float32)
@@ -228,18 +237,22 @@ def generate_decode(wl: Workload = WORKLOADS["rot"], N: int = DECODE_N,
     b_logit = rng.standard_normal((N, H), dtype=np.float32)
     w_logit = rng.standard_normal((N, H), dtype=np.float32)
     theta = None
+    refl = None
     if wl.decay == "diag":
         a_noise = rng.standard_normal((N, H, dk), dtype=np.float32)
     else:
         theta = rng.uniform(-math.pi, math.pi, (N, H, dk // 2)).astype(np.float32)
         a_noise = rng.standard_normal((N, H, dk // 2), dtype=np.float32)
+        if wl.decay == "dihedral":
+            refl = rng.uniform(0.0, 1.0, (N, H, dk // 2)) < 0.5
     io = wl.io
+    alpha = np.exp(np.float32(-wl.decay_scale) * _softplus(a_noise)).astype(np.float32)
+    if refl is not None:
+        alpha = np.where(refl, -alpha, alpha).astype(np.float32)
     return DecodeInputs(
         N, H, dk, dv, io, wl.decay, S,
         _io_cast(_l2_normalise(q), io), _io_cast(_l2_normalise(k), io), _io_cast(v, io),
-        _sigmoid(b_logit), _sigmoid(w_logit),
-        np.exp(np.float32(-wl.decay_scale) * _softplus(a_noise)).astype(np.float32),
-        theta)
+        _sigmoid(b_logit), _sigmoid(w_logit), alpha, theta)
 
 
 @dataclasses.dataclass

@@ -497,3 +497,88 @@ def test_forward_gated_matches_explicit_inputs():
     o2, _ = seq.forward(qu, ku, v, w, np.full((B, T, H, dk // 2), 0.5), beta=beta, theta=th,
                         decay="rot2")
     np.testing.assert_allclose(o1, o2, rtol=0, atol=1e-6)
+
+
+# ----------------------------------------------------------------------------
+# Reflection blocks (dihedral memory; SFDA technical summary, finite-state
+# expressivity: "with reflections" the family realises dihedral phase-
+# orientation memory).  Pinned against the group law of D_n, not the matrices.
+# ----------------------------------------------------------------------------
+def _dihedral_apply(a_b_seq, n):
+    """Fold (a, b) pairs (rotation index, reflection bit) by the D_n law
+    (a1, b1)(a2, b2) = (a1 + (-1)^b1 a2 mod n, b1 xor b2), left to right."""
+    a, b = 0, 0
+    for a2, b2 in a_b_seq:
+        a, b = (a + (-a2 if b else a2)) % n, b ^ b2
+    return a, b
+
+
+def _dihedral_matrix(a, b, n):
+    """M(a, b) = R(2 pi a / n) F^b acting on the right of a row pair, with
+    R(phi) = [[cos, -sin], [sin, cos]] and F = Diag(1, -1)."""
+    ph = 2 * np.pi * a / n
+    R = np.array([[np.cos(ph), -np.sin(ph)], [np.sin(ph), np.cos(ph)]])
+    return R @ (np.diag([1.0, -1.0]) if b else np.eye(2))
+
+
+@pytest.mark.parametrize("n", [3, 5, 8])
+def test_dihedral_memory_follows_the_group_law(n):
+    """With beta = 0 the state of each key pair is S0 times the product of the
+    tokens' D_n elements; the oracle must agree with the group law folded by
+    hand (a wrong reflection matrix or a swapped product order fails for the
+    non-abelian D_n, n >= 3)."""
+    rng = np.random.default_rng(n)
+    B, T, H, dk, dv = 1, 40, 1, 6, 3
+    a_idx = rng.integers(0, n, (T, dk // 2))
+    b_bit = rng.integers(0, 2, (T, dk // 2))
+    theta = (2 * np.pi * a_idx / n)[None, :, None, :]
+    gam = np.where(b_bit == 1, -1.0, 1.0)[None, :, None, :]
+    S0 = rng.standard_normal((B, H, dv, dk))
+    z = np.zeros((B, T, H))
+    q = rng.standard_normal((B, T, H, dk))
+    k = rng.standard_normal((B, T, H, dk))
+    v = rng.standard_normal((B, T, H, dv))
+    _, S = seq.forward(q, k, v, z, gam, beta=z, theta=theta, decay="dihedral", S0=S0)
+    for j in range(dk // 2):
+        a, b = _dihedral_apply(list(zip(a_idx[:, j], b_bit[:, j])), n)
+        want = S0[0, 0][:, 2 * j:2 * j + 2] @ _dihedral_matrix(a, b, n)
+        assert np.allclose(S[0, 0][:, 2 * j:2 * j + 2], want, atol=1e-12)
+
+
+def test_dihedral_reflection_is_an_involution_and_does_not_commute():
+    """Two equal reflections give |gamma|^2 S0; a rotation then a reflection
+    differs from the reverse order."""
+    rng = np.random.default_rng(3)
+    S0 = rng.standard_normal((1, 1, 2, 2))
+    z = np.zeros((1, 2, 1))
+    qkv = rng.standard_normal((1, 2, 1, 2))
+
+    def run(gam, th):
+        g = np.asarray(gam, np.float64).reshape(1, 2, 1, 1)
+        t = np.asarray(th, np.float64).reshape(1, 2, 1, 1)
+        return seq.forward(qkv, qkv, qkv, z, g, beta=z, theta=t, decay="dihedral", S0=S0)[1]
+    assert np.allclose(run([-0.5, -0.5], [0.7, 0.7]), 0.25 * S0, atol=1e-14)
+    a = run([0.9, -0.9], [0.7, 0.2])
+    b = run([-0.9, 0.9], [0.2, 0.7])
+    assert not np.allclose(a, b)
+
+
+@pytest.mark.parametrize("L", [1, 3, 8, 16])
+def test_dihedral_chunked_equals_sequential(L):
+    """Brute force: the chunk-WY algebra with dense, non-commuting transition
+    products equals the token recurrence (random magnitudes, angles and
+    reflection signs, writes on, ragged tail, S0 != 0)."""
+    from oracle import chunk
+    rng = np.random.default_rng(10 + L)
+    B, T, H, dk, dv = 2, 21, 2, 4, 3
+    q = rng.standard_normal((B, T, H, dk)) * 0.5
+    k = rng.standard_normal((B, T, H, dk)) * 0.5
+    v = rng.standard_normal((B, T, H, dv))
+    w = rng.uniform(0.2, 1.0, (B, T, H))
+    beta = rng.uniform(0.1, 0.9, (B, T, H))
+    gam = rng.uniform(0.7, 1.0, (B, T, H, dk // 2)) * np.where(rng.uniform(size=(B, T, H, dk // 2)) < 0.5, -1, 1)
+    theta = rng.uniform(-np.pi, np.pi, (B, T, H, dk // 2))
+    S0 = rng.standard_normal((B, H, dv, dk)) * 0.3
+    o1, S1 = seq.forward(q, k, v, w, gam, beta=beta, theta=theta, decay="dihedral", S0=S0)
+    o2, S2 = chunk.forward(q, k, v, w, gam, beta=beta, theta=theta, decay="dihedral", S0=S0, chunk=L)
+    assert np.max(np.abs(o1 - o2)) < 1e-10 and np.max(np.abs(S1 - S2)) < 1e-10
