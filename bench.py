@@ -16,7 +16,7 @@ kernel (algorithmic bytes per launch / measured launch time, against the HBM
 peak) and a CPU baseline: the fp64 oracle timed on a bounded sample of the
 same workload on this host.
 
-Other workloads (``--workload small|rot|long|decode|copy``) are for profiling
+Other workloads (``--workload small|rot|dihedral|long|decode|copy``) are for profiling
 and are not the reported metric; ``copy`` is a plain device copy of known size
 used to calibrate the HBM byte counters.
 """
@@ -141,7 +141,8 @@ def _fwd_closure(wl):
 
     def step():
         gdr.gdr_chunk_fwd(q, k, v, alpha, w, beta, theta=theta, chunk=wl.chunk, o=o,
-                          S_out=S, beta_logit=bl, ub_down=ud, ub_up=uu)
+                          S_out=S, beta_logit=bl, ub_down=ud, ub_up=uu,
+                          reflections=wl.decay == "dihedral")
     return step, x
 
 
@@ -315,7 +316,7 @@ def main(argv=None):
     ap.add_argument("--steps", type=int, default=200)
     ap.add_argument("--warmup", type=int, default=150)
     ap.add_argument("--workload", default="layer",
-                    choices=["layer", "small", "rot", "long", "tiny", "decode", "copy"])
+                    choices=["layer", "small", "rot", "dihedral", "long", "tiny", "decode", "copy"])
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--bwd", action="store_true",
                     help="gdr_chunk_bwd: the backward (forward recompute + reverse blocks + reduction)")
@@ -360,8 +361,9 @@ def main(argv=None):
 
     wl = WORKLOADS[a.workload]
     if a.bwd:
-        if wl.content or wl.io != "bf16" or wl.dk not in (64, 128):
-            print("--bwd runs the bf16 plain-erase workloads with d in {64, 128}", file=sys.stderr)
+        if wl.content or wl.io != "bf16" or wl.dk not in (64, 128) or wl.decay == "dihedral":
+            print("--bwd runs the bf16 plain-erase workloads with d in {64, 128} "
+                  "(no reflection blocks)", file=sys.stderr)
             return 2
         step, x = _bwd_closure(wl)
         secs, wall = _time(step, a.steps, a.warmup)
@@ -386,7 +388,8 @@ def main(argv=None):
         print(json.dumps(out))
         return 0
     gated = a.gated
-    if gated and (wl.content or wl.io != "bf16" or wl.dk not in (64, 128)):
+    if gated and (wl.content or wl.io != "bf16" or wl.dk not in (64, 128)
+                  or wl.decay == "dihedral"):
         print("--gated runs the bf16 plain-erase workloads with d in {64, 128}", file=sys.stderr)
         return 2
     step, x = _gated_closure(wl) if gated else _fwd_closure(wl)
@@ -425,8 +428,9 @@ def main(argv=None):
                          + (f"{wl.io} q/k/v, fp32 gates and state, " if not gated else
                             "gated: bf16 raw q/k (L2-normalised in the kernel), bf16 v, bf16 decay "
                             "pre-activation exp(-a softplus(x)), fp32 beta/w/state, ")
-                         + f"{'2x2 rotation-decay' if wl.decay == 'rot2' else 'per-channel decay'}"
-                         f"{', content-aware erase' if wl.content else ''}"),
+                         + {"rot2": "2x2 rotation-decay", "diag": "per-channel decay",
+                            "dihedral": "2x2 rotation/reflection blocks (dihedral)"}[wl.decay]
+                         + (", content-aware erase" if wl.content else "")),
             "global_batch": wl.B, "seq_len": wl.T, "parallelism": "single GPU",
         },
         "roofline": {
@@ -443,7 +447,7 @@ def main(argv=None):
         },
         "wall_s_timed_region": round(wall, 4),
     }
-    if not a.no_cpu_baseline and a.workload in ("layer", "small", "rot", "tiny"):
+    if not a.no_cpu_baseline and a.workload in ("layer", "small", "rot", "dihedral", "tiny"):
         out["cpu_baseline"] = cpu_baseline(wl, x, gated=gated)
     print(json.dumps(out))
     return 0

@@ -30,6 +30,15 @@
  *       GDR_DECAY_ROT2  D_t = direct sum over j < d_k/2 of
  *                       gamma_{t,j} [[cos th, -sin th], [sin th, cos th]]
  *                       acting on key channels (2j, 2j+1), th = theta_{t,j}.
+ *       GDR_DECAY_DIHEDRAL  as ROT2, except that a block whose gamma has its
+ *                       sign bit set is the reflection
+ *                       |gamma| [[cos th, sin th], [sin th, -cos th]]
+ *                       (SFDA technical summary, finite-state expressivity:
+ *                       with reflections the family realises dihedral
+ *                       memory).  Products of such blocks do not commute.
+ *                       Forward: bf16 io, d_k = d_v in {64, 128}, plain erase
+ *                       (else GDR_ERR_UNSUPPORTED); decode: every size.  No
+ *                       gated or backward variant.
  *
  * Conventions for every entry point:
  *   - All pointers are DEVICE pointers (hipMalloc / torch CUDA tensors), owned
@@ -45,7 +54,7 @@
  *   - NaN / Inf inputs are not checked; they propagate.
  *   - Calls on different streams touching disjoint outputs may overlap.
  *
- * Decay range.  Every decay factor (alpha, or the rotation magnitude gamma)
+ * Decay range.  Every decay factor (alpha, or the block magnitude |gamma|)
  * may take any value in [0, 1], including 0 (a full reset of that key channel,
  * the register/reset construction of the SFDA technical summary, finite-state
  * expressivity) and subnormals.  The chunked kernels pair Gamma_r k with
@@ -80,7 +89,7 @@ typedef enum {
 } gdr_status;
 
 typedef enum { GDR_F32 = 0, GDR_BF16 = 1 } gdr_dtype;        /* q, k, v and o */
-typedef enum { GDR_DECAY_DIAG = 0, GDR_DECAY_ROT2 = 1 } gdr_decay;
+typedef enum { GDR_DECAY_DIAG = 0, GDR_DECAY_ROT2 = 1, GDR_DECAY_DIHEDRAL = 2 } gdr_decay;
 
 /* ------------------------------------------------------------------------ */
 /* Chunked forward over a sequence.                                          */

@@ -26,7 +26,7 @@ LIB_PATH = os.path.join(_HERE, "libgdr.so")
 GDR_OK, GDR_ERR_NULL, GDR_ERR_SHAPE, GDR_ERR_DTYPE, GDR_ERR_UNSUPPORTED, \
     GDR_ERR_ALIGN, GDR_ERR_WORKSPACE, GDR_ERR_HIP, GDR_ERR_ARG = range(9)
 GDR_F32, GDR_BF16 = 0, 1
-GDR_DECAY_DIAG, GDR_DECAY_ROT2 = 0, 1
+GDR_DECAY_DIAG, GDR_DECAY_ROT2, GDR_DECAY_DIHEDRAL = 0, 1, 2
 ABI_VERSION = 1
 
 _vp = ctypes.c_void_p
@@ -206,14 +206,24 @@ def call_step_decode(args: StepArgs, stream=None) -> int:
     return lib.gdr_step_decode(ctypes.byref(args), s)
 
 
+def _decay_kind(rot, reflections):
+    if reflections and not rot:
+        raise ValueError("gdr: reflection blocks need theta (2x2 blocks)")
+    if reflections:
+        return GDR_DECAY_DIHEDRAL
+    return GDR_DECAY_ROT2 if rot else GDR_DECAY_DIAG
+
+
 def gdr_chunk_fwd(q, k, v, alpha, w, beta=None, *, theta=None, S0=None, chunk=64,
                   o=None, S_out=None, return_state=True, beta_logit=None,
-                  ub_down=None, ub_up=None, m_carry=None, stream=None):
+                  ub_down=None, ub_up=None, m_carry=None, reflections=False, stream=None):
     """Chunked gated delta-rule forward (see ``gdr_chunk_fwd`` in include/gdr.h).
 
     q, k [B,T,H,dk], v [B,T,H,dv] (bf16 or fp32, same dtype); alpha fp32
     [B,T,H,dk] (per-channel decay) or [B,T,H,dk/2] with ``theta`` (2x2
-    rotation-decay blocks); beta, w fp32 [B,T,H].  Content-aware erase: pass
+    rotation-decay blocks); beta, w fp32 [B,T,H].  ``reflections=True`` (with
+    ``theta``) makes a block whose alpha is negative (sign bit set) the
+    reflection of magnitude |alpha| (GDR_DECAY_DIHEDRAL).  Content-aware erase: pass
     ``beta_logit``, ``ub_down`` [H,r,dv], ``ub_up`` [H,r] instead of ``beta``.
     Returns (o [B,T,H,dv], S_out [B,H,dv,dk] fp32 or None).
 
@@ -262,7 +272,7 @@ def gdr_chunk_fwd(q, k, v, alpha, w, beta=None, *, theta=None, S0=None, chunk=64
     a = FwdArgs()
     a.B, a.T, a.H, a.dk, a.dv, a.chunk = B, T, H, dk, dv, chunk
     a.io_dtype = _io(q)
-    a.decay = GDR_DECAY_ROT2 if rot else GDR_DECAY_DIAG
+    a.decay = _decay_kind(rot, reflections)
     a.q, a.k, a.v, a.alpha, a.theta = map(_ptr, (q, k, v, alpha, theta))
     a.beta, a.w, a.beta_logit = map(_ptr, (beta, w, beta_logit))
     a.ub_down, a.ub_up, a.m_carry = map(_ptr, (ub_down, ub_up, m_carry))
@@ -389,11 +399,13 @@ def gdr_chunk_bwd(q, k, v, alpha, w, beta, grad_o, *, theta=None, S0=None, grad_
     return g
 
 
-def gdr_step_decode(S, q, k, v, alpha, beta, w, *, theta=None, o=None, stream=None):
+def gdr_step_decode(S, q, k, v, alpha, beta, w, *, theta=None, o=None, reflections=False,
+                    stream=None):
     """One token on N states in place (see ``gdr_step_decode`` in include/gdr.h).
 
     S [N,H,dv,dk] fp32 (overwritten), q,k [N,H,dk], v [N,H,dv], alpha [N,H,dk]
-    or gamma [N,H,dk/2] with theta, beta, w [N,H].  Returns o [N,H,dv].
+    or gamma [N,H,dk/2] with theta, beta, w [N,H]; ``reflections`` as in
+    ``gdr_chunk_fwd``.  Returns o [N,H,dv].
     Every tensor's shape, dtype and contiguity is checked first.
     """
     import torch
@@ -419,7 +431,7 @@ def gdr_step_decode(S, q, k, v, alpha, beta, w, *, theta=None, o=None, stream=No
     a = StepArgs()
     a.N, a.H, a.dk, a.dv = N, H, dk, dv
     a.io_dtype = _io(q)
-    a.decay = GDR_DECAY_ROT2 if rot else GDR_DECAY_DIAG
+    a.decay = _decay_kind(rot, reflections)
     a.q, a.k, a.v, a.alpha, a.theta = map(_ptr, (q, k, v, alpha, theta))
     a.beta, a.w, a.S, a.o = map(_ptr, (beta, w, S, o))
     _check(call_step_decode(a, _stream(stream)))

@@ -15,10 +15,12 @@ bool supported_d(int d) { return d == 32 || d == 64 || d == 128; }
 
 bool supported_chunk(int c) { return c == 16 || c == 32 || c == 64 || c == 128; }
 
+bool block_decay(int d) { return d == GDR_DECAY_ROT2 || d == GDR_DECAY_DIHEDRAL; }
+
 gdr_status check_fwd(const gdr_fwd_args* a) {
   if (!a) return GDR_ERR_NULL;
   if (a->io_dtype != GDR_F32 && a->io_dtype != GDR_BF16) return GDR_ERR_DTYPE;
-  if (a->decay != GDR_DECAY_DIAG && a->decay != GDR_DECAY_ROT2) return GDR_ERR_DTYPE;
+  if (a->decay != GDR_DECAY_DIAG && !block_decay(a->decay)) return GDR_ERR_DTYPE;
   if (a->B <= 0 || a->T <= 0 || a->H <= 0 || a->dk <= 0 || a->dv <= 0 || a->chunk <= 0)
     return GDR_ERR_SHAPE;
   if (!supported_d(a->dk) || a->dv != a->dk) return GDR_ERR_UNSUPPORTED;
@@ -40,11 +42,16 @@ gdr_status check_fwd(const gdr_fwd_args* a) {
     if (!a->beta) return GDR_ERR_NULL;
     if (a->ub_down || a->ub_up || a->m_carry) return GDR_ERR_ARG;
   }
-  if (a->decay == GDR_DECAY_ROT2) {
+  if (block_decay(a->decay)) {
     if (!a->theta) return GDR_ERR_NULL;
   } else if (a->theta) {
     return GDR_ERR_ARG;
   }
+  // reflection blocks: the pipelined kernel's plain launch only
+  if (a->decay == GDR_DECAY_DIHEDRAL &&
+      (a->io_dtype != GDR_BF16 || (a->dk != 64 && a->dk != 128) || content ||
+       (long long)a->T * a->H >= (1LL << 29) / a->dk))
+    return GDR_ERR_UNSUPPORTED;
   const void* vec[] = {a->q, a->k, a->v, a->alpha, a->theta, a->o, a->S0, a->S_out};
   for (const void* p : vec)
     if (p && !aligned16(p)) return GDR_ERR_ALIGN;
@@ -62,13 +69,13 @@ gdr_status check_fwd(const gdr_fwd_args* a) {
 gdr_status check_step(const gdr_step_args* a) {
   if (!a) return GDR_ERR_NULL;
   if (a->io_dtype != GDR_F32 && a->io_dtype != GDR_BF16) return GDR_ERR_DTYPE;
-  if (a->decay != GDR_DECAY_DIAG && a->decay != GDR_DECAY_ROT2) return GDR_ERR_DTYPE;
+  if (a->decay != GDR_DECAY_DIAG && !block_decay(a->decay)) return GDR_ERR_DTYPE;
   if (a->N <= 0 || a->H <= 0 || a->dk <= 0 || a->dv <= 0) return GDR_ERR_SHAPE;
   if ((long long)a->N * a->H >= (1LL << 31)) return GDR_ERR_SHAPE;
   if (!supported_d(a->dk) || a->dv != a->dk) return GDR_ERR_UNSUPPORTED;
   if (!a->q || !a->k || !a->v || !a->alpha || !a->beta || !a->w || !a->S || !a->o)
     return GDR_ERR_NULL;
-  if (a->decay == GDR_DECAY_ROT2) {
+  if (block_decay(a->decay)) {
     if (!a->theta) return GDR_ERR_NULL;
   } else if (a->theta) {
     return GDR_ERR_ARG;
@@ -143,6 +150,7 @@ gdr_status check_gated(const gdr_fwd_args* a, const gdr_gate_args* g) {
   if (a->io_dtype != GDR_BF16) return GDR_ERR_UNSUPPORTED;
   if (a->dk != 64 && a->dk != 128) return GDR_ERR_UNSUPPORTED;
   if (a->beta_logit) return GDR_ERR_UNSUPPORTED;
+  if (a->decay == GDR_DECAY_DIHEDRAL) return GDR_ERR_UNSUPPORTED;
   // 32-bit byte offsets of the kernel's buffer resources (T * H * dk < 2^29)
   if ((long long)a->T * a->H >= (1LL << 29) / a->dk) return GDR_ERR_UNSUPPORTED;
   if ((reinterpret_cast<uintptr_t>(g->decay_a) & 3u) != 0) return GDR_ERR_ALIGN;
@@ -171,9 +179,10 @@ BwdLayout bwd_layout(const gdr_bwd_args* a) {
 // Everything but the workspace size.
 gdr_status check_bwd_args(const gdr_bwd_args* a) {
   if (!a) return GDR_ERR_NULL;
-  if (a->decay != GDR_DECAY_DIAG && a->decay != GDR_DECAY_ROT2) return GDR_ERR_DTYPE;
+  if (a->decay != GDR_DECAY_DIAG && !block_decay(a->decay)) return GDR_ERR_DTYPE;
   if (a->B <= 0 || a->T <= 0 || a->H <= 0 || a->dk <= 0 || a->dv <= 0) return GDR_ERR_SHAPE;
   if ((a->dk != 64 && a->dk != 128) || a->dv != a->dk) return GDR_ERR_UNSUPPORTED;
+  if (a->decay == GDR_DECAY_DIHEDRAL) return GDR_ERR_UNSUPPORTED;
   if ((long long)a->B * a->T >= (1LL << 31)) return GDR_ERR_SHAPE;
   // 32-bit byte offsets of the forward's buffer resources (T * H * dk < 2^29)
   if ((long long)a->T * a->H >= (1LL << 29) / a->dk) return GDR_ERR_UNSUPPORTED;

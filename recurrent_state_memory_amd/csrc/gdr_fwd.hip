@@ -712,7 +712,8 @@ static hipError_t pick_variant(const FwdParams& p, hipStream_t s) {
 
 hipError_t launch_fwd(const FwdParams& p, hipStream_t stream) {
   if (fwd_pipe_supported(p)) return launch_fwd_pipe(p, stream);
-  if (p.gmode != 0) return hipErrorInvalidValue;   // the gated forward runs only pipelined
+  // the gated forward and reflection blocks run only pipelined
+  if (p.gmode != 0 || p.decay == 2) return hipErrorInvalidValue;
   if (p.io_bf16) return pick_variant<__bf16>(p, stream);
   return pick_variant<float>(p, stream);
 }

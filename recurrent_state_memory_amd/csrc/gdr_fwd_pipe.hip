@@ -43,6 +43,27 @@ __device__ inline f32x2 cmul(f32x2 a, f32x2 b) {
 }
 __device__ inline f32x2 conj(f32x2 a) { return f32x2{a.x, -a.y}; }
 
+// Rotation and reflection blocks (DECAY == 2).  A block acts on a key pair,
+// as a complex number x, by x -> w x (rotation-scale) or x -> w conj(x)
+// (reflection-scale, |gamma| R(theta) Diag(1, -1)); such maps compose as
+// (w1, s1) o (w2, s2) = (w1 c^s1(w2), s1 xor s2) and do not commute.  The
+// reflection bit s travels in the lowest mantissa bit of w.x (a 2^-24 relative
+// perturbation, far below the bf16 operands), so a map is still one f32x2.
+__device__ inline unsigned refl_bit(f32x2 m) { return __float_as_uint(m.x) & 1u; }
+__device__ inline f32x2 with_refl(f32x2 w, unsigned s) {
+  return f32x2{__uint_as_float((__float_as_uint(w.x) & ~1u) | s), w.y};
+}
+// f o g: apply g first
+__device__ inline f32x2 compose(f32x2 f, f32x2 g) {
+  const unsigned sf = refl_bit(f), sg = refl_bit(g);
+  const f32x2 fw = with_refl(f, 0u), gw = with_refl(g, 0u);
+  return with_refl(cmul(fw, sf ? conj(gw) : gw), sf ^ sg);
+}
+// the map applied to a key pair (column action)
+__device__ inline f32x2 apply_map(f32x2 m, f32x2 x) {
+  return cmul(with_refl(m, 0u), refl_bit(m) ? conj(x) : x);
+}
+
 __device__ inline f32x2 bf2_to_f2(uint32_t u) {
   return f32x2{__uint_as_float(u << 16), __uint_as_float(u & 0xffff0000u)};
 }
@@ -385,16 +406,27 @@ __device__ __forceinline__ void prep_chunk(Shared<DK, TV>& sh, const RawT<DK, TV
       d[r].y = ok ? ain[r].y : (DECAY == 0 ? 1.f : 0.f);
     }
   }
-  if constexpr (DECAY != 0) {
+  if constexpr (DECAY == 1) {
 #pragma unroll
     for (int r = 0; r < TPS; ++r) {   // (gamma, theta) -> gamma e^{i theta}
       float sn, cs;
       __sincosf(d[r].y, &sn, &cs);
       d[r] = f32x2{d[r].x * cs, d[r].x * sn};
     }
+  } else if constexpr (DECAY == 2) {
+#pragma unroll
+    for (int r = 0; r < TPS; ++r) {   // sign bit of gamma: reflection
+      float sn, cs;
+      __sincosf(d[r].y, &sn, &cs);
+      const float gm = __builtin_fabsf(d[r].x);
+      d[r] = with_refl(f32x2{gm * cs, gm * sn}, __float_as_uint(d[r].x) >> 31);
+    }
   }
+  // products in token order: u's tokens come before v's
   auto mulz = [](f32x2 u, f32x2 v) {
-    return (DECAY == 0) ? f32x2{u.x * v.x, u.y * v.y} : cmul(u, v);
+    if constexpr (DECAY == 0) return f32x2{u.x * v.x, u.y * v.y};
+    else if constexpr (DECAY == 1) return cmul(u, v);
+    else return compose(u, v);
   };
   const f32x2 one = {1.f, DECAY == 0 ? 1.f : 0.f};
   if constexpr (NEXT) {
@@ -436,16 +468,22 @@ __device__ __forceinline__ void prep_chunk(Shared<DK, TV>& sh, const RawT<DK, TV
   }
   // products over the earlier (pre) and later (post) segments of this lane's
   // channel pair, and over the whole chunk (tot): a butterfly over the NSEG
-  // segments (lanes PPW apart) with cross-lane swaps; every factor is a
-  // diagonal or 2x2-rotation transition, so the products commute
+  // segments (lanes PPW apart) with cross-lane swaps, each product taken in
+  // token order (the partner block of an upper lane holds earlier segments)
   f32x2 pre = one, post = one, tot = run;
 #pragma unroll
   for (int d = 1; d < NSEG; d *= 2) {
     const f32x2 tp = {xor_lanes<PPW>(tot.x, d, l), xor_lanes<PPW>(tot.y, d, l)};
-    const bool upper = (seg & d) != 0;   // partner block holds earlier segments
-    pre = mulz(pre, upper ? tp : one);
-    post = mulz(post, upper ? one : tp);
-    tot = mulz(tot, tp);
+    const bool upper = (seg & d) != 0;
+    if constexpr (DECAY == 2) {
+      pre = upper ? mulz(tp, pre) : pre;
+      post = upper ? post : mulz(post, tp);
+      tot = upper ? mulz(tp, tot) : mulz(tot, tp);
+    } else {   // commuting factors
+      pre = mulz(pre, upper ? tp : one);
+      post = mulz(post, upper ? one : tp);
+      tot = mulz(tot, tp);
+    }
   }
   if (seg == 0) A.GL[pp] = tot;
   {   // chunk-level range check of the split form (gdr_token.h)
@@ -467,6 +505,7 @@ __device__ __forceinline__ void prep_chunk(Shared<DK, TV>& sh, const RawT<DK, TV
     const float nz = __builtin_amdgcn_rcpf(tot.x * tot.x + tot.y * tot.y);
     ig = f32x2{tot.x * nz, tot.y * nz};
   }
+  (void)ig;
   // running products from the chunk start (gf = Gamma_r) and, for Kh, the
   // product to the chunk end times Gamma_L^{-T} (hb = Gamma_L^{-T} h_r^T)
   f32x2 gfv[TPS], hbv[TPS];
@@ -477,11 +516,21 @@ __device__ __forceinline__ void prep_chunk(Shared<DK, TV>& sh, const RawT<DK, TV
       rf = mulz(rf, d[r]);
       gfv[r] = rf;
     }
-    f32x2 rb = (DECAY == 0) ? mulz(post, ig) : cmul(ig, conj(post));
+    if constexpr (DECAY == 2) {
+      // Gamma_r^{-T} of a map (w, s) is (w / |w|^2, s)
 #pragma unroll
-    for (int r = TPS - 1; r >= 0; --r) {
-      hbv[r] = rb;
-      rb = (DECAY == 0) ? mulz(rb, d[r]) : cmul(rb, conj(d[r]));
+      for (int r = 0; r < TPS; ++r) {
+        const f32x2 w = with_refl(gfv[r], 0u);
+        const float nz = __builtin_amdgcn_rcpf(w.x * w.x + w.y * w.y);
+        hbv[r] = with_refl(f32x2{w.x * nz, w.y * nz}, refl_bit(gfv[r]));
+      }
+    } else {
+      f32x2 rb = (DECAY == 0) ? mulz(post, ig) : cmul(ig, conj(post));
+#pragma unroll
+      for (int r = TPS - 1; r >= 0; --r) {
+        hbv[r] = rb;
+        rb = (DECAY == 0) ? mulz(rb, d[r]) : cmul(rb, conj(d[r]));
+      }
     }
   }
   // stored position of this channel pair (rows of one lane share bit 3 when
@@ -507,10 +556,14 @@ __device__ __forceinline__ void prep_chunk(Shared<DK, TV>& sh, const RawT<DK, TV
         kp = f32x2{kx.x * gf.x, kx.y * gf.y};
         qp = f32x2{qx.x * gf.x, qx.y * gf.y};
         kh = f32x2{kx.x * hb.x, kx.y * hb.y};
-      } else {
+      } else if constexpr (DECAY == 1) {
         kp = cmul(gf, kx);
         qp = cmul(gf, qx);
         kh = cmul(hb, kx);
+      } else {
+        kp = apply_map(gf, kx);
+        qp = apply_map(gf, qx);
+        kh = apply_map(hb, kx);
       }
       *(uint32_t*)(A.Kp + row * RSK + pc) = f2_to_bf2(kp);
       *(uint32_t*)(A.Qp + row * RSK + pc) = f2_to_bf2(qp);
@@ -646,8 +699,15 @@ __device__ inline void stage_raw(SlotA<DK, TV>& A, const Rsrc& rs, int c0, int i
       for (int e = 0; e < 4; ++e) {
         float sn, cs;
         __sincosf(__uint_as_float(xt[e]), &sn, &cs);
-        (e < 2 ? lo : hi)[2 * (e & 1)] = gm4[e] * cs;
-        (e < 2 ? lo : hi)[2 * (e & 1) + 1] = gm4[e] * sn;
+        if constexpr (DECAY == 2) {   // reflection bit in the lowest bit of the first value
+          const float gm = __builtin_fabsf(gm4[e]);
+          const f32x2 m = with_refl(f32x2{gm * cs, gm * sn}, __float_as_uint(gm4[e]) >> 31);
+          (e < 2 ? lo : hi)[2 * (e & 1)] = m.x;
+          (e < 2 ? lo : hi)[2 * (e & 1) + 1] = m.y;
+        } else {
+          (e < 2 ? lo : hi)[2 * (e & 1)] = gm4[e] * cs;
+          (e < 2 ? lo : hi)[2 * (e & 1) + 1] = gm4[e] * sn;
+        }
       }
       *(f32x4*)(ra + t * DK + c + 2 * u) = lo;
       *(f32x4*)(ra + t * DK + c + 2 * u + 4) = hi;
@@ -1230,9 +1290,15 @@ __global__ __launch_bounds__((NWP + NWS + TV / 16 + (CONTENT ? 1 : 0)) * 64) voi
                         if constexpr (DECAY == 0) {
                           Sacc[ct][jj] = x0 * z.x;
                           Sacc[ct][jj + 1] = x1 * z.y;
-                        } else {
+                        } else if constexpr (DECAY == 1) {
                           Sacc[ct][jj] = z.x * x0 + z.y * x1;
                           Sacc[ct][jj + 1] = -z.y * x0 + z.x * x1;
+                        } else {
+                          // a state row times Gamma_L: conj(w) y, or for a
+                          // reflection (symmetric block) w conj(y)
+                          const float y1 = -z.y * x0 + z.x * x1;
+                          Sacc[ct][jj] = z.x * x0 + z.y * x1;
+                          Sacc[ct][jj + 1] = __uint_as_float(__float_as_uint(y1) ^ (refl_bit(z) << 31));
                         }
                       }
                     }
@@ -1353,6 +1419,8 @@ hipError_t launch_fwd_gated(const FwdParams& p, hipStream_t s) {
 
 hipError_t launch_fwd_pipe(const FwdParams& p, hipStream_t s) {
   const bool rot = p.decay != 0;
+  // reflection blocks run only in the plain launch
+  if (p.decay == 2 && (p.beta_logit != nullptr || p.gmode != 0 || p.ckpt != nullptr)) return hipErrorInvalidValue;
   if (p.beta_logit != nullptr) {
     // content-aware: 16-channel value tiles, each workgroup with its own
     // projection wave (few heads, long sequences: spread over more CUs)
@@ -1363,6 +1431,14 @@ hipError_t launch_fwd_pipe(const FwdParams& p, hipStream_t s) {
   if (p.ckpt != nullptr) {   // the backward's forward recompute
     if (p.DK == 128) return rot ? pipe::launch<128, 32, 1, false, 0, true>(p, s) : pipe::launch<128, 32, 0, false, 0, true>(p, s);
     if (p.DK == 64) return rot ? pipe::launch<64, 32, 1, false, 0, true>(p, s) : pipe::launch<64, 32, 0, false, 0, true>(p, s);
+    return hipErrorInvalidValue;
+  }
+  if (p.decay == 2) {   // rotation and reflection blocks
+    if (p.DK == 128) {
+      if ((long)p.B * p.H * 2 >= 192) return pipe::launch<128, 64, 2>(p, s);
+      return pipe::launch<128, 32, 2>(p, s);
+    }
+    if (p.DK == 64) return pipe::launch<64, 32, 2>(p, s);
     return hipErrorInvalidValue;
   }
   if (p.DK == 128) {

@@ -71,7 +71,11 @@ __global__ __launch_bounds__((DV * DK / 8) < 256 ? (DV * DK / 8) : 256) void gdr
   for (int ps = 0; ps < NPASS; ++ps) vr[ps] = to_f32(gv[ps * RPP + rw]);
   const float beta = p.beta[unit], wg = p.w[unit];
 
-  float d0[8], d1[4];   // DIAG: d0 = alpha; ROT2: d0 = (gamma cos, gamma sin) pairs
+  // DIAG: d0 = alpha; ROT2: d0 = (gamma cos, gamma sin) pairs; DECAY 2 (rotation
+  // and reflection blocks): the same with |gamma|, refl[j] set where gamma's
+  // sign bit is (the block |gamma| [[c, s], [s, -c]])
+  float d0[8], d1[4];
+  unsigned refl[4] = {0u, 0u, 0u, 0u};
   if constexpr (DECAY == 0) {
     const float* a = p.alpha + (size_t)unit * DK + c0;
     const f32x4 x = *(const f32x4*)a, y = *(const f32x4*)(a + 4);
@@ -88,8 +92,10 @@ __global__ __launch_bounds__((DV * DK / 8) < 256 ? (DV * DK / 8) : 256) void gdr
     for (int j = 0; j < 4; ++j) {
       float sn, cs;
       sincosf(y[j], &sn, &cs);
-      d0[2 * j] = x[j] * cs;
-      d0[2 * j + 1] = x[j] * sn;
+      const float g = DECAY == 2 ? __builtin_fabsf(x[j]) : x[j];
+      if (DECAY == 2) refl[j] = __float_as_uint(x[j]) >> 31;
+      d0[2 * j] = g * cs;
+      d0[2 * j + 1] = g * sn;
     }
     (void)d1;
   }
@@ -107,7 +113,7 @@ __global__ __launch_bounds__((DV * DK / 8) < 256 ? (DV * DK / 8) : 256) void gdr
         const float gc = d0[2 * j], gs = d0[2 * j + 1];
         const float s0 = srow[ps][2 * j], s1 = srow[ps][2 * j + 1];
         x[2 * j] = gc * s0 + gs * s1;
-        x[2 * j + 1] = -gs * s0 + gc * s1;
+        x[2 * j + 1] = refl[j] ? gs * s0 - gc * s1 : -gs * s0 + gc * s1;
       }
     }
     float y = 0.f;
@@ -150,7 +156,11 @@ static hipError_t step_dk(const StepParams& p, hipStream_t s) {
 }
 
 hipError_t launch_step(const StepParams& p, hipStream_t s) {
-  if (p.io_bf16) return p.decay ? step_dk<__bf16, 1>(p, s) : step_dk<__bf16, 0>(p, s);
+  if (p.io_bf16) {
+    if (p.decay == 2) return step_dk<__bf16, 2>(p, s);
+    return p.decay ? step_dk<__bf16, 1>(p, s) : step_dk<__bf16, 0>(p, s);
+  }
+  if (p.decay == 2) return step_dk<float, 2>(p, s);
   return p.decay ? step_dk<float, 1>(p, s) : step_dk<float, 0>(p, s);
 }
 

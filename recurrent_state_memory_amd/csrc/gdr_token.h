@@ -60,7 +60,8 @@ __device__ inline float sum_over_g(float x) {
 
 // Run tokens 0 .. ntok-1 of a chunk from raw inputs in LDS:
 //   tr [ntok][DK] fp32: DIAG alpha per channel; ROT2 (gamma cos, gamma sin) per
-//                       channel pair, pair p at channels 2p, 2p + 1
+//                       channel pair, pair p at channels 2p, 2p + 1 (DECAY 2:
+//                       the lowest bit of the first value marks a reflection)
 //   kr, qr [ntok][ldk]: raw keys and queries (io type)
 //   vval(t): value of row n of this wave at token t, as float
 //   beta[t], bw[t]: erase strength and beta * w
@@ -86,7 +87,14 @@ __device__ inline void token_steps(f32x4 (&Sacc)[DK / 16], const float* tr, cons
         for (int j = 0; j < 4; j += 2) {   // S times gamma [[c, -s], [s, c]] on the pair
           const float x0 = Sacc[ct][j], x1 = Sacc[ct][j + 1];
           Sacc[ct][j] = z[j] * x0 + z[j + 1] * x1;
-          Sacc[ct][j + 1] = -z[j + 1] * x0 + z[j] * x1;
+          const float y1 = -z[j + 1] * x0 + z[j] * x1;
+          if constexpr (DECAY == 2) {
+            // reflection block gamma [[c, s], [s, -c]] when the lowest bit
+            // of the first value is set: the second component changes sign
+            Sacc[ct][j + 1] = __uint_as_float(__float_as_uint(y1) ^ ((__float_as_uint(z[j]) & 1u) << 31));
+          } else {
+            Sacc[ct][j + 1] = y1;
+          }
         }
       }
       const f32x4 k4 = load4_f32<T>(kp + 16 * ct);

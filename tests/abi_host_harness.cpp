@@ -72,6 +72,14 @@ int main() {
   a.ub_up = (const float*)fake(12); a.ub_rank = 16; a.chunk = 128; a.T = 256;
   a.m_carry = (float*)fake(13);
   CHECK(gdr_chunk_fwd(&a, nullptr) == GDR_OK && gdr::g_fwd.window == 128 && gdr::g_fwd.ub_rank == 16);
+  // reflection blocks: marshalled as decay kind 2; other io dtypes and the
+  // content-aware erase are refused
+  a = good_fwd(); a.decay = GDR_DECAY_DIHEDRAL; a.theta = (const float*)fake(16);
+  CHECK(gdr_chunk_fwd(&a, nullptr) == GDR_OK && gdr::g_fwd.decay == 2 && gdr::g_fwd.theta == a.theta);
+  const int nrefl = gdr::g_nfwd;
+  a.io_dtype = GDR_F32; CHECK(gdr_chunk_fwd(&a, nullptr) == GDR_ERR_UNSUPPORTED);
+  a.io_dtype = GDR_BF16; a.theta = nullptr; CHECK(gdr_chunk_fwd(&a, nullptr) == GDR_ERR_NULL);
+  CHECK(gdr::g_nfwd == nrefl);
 
   // rejected before any launch
   const int before = gdr::g_nfwd;
@@ -155,6 +163,7 @@ int main() {
     x = w; x.decay = GDR_DECAY_ROT2; CHECK(gdr_chunk_bwd(&x, nullptr) == GDR_ERR_NULL);
     x = w; x.decay = GDR_DECAY_ROT2; x.theta = (const float*)fake(21); x.grad_theta = (float*)fake(22);
     CHECK(gdr_chunk_bwd(&x, nullptr) == GDR_OK && gdr::g_bwd.decay == 1);
+    x.decay = GDR_DECAY_DIHEDRAL; CHECK(gdr_chunk_bwd(&x, nullptr) == GDR_ERR_UNSUPPORTED);
     x = w; x.grad_q = (float*)((char*)fake(8) + 4); CHECK(gdr_chunk_bwd(&x, nullptr) == GDR_ERR_ALIGN);
     x = w; x.T = 0; CHECK(gdr_chunk_bwd(&x, nullptr) == GDR_ERR_SHAPE);
     x = w; x.B = 0x7fffffff; x.T = 0x7fffffff; CHECK(gdr_chunk_bwd(&x, nullptr) == GDR_ERR_SHAPE);
@@ -169,6 +178,9 @@ int main() {
   s.theta = (const float*)fake(5); s.beta = (const float*)fake(6); s.w = (const float*)fake(7);
   s.S = (float*)fake(8); s.o = fake(9);
   CHECK(gdr_step_decode(&s, nullptr) == GDR_OK && gdr::g_nstep == 1 && gdr::g_step.decay == 1);
+  s.decay = GDR_DECAY_DIHEDRAL;
+  CHECK(gdr_step_decode(&s, nullptr) == GDR_OK && gdr::g_nstep == 2 && gdr::g_step.decay == 2);
+  s.decay = GDR_DECAY_ROT2;
   s.N = 0x7fffffff; s.H = 0x7fffffff; CHECK(gdr_step_decode(&s, nullptr) == GDR_ERR_SHAPE);
   CHECK(gdr_step_decode(nullptr, nullptr) == GDR_ERR_NULL);
 

@@ -74,6 +74,14 @@ FWD_CASES = [
     (dict(S0=MISALIGNED), gdr.GDR_ERR_ALIGN),
     (dict(theta=FAKE), gdr.GDR_ERR_ARG),                       # diag with theta
     (dict(decay=gdr.GDR_DECAY_ROT2), gdr.GDR_ERR_NULL),        # rot2 without theta
+    (dict(decay=gdr.GDR_DECAY_DIHEDRAL), gdr.GDR_ERR_NULL),    # reflections without theta
+    # reflection blocks: the pipelined kernel's plain launch only
+    (dict(decay=gdr.GDR_DECAY_DIHEDRAL, theta=FAKE, io_dtype=gdr.GDR_F32),
+     gdr.GDR_ERR_UNSUPPORTED),
+    (dict(decay=gdr.GDR_DECAY_DIHEDRAL, theta=FAKE, dk=32, dv=32), gdr.GDR_ERR_UNSUPPORTED),
+    (dict(decay=gdr.GDR_DECAY_DIHEDRAL, theta=FAKE, beta=None, beta_logit=FAKE, ub_down=FAKE,
+          ub_up=FAKE, ub_rank=16), gdr.GDR_ERR_UNSUPPORTED),
+    (dict(decay=gdr.GDR_DECAY_DIHEDRAL, theta=FAKE, T=1 << 23, H=1), gdr.GDR_ERR_UNSUPPORTED),
     (dict(m_carry=FAKE), gdr.GDR_ERR_ARG),                     # carry without content
     (dict(ub_down=FAKE), gdr.GDR_ERR_ARG),
     (dict(beta_logit=FAKE, ub_down=FAKE, ub_up=FAKE, ub_rank=16), gdr.GDR_ERR_ARG),  # beta too
@@ -114,6 +122,7 @@ GATE_CASES = [
     (dict(T=1 << 23, H=1), dict(), gdr.GDR_ERR_UNSUPPORTED),  # T * H * dk >= 2^29
     (dict(beta=None), dict(), gdr.GDR_ERR_NULL),
     (dict(decay=gdr.GDR_DECAY_ROT2), dict(), gdr.GDR_ERR_NULL),  # rot2 without theta
+    (dict(decay=gdr.GDR_DECAY_DIHEDRAL, theta=FAKE), dict(), gdr.GDR_ERR_UNSUPPORTED),
     (dict(B=0), dict(), gdr.GDR_ERR_SHAPE),
 ]
 
@@ -155,6 +164,7 @@ BWD_CASES = [
     (dict(T=1 << 23, H=1), gdr.GDR_ERR_UNSUPPORTED),
     (dict(theta=FAKE), gdr.GDR_ERR_ARG),
     (dict(decay=gdr.GDR_DECAY_ROT2, theta=FAKE), gdr.GDR_ERR_NULL),   # no grad_theta
+    (dict(decay=gdr.GDR_DECAY_DIHEDRAL, theta=FAKE, grad_theta=FAKE), gdr.GDR_ERR_UNSUPPORTED),
     (dict(grad_S0=MISALIGNED), gdr.GDR_ERR_ALIGN),
     (dict(), gdr.GDR_ERR_WORKSPACE),                                  # no workspace
     (dict(workspace=FAKE, workspace_bytes=1024), gdr.GDR_ERR_WORKSPACE),
@@ -218,6 +228,7 @@ STEP_CASES = [
     (dict(io_dtype=2), gdr.GDR_ERR_DTYPE),
     (dict(S=MISALIGNED), gdr.GDR_ERR_ALIGN),
     (dict(decay=gdr.GDR_DECAY_ROT2), gdr.GDR_ERR_NULL),
+    (dict(decay=gdr.GDR_DECAY_DIHEDRAL), gdr.GDR_ERR_NULL),
     (dict(theta=FAKE), gdr.GDR_ERR_ARG),
 ]
 
@@ -326,6 +337,9 @@ def test_binding_rejects_bad_content_and_rotation_arguments():
     a["m_carry"] = torch.zeros(2, 3, 8)
     with pytest.raises(ValueError, match="content-aware"):
         gdr.gdr_chunk_fwd(**a)
+    a = _cpu_fwd_args()
+    with pytest.raises(ValueError, match="reflection"):
+        gdr.gdr_chunk_fwd(**a, reflections=True)               # no theta
 
 
 def _cpu_gated_args(B=2, T=5, H=3, d=8, rot=False):
@@ -401,6 +415,8 @@ def test_decode_binding_checks():
         a[name] = val
         with pytest.raises(ValueError, match=name):
             gdr.gdr_step_decode(**a)
+    with pytest.raises(ValueError, match="reflection"):
+        gdr.gdr_step_decode(**good, reflections=True)
 
 
 def test_host_half_under_sanitizers(tmp_path):
