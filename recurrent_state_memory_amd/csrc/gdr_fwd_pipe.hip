@@ -53,16 +53,6 @@ __device__ inline unsigned refl_bit(f32x2 m) { return __float_as_uint(m.x) & 1u;
 __device__ inline f32x2 with_refl(f32x2 w, unsigned s) {
   return f32x2{__uint_as_float((__float_as_uint(w.x) & ~1u) | s), w.y};
 }
-// f o g: apply g first
-__device__ inline f32x2 compose(f32x2 f, f32x2 g) {
-  const unsigned sf = refl_bit(f), sg = refl_bit(g);
-  const f32x2 fw = with_refl(f, 0u), gw = with_refl(g, 0u);
-  return with_refl(cmul(fw, sf ? conj(gw) : gw), sf ^ sg);
-}
-// the map applied to a key pair (column action)
-__device__ inline f32x2 apply_map(f32x2 m, f32x2 x) {
-  return cmul(with_refl(m, 0u), refl_bit(m) ? conj(x) : x);
-}
 
 __device__ inline f32x2 bf2_to_f2(uint32_t u) {
   return f32x2{__uint_as_float(u << 16), __uint_as_float(u & 0xffff0000u)};
@@ -413,20 +403,43 @@ __device__ __forceinline__ void prep_chunk(Shared<DK, TV>& sh, const RawT<DK, TV
       __sincosf(d[r].y, &sn, &cs);
       d[r] = f32x2{d[r].x * cs, d[r].x * sn};
     }
-  } else if constexpr (DECAY == 2) {
+  }
+  // Reflection blocks: the map of tokens 1..r is (w_1 c^p1(w_2) c^p2(w_3) ...,
+  // p_r) with p_i the parity of reflections among tokens 1..i (c: complex
+  // conjugate), so conjugating each w_i by the parity before it turns every
+  // product into a plain, commuting complex product.  psg[r]: that parity
+  // through token r of the chunk, as a sign bit.  The parity of this pair's
+  // earlier segments comes from one ballot of the segment parities (bit
+  // pl + PPW j: segment j).
+  unsigned psg[TPS];
+  unsigned ptot = 0u;   // reflection parity of the whole chunk (bit 0)
+  if constexpr (DECAY == 2) {
+    unsigned sp = 0u;
 #pragma unroll
-    for (int r = 0; r < TPS; ++r) {   // sign bit of gamma: reflection
+    for (int r = 0; r < TPS; ++r) sp ^= __float_as_uint(d[r].x);   // sign bit of gamma: reflection
+    constexpr unsigned long long REP = [] {
+      unsigned long long m = 0ull;
+      for (int j = 0; j < NSEG; ++j) m |= 1ull << (j * PPW);
+      return m;
+    }();
+    const unsigned long long bm = __ballot((int)sp < 0) >> pl;
+    unsigned par = (unsigned)(__popcll(bm & REP & ((1ull << (seg * PPW)) - 1ull)) & 1) << 31;
+    ptot = (unsigned)__popcll(bm & REP) & 1u;
+#pragma unroll
+    for (int r = 0; r < TPS; ++r) {
       float sn, cs;
       __sincosf(d[r].y, &sn, &cs);
       const float gm = __builtin_fabsf(d[r].x);
-      d[r] = with_refl(f32x2{gm * cs, gm * sn}, __float_as_uint(d[r].x) >> 31);
+      const unsigned sr = __float_as_uint(d[r].x) & 0x80000000u;
+      d[r] = f32x2{gm * cs, __uint_as_float(__float_as_uint(gm * sn) ^ par)};
+      par ^= sr;
+      psg[r] = par;
     }
   }
-  // products in token order: u's tokens come before v's
+  // products of commuting factors (reflection blocks: conjugated as above)
   auto mulz = [](f32x2 u, f32x2 v) {
     if constexpr (DECAY == 0) return f32x2{u.x * v.x, u.y * v.y};
-    else if constexpr (DECAY == 1) return cmul(u, v);
-    else return compose(u, v);
+    else return cmul(u, v);
   };
   const f32x2 one = {1.f, DECAY == 0 ? 1.f : 0.f};
   if constexpr (NEXT) {
@@ -475,17 +488,11 @@ __device__ __forceinline__ void prep_chunk(Shared<DK, TV>& sh, const RawT<DK, TV
   for (int d = 1; d < NSEG; d *= 2) {
     const f32x2 tp = {xor_lanes<PPW>(tot.x, d, l), xor_lanes<PPW>(tot.y, d, l)};
     const bool upper = (seg & d) != 0;
-    if constexpr (DECAY == 2) {
-      pre = upper ? mulz(tp, pre) : pre;
-      post = upper ? post : mulz(post, tp);
-      tot = upper ? mulz(tp, tot) : mulz(tot, tp);
-    } else {   // commuting factors
-      pre = mulz(pre, upper ? tp : one);
-      post = mulz(post, upper ? one : tp);
-      tot = mulz(tot, tp);
-    }
+    pre = mulz(pre, upper ? tp : one);
+    post = mulz(post, upper ? one : tp);
+    tot = mulz(tot, tp);
   }
-  if (seg == 0) A.GL[pp] = tot;
+  if (seg == 0) A.GL[pp] = DECAY == 2 ? with_refl(tot, ptot) : tot;
   {   // chunk-level range check of the split form (gdr_token.h)
     const unsigned long long bad = __ballot(!decay_in_range<DECAY>(tot));
     if constexpr (ROBUST) {
@@ -516,21 +523,11 @@ __device__ __forceinline__ void prep_chunk(Shared<DK, TV>& sh, const RawT<DK, TV
       rf = mulz(rf, d[r]);
       gfv[r] = rf;
     }
-    if constexpr (DECAY == 2) {
-      // Gamma_r^{-T} of a map (w, s) is (w / |w|^2, s)
+    f32x2 rb = (DECAY == 0) ? mulz(post, ig) : cmul(ig, conj(post));
 #pragma unroll
-      for (int r = 0; r < TPS; ++r) {
-        const f32x2 w = with_refl(gfv[r], 0u);
-        const float nz = __builtin_amdgcn_rcpf(w.x * w.x + w.y * w.y);
-        hbv[r] = with_refl(f32x2{w.x * nz, w.y * nz}, refl_bit(gfv[r]));
-      }
-    } else {
-      f32x2 rb = (DECAY == 0) ? mulz(post, ig) : cmul(ig, conj(post));
-#pragma unroll
-      for (int r = TPS - 1; r >= 0; --r) {
-        hbv[r] = rb;
-        rb = (DECAY == 0) ? mulz(rb, d[r]) : cmul(rb, conj(d[r]));
-      }
+    for (int r = TPS - 1; r >= 0; --r) {
+      hbv[r] = rb;
+      rb = (DECAY == 0) ? mulz(rb, d[r]) : cmul(rb, conj(d[r]));
     }
   }
   // stored position of this channel pair (rows of one lane share bit 3 when
@@ -560,10 +557,12 @@ __device__ __forceinline__ void prep_chunk(Shared<DK, TV>& sh, const RawT<DK, TV
         kp = cmul(gf, kx);
         qp = cmul(gf, qx);
         kh = cmul(hb, kx);
-      } else {
-        kp = apply_map(gf, kx);
-        qp = apply_map(gf, qx);
-        kh = apply_map(hb, kx);
+      } else {   // Gamma_r and Gamma_r^{-T} reflect when the parity through r is odd
+        const f32x2 kc = {kx.x, __uint_as_float(__float_as_uint(kx.y) ^ psg[r])};
+        const f32x2 qc = {qx.x, __uint_as_float(__float_as_uint(qx.y) ^ psg[r])};
+        kp = cmul(gf, kc);
+        qp = cmul(gf, qc);
+        kh = cmul(hb, kc);
       }
       *(uint32_t*)(A.Kp + row * RSK + pc) = f2_to_bf2(kp);
       *(uint32_t*)(A.Qp + row * RSK + pc) = f2_to_bf2(qp);
