@@ -19,6 +19,10 @@ long  1, 16, 32768, 128               128    bf16         decay + content erase
 rot   4, 16, 8192, 128 (+ decode)     64     bf16         2x2 rotation blocks
 ====  ==============================  =====  ===========  ====================
 
+The Raven slot-memory forward has its own workload (``RAVEN_WORKLOADS``:
+the layer shape B=8, H=16, T=4096, d=128 with 64 slots and top-8 routing) and
+generator (``generate_raven``).
+
 Draw order for one workload (all fp32 standard normal unless noted):
 q, k, v, beta-logit (content-aware: b_x), w-logit, then either the decay
 noise [B,T,H,d_k] or theta ~ U(-pi, pi) followed by the block-magnitude noise
@@ -292,3 +296,65 @@ def generate_gated(wl: Workload, T: Optional[int] = None) -> GatedInputs:
     return GatedInputs(wl, bf16_round(q), bf16_round(k), _io_cast(v, "bf16"), _sigmoid(b_logit),
                        _sigmoid(w_logit), bf16_round(noise),
                        np.full((H,), wl.decay_scale, dtype=np.float32), theta)
+
+
+# --------------------------------------------------------------------------
+# Raven routing slot memory (a second recurrence: M slots, top-K router)
+# --------------------------------------------------------------------------
+@dataclasses.dataclass(frozen=True)
+class RavenWorkload:
+    """Shapes of the slot-memory forward: M slots of d_k (keys) and d_v (values)
+    per head, the top-K router, and the decay rate a = -a_scale * softplus(x)."""
+    name: str
+    B: int
+    H: int
+    T: int
+    dk: int
+    dv: int
+    slots: int
+    topk: int
+    seed: int
+    a_scale: float = 1.0
+
+    def replace(self, **kw) -> "RavenWorkload":
+        return dataclasses.replace(self, **kw)
+
+    @property
+    def scale(self) -> float:
+        return 1.0 / math.sqrt(self.dk)
+
+
+RAVEN_WORKLOADS = {
+    # the layer shape (B=8, H=16, T=4096, d=128) with 64 slots, top-8 routing
+    "raven": RavenWorkload("raven", 8, 16, 4096, 128, 128, 64, 8, 6),
+}
+
+
+@dataclasses.dataclass
+class RavenInputs:
+    """fp32 host arrays; q, k, v and the router logits z hold bf16 values."""
+    wl: RavenWorkload
+    q: np.ndarray      # [B,T,H,dk], L2-normalised per token
+    k: np.ndarray      # [B,T,H,dk], L2-normalised per token
+    v: np.ndarray      # [B,T,H,dv]
+    z: np.ndarray      # [B,T,H,slots] router logits
+    a: np.ndarray      # [B,T,H] decay rate, <= 0
+
+
+def generate_raven(wl: RavenWorkload, T: Optional[int] = None,
+                   B: Optional[int] = None) -> RavenInputs:
+    """Draw order: q, k, v, router logits z, decay noise x (all fp32 standard
+    normal); then q, k L2-normalised and rounded to bf16, v and z rounded to
+    bf16, a = -a_scale * softplus(x) in fp32."""
+    if T is not None or B is not None:
+        wl = wl.replace(T=T if T is not None else wl.T, B=B if B is not None else wl.B)
+    rng = np.random.default_rng(wl.seed)
+    Bn, Tn, H = wl.B, wl.T, wl.H
+    q = rng.standard_normal((Bn, Tn, H, wl.dk), dtype=np.float32)
+    k = rng.standard_normal((Bn, Tn, H, wl.dk), dtype=np.float32)
+    v = rng.standard_normal((Bn, Tn, H, wl.dv), dtype=np.float32)
+    z = rng.standard_normal((Bn, Tn, H, wl.slots), dtype=np.float32)
+    x = rng.standard_normal((Bn, Tn, H), dtype=np.float32)
+    a = (np.float32(-wl.a_scale) * _softplus(x)).astype(np.float32)
+    return RavenInputs(wl, bf16_round(_l2_normalise(q)), bf16_round(_l2_normalise(k)),
+                       bf16_round(v), bf16_round(z), a)
