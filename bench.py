@@ -16,7 +16,7 @@ kernel (algorithmic bytes per launch / measured launch time, against the HBM
 peak) and a CPU baseline: the fp64 oracle timed on a bounded sample of the
 same workload on this host.
 
-Other workloads (``--workload small|rot|dihedral|long|decode|copy``) are for profiling
+Other workloads (``--workload small|rot|dihedral|long|decode|raven|copy``) are for profiling
 and are not the reported metric; ``copy`` is a plain device copy of known size
 used to calibrate the HBM byte counters.
 """
@@ -200,6 +200,70 @@ def _bwd_closure(wl):
     return step, x
 
 
+def raven_bytes(wl) -> int:
+    """Bytes the Raven slot-memory forward must move at least once: q, k, v and
+    the router logits (bf16), the decay rate (fp32) in; o (bf16) out; the final
+    key and value slots (fp32) out."""
+    per_th = (2 * wl.dk + wl.dv + wl.slots) * 2 + 4 + wl.dv * 2
+    return per_th * wl.B * wl.T * wl.H + 4 * wl.slots * (wl.dk + wl.dv) * wl.B * wl.H
+
+
+def raven_flops(wl, L: int = 32) -> float:
+    """Matrix flops of the chunk form per launch, each product counted once:
+    per token q.Sk (M d), the value read-out (M d), both slot updates (2 M d),
+    and the in-chunk token-pair terms at half (L d / 2 twice, L M / 2 twice)."""
+    d, M = wl.dk, wl.slots
+    return 2.0 * (4 * M * d + L * d + L * M) * wl.B * wl.T * wl.H
+
+
+def _raven_closure(wl):
+    import torch
+    import recurrent_state_memory_amd as gdr
+    from synth.gen import generate_raven
+    x = generate_raven(wl)
+    bf = torch.bfloat16
+    q, k, v, z = (_to_dev(t, bf) for t in (x.q, x.k, x.v, x.z))
+    a = _to_dev(x.a)
+    o = torch.empty((wl.B, wl.T, wl.H, wl.dv), dtype=bf, device="cuda")
+    Sk = torch.empty((wl.B, wl.H, wl.slots, wl.dk), dtype=torch.float32, device="cuda")
+    Sv = torch.empty((wl.B, wl.H, wl.slots, wl.dv), dtype=torch.float32, device="cuda")
+
+    def step():
+        gdr.gdr_raven_fwd(q, k, v, z, a, topk=wl.topk, scale=wl.scale, o=o, Sk_out=Sk, Sv_out=Sv)
+    return step, x
+
+
+def cpu_baseline_raven(wl, x, budget_s: float = 15.0):
+    """The Raven oracle on this host's cores, as ``cpu_baseline``: one worker
+    thread per batch row, all heads, a prefix sized to about ``budget_s``."""
+    import concurrent.futures as cf
+    import numpy as np
+    from threadpoolctl import threadpool_limits
+    from oracle import raven
+
+    workers = max(1, min(16, len(os.sched_getaffinity(0)), wl.B))
+
+    def run(b, T_s):
+        sl = (slice(b, b + 1), slice(0, T_s))
+        return raven.forward(x.q[sl], x.k[sl], x.v[sl], x.z[sl], x.a[sl], wl.topk, wl.scale)[0]
+
+    with threadpool_limits(limits=1), cf.ThreadPoolExecutor(max_workers=workers) as ex:
+        probe = 16
+        t0 = time.perf_counter()
+        list(ex.map(lambda b: run(b, probe), range(wl.B)))
+        per_tok = (time.perf_counter() - t0) / probe
+        T_s = int(max(32, min(wl.T, budget_s / max(per_tok, 1e-9))))
+        t0 = time.perf_counter()
+        outs = list(ex.map(lambda b: run(b, T_s), range(wl.B)))
+        secs = time.perf_counter() - t0
+    assert all(np.all(np.isfinite(o)) for o in outs)
+    return {"value": round(wl.B * T_s / secs, 2), "unit": "tokens/s", "cores": workers,
+            "kind": "oracle",
+            "sample": (f"fp64 numpy token-by-token Raven oracle, {workers} worker threads "
+                       f"(BLAS single-threaded) on {_cpu_model()}, all {wl.B}x{wl.H} heads, "
+                       f"first {T_s} of {wl.T} tokens, {secs:.1f} s")}
+
+
 def _decode_closure():
     import torch
     import recurrent_state_memory_amd as gdr
@@ -316,7 +380,8 @@ def main(argv=None):
     ap.add_argument("--steps", type=int, default=200)
     ap.add_argument("--warmup", type=int, default=150)
     ap.add_argument("--workload", default="layer",
-                    choices=["layer", "small", "rot", "dihedral", "long", "tiny", "decode", "copy"])
+                    choices=["layer", "small", "rot", "dihedral", "long", "tiny", "decode", "copy",
+                             "raven"])
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--bwd", action="store_true",
                     help="gdr_chunk_bwd: the backward (forward recompute + reverse blocks + reduction)")
@@ -357,6 +422,37 @@ def main(argv=None):
                          "peak": HBM_PEAK_GBS, "unit": "GB/s",
                          "frac": round(nbytes / per / 1e9 / HBM_PEAK_GBS, 4)},
             "config": {"workload": f"decode N={d.N} H={d.H} d={d.dk} rot2 bf16, fp32 state"}}))
+        return 0
+
+    if a.workload == "raven":
+        from synth.gen import RAVEN_WORKLOADS
+        wl = RAVEN_WORKLOADS["raven"]
+        step, x = _raven_closure(wl)
+        secs, wall = _time(step, a.steps, a.warmup)
+        per = secs / a.steps
+        nbytes = raven_bytes(wl)
+        fl = raven_flops(wl)
+        out = {
+            "metric": "tokens/sec Raven routing slot-memory fwd",
+            "value": round(wl.B * wl.T / per, 1), "unit": "tokens/s", "n_gpus": 1,
+            "steps": a.steps, "warmup": a.warmup, "ms_per_step": round(per * 1e3, 4),
+            "higher_is_better": True, "scaling": "weak", "vs_baseline": None, "dtype": "bf16",
+            "data": "synthetic (seeded; q,k L2-normalised, N(0,1) router logits, a = -softplus(x))",
+            "config": {"workload": (f"raven: B={wl.B} H={wl.H} T={wl.T} d_k=d_v={wl.dk} "
+                                    f"slots={wl.slots} top-{wl.topk}, bf16 q/k/v/logits, fp32 "
+                                    "decay rate and slot states, 32-token chunks"),
+                       "global_batch": wl.B, "seq_len": wl.T, "parallelism": "single GPU"},
+            "roofline": {"bound": "hbm", "achieved": round(nbytes / per / 1e9, 1),
+                         "peak": HBM_PEAK_GBS, "unit": "GB/s",
+                         "frac": round(nbytes / per / 1e9 / HBM_PEAK_GBS, 4), "traffic": None},
+            "roofline_mfma": {"achieved": round(fl / per / 1e12, 2), "peak": MFMA_BF16_PEAK_TFS,
+                              "unit": "TFLOP/s",
+                              "frac": round(fl / per / 1e12 / MFMA_BF16_PEAK_TFS, 4)},
+            "wall_s_timed_region": round(wall, 4),
+        }
+        if not a.no_cpu_baseline:
+            out["cpu_baseline"] = cpu_baseline_raven(wl, x)
+        print(json.dumps(out))
         return 0
 
     wl = WORKLOADS[a.workload]

@@ -13,6 +13,8 @@ Entry points (same names as the C ABI):
   the q/k L2 normalisation) computed in the kernel from raw inputs
 * ``gdr_chunk_bwd``   -- gradients of the plain-erase forward (recomputes it)
 * ``gdr_step_decode`` -- one token on a batch of states, in place, returns o
+* ``gdr_raven_fwd``   -- the Raven routing slot memory (include/gdr_raven.h),
+  returns (o, Sk_out, Sv_out)
 """
 from __future__ import annotations
 
@@ -73,6 +75,16 @@ class StepArgs(ctypes.Structure):
     ]
 
 
+class RavenArgs(ctypes.Structure):
+    """Mirror of ``gdr_raven_args`` (include/gdr_raven.h)."""
+    _fields_ = [
+        ("B", _i32), ("T", _i32), ("H", _i32), ("dk", _i32), ("dv", _i32),
+        ("slots", _i32), ("topk", _i32), ("scale", ctypes.c_float),
+        ("q", _vp), ("k", _vp), ("v", _vp), ("z", _vp), ("a", _vp),
+        ("Sk0", _vp), ("Sv0", _vp), ("o", _vp), ("Sk_out", _vp), ("Sv_out", _vp),
+    ]
+
+
 class GdrError(RuntimeError):
     def __init__(self, status: int, msg: str):
         super().__init__(f"gdr status {status}: {msg}")
@@ -106,6 +118,8 @@ def load_library(path: Optional[str] = None) -> ctypes.CDLL:
     lib.gdr_chunk_fwd_workspace.restype = ctypes.c_size_t
     lib.gdr_step_decode.argtypes = [ctypes.POINTER(StepArgs), _vp]
     lib.gdr_step_decode.restype = ctypes.c_int
+    lib.gdr_raven_fwd.argtypes = [ctypes.POINTER(RavenArgs), _vp]
+    lib.gdr_raven_fwd.restype = ctypes.c_int
     lib.gdr_status_str.argtypes = [ctypes.c_int]
     lib.gdr_status_str.restype = ctypes.c_char_p
     lib.gdr_abi_version.argtypes = []
@@ -197,6 +211,14 @@ def call_chunk_bwd_noalloc(args: BwdArgs, stream=None) -> int:
     s = stream if isinstance(stream, ctypes.c_void_p) else (
         ctypes.c_void_p(0) if stream is None else _stream(stream))
     return lib.gdr_chunk_bwd_noalloc(ctypes.byref(args), s)
+
+
+def call_raven_fwd(args: RavenArgs, stream=None) -> int:
+    """Raw call with a filled ``RavenArgs``; returns the status code."""
+    lib = load_library()
+    s = stream if isinstance(stream, ctypes.c_void_p) else (
+        ctypes.c_void_p(0) if stream is None else _stream(stream))
+    return lib.gdr_raven_fwd(ctypes.byref(args), s)
 
 
 def call_step_decode(args: StepArgs, stream=None) -> int:
@@ -436,3 +458,49 @@ def gdr_step_decode(S, q, k, v, alpha, beta, w, *, theta=None, o=None, reflectio
     a.beta, a.w, a.S, a.o = map(_ptr, (beta, w, S, o))
     _check(call_step_decode(a, _stream(stream)))
     return o
+
+
+def gdr_raven_fwd(q, k, v, z, a, *, topk, scale=None, Sk0=None, Sv0=None, o=None,
+                  Sk_out=None, Sv_out=None, return_state=True, stream=None):
+    """Raven routing slot-memory forward (see ``gdr_raven_fwd`` in
+    include/gdr_raven.h).
+
+    q, k [B,T,H,dk], v [B,T,H,dv], router logits z [B,T,H,slots], all bf16;
+    decay rate a fp32 [B,T,H] (finite, <= 0); ``topk`` slots written per token;
+    ``scale`` of the read-out logits (default 1/sqrt(dk)); start slots Sk0
+    [B,H,slots,dk], Sv0 [B,H,slots,dv] fp32 or None (zero).  Returns
+    (o [B,T,H,dv] bf16, Sk_out, Sv_out) -- the states None unless
+    ``return_state`` or given.
+    """
+    import math
+    import torch
+    if q.dim() != 4 or k.dim() != 4 or v.dim() != 4 or z.dim() != 4:
+        raise ValueError("gdr: q, k, v and z must be [B,T,H,*]")
+    B, T, H, dk = q.shape
+    dv = v.shape[-1]
+    M = z.shape[-1]
+    bf, f32 = torch.bfloat16, torch.float32
+    _expect(q, "q", (B, T, H, dk), bf)
+    _expect(k, "k", (B, T, H, dk), bf)
+    _expect(v, "v", (B, T, H, dv), bf)
+    _expect(z, "z", (B, T, H, M), bf)
+    _expect(a, "a", (B, T, H), f32)
+    _expect(Sk0, "Sk0", (B, H, M, dk), f32, required=False)
+    _expect(Sv0, "Sv0", (B, H, M, dv), f32, required=False)
+    if o is None:
+        o = torch.empty((B, T, H, dv), dtype=bf, device=q.device)
+    _expect(o, "o", (B, T, H, dv), bf)
+    if return_state:
+        if Sk_out is None:
+            Sk_out = torch.empty((B, H, M, dk), dtype=f32, device=q.device)
+        if Sv_out is None:
+            Sv_out = torch.empty((B, H, M, dv), dtype=f32, device=q.device)
+    _expect(Sk_out, "Sk_out", (B, H, M, dk), f32, required=False)
+    _expect(Sv_out, "Sv_out", (B, H, M, dv), f32, required=False)
+    r = RavenArgs()
+    r.B, r.T, r.H, r.dk, r.dv, r.slots, r.topk = B, T, H, dk, dv, M, int(topk)
+    r.scale = 1.0 / math.sqrt(dk) if scale is None else float(scale)
+    r.q, r.k, r.v, r.z, r.a = map(_ptr, (q, k, v, z, a))
+    r.Sk0, r.Sv0, r.o, r.Sk_out, r.Sv_out = map(_ptr, (Sk0, Sv0, o, Sk_out, Sv_out))
+    _check(call_raven_fwd(r, _stream(stream)))
+    return o, Sk_out, Sv_out

@@ -8,6 +8,8 @@
 
 #include "gdr.h"
 #include "gdr_kernels.h"
+#include "gdr_raven.h"
+#include "raven_kernels.h"
 
 namespace gdr {
 static FwdParams g_fwd;
@@ -29,6 +31,15 @@ hipError_t launch_bwd(const BwdParams& p, hipStream_t) {
   ++g_nbwd;
   return hipSuccess;
 }
+namespace raven {
+static RavenParams g_rv;
+static int g_nrv = 0;
+hipError_t launch_raven_fwd(const RavenParams& p, hipStream_t) {
+  g_rv = p;
+  ++g_nrv;
+  return hipSuccess;
+}
+}  // namespace raven
 }  // namespace gdr
 
 static int g_fail = 0;
@@ -183,6 +194,34 @@ int main() {
   s.decay = GDR_DECAY_ROT2;
   s.N = 0x7fffffff; s.H = 0x7fffffff; CHECK(gdr_step_decode(&s, nullptr) == GDR_ERR_SHAPE);
   CHECK(gdr_step_decode(nullptr, nullptr) == GDR_ERR_NULL);
+
+  // Raven slot memory: marshalled, and rejected before any launch
+  {
+    gdr_raven_args r;
+    std::memset(&r, 0, sizeof r);
+    r.B = 2; r.T = 77; r.H = 3; r.dk = r.dv = 128; r.slots = 64; r.topk = 8; r.scale = 0.125f;
+    r.q = fake(1); r.k = fake(2); r.v = fake(3); r.z = fake(4); r.a = (const float*)fake(5);
+    r.o = fake(6); r.Sk0 = (const float*)fake(7); r.Sv0 = (const float*)fake(8);
+    r.Sk_out = (float*)fake(7); r.Sv_out = (float*)fake(8);   // in place
+    CHECK(gdr_raven_fwd(&r, nullptr) == GDR_OK && gdr::raven::g_nrv == 1);
+    const gdr::raven::RavenParams& p = gdr::raven::g_rv;
+    CHECK(p.B == 2 && p.T == 77 && p.H == 3 && p.D == 128 && p.topk == 8 && p.scale == 0.125f);
+    CHECK((const void*)p.q == r.q && (const void*)p.z == r.z && p.a == r.a && (void*)p.o == r.o);
+    CHECK(p.Sk0 == r.Sk0 && p.Sv_out == r.Sv_out);
+    gdr_raven_args x = r; x.topk = 9; CHECK(gdr_raven_fwd(&x, nullptr) == GDR_ERR_UNSUPPORTED);
+    x = r; x.topk = 0; CHECK(gdr_raven_fwd(&x, nullptr) == GDR_ERR_SHAPE);
+    x = r; x.slots = 32; CHECK(gdr_raven_fwd(&x, nullptr) == GDR_ERR_UNSUPPORTED);
+    x = r; x.dv = 64; CHECK(gdr_raven_fwd(&x, nullptr) == GDR_ERR_UNSUPPORTED);
+    x = r; x.z = nullptr; CHECK(gdr_raven_fwd(&x, nullptr) == GDR_ERR_NULL);
+    x = r; x.a = (const float*)((const char*)fake(5) + 4); CHECK(gdr_raven_fwd(&x, nullptr) == GDR_ERR_ALIGN);
+    x = r; x.Sk_out = (float*)((char*)fake(7) + 256); CHECK(gdr_raven_fwd(&x, nullptr) == GDR_ERR_ARG);
+    x = r; x.Sv_out = (float*)fake(7); x.Sk_out = nullptr; CHECK(gdr_raven_fwd(&x, nullptr) == GDR_ERR_ARG);
+    x = r; x.B = 0x7fffffff; x.T = 0x7fffffff; x.H = 0x7fffffff;
+    CHECK(gdr_raven_fwd(&x, nullptr) == GDR_ERR_SHAPE);
+    x = r; x.scale = 1.f / 0.f; CHECK(gdr_raven_fwd(&x, nullptr) == GDR_ERR_UNSUPPORTED);
+    CHECK(gdr_raven_fwd(nullptr, nullptr) == GDR_ERR_NULL);
+    CHECK(gdr::raven::g_nrv == 1);
+  }
 
   for (int st = -1; st < 12; ++st) CHECK(gdr_status_str((gdr_status)st) != nullptr);
   CHECK(gdr_abi_version() == GDR_ABI_VERSION);

@@ -11,15 +11,21 @@ import recurrent_state_memory_amd as gdr
 
 ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
 HEADER = os.path.join(ROOT, "include", "gdr.h")
+RAVEN_HEADER = os.path.join(ROOT, "include", "gdr_raven.h")
 
 FAKE = 0x10000          # aligned, never dereferenced: validation fails first
 MISALIGNED = 0x10004
 
 
 def _declared():
-    src = open(HEADER).read()
-    src = re.sub(r"/\*.*?\*/", "", src, flags=re.S)
-    return sorted(set(re.findall(r"\b(gdr_[a-z_0-9]+)\s*\(", src)))
+    """Functions declared by every header under include/."""
+    names = set()
+    inc = os.path.join(ROOT, "include")
+    for f in sorted(os.listdir(inc)):
+        if f.endswith(".h"):
+            src = re.sub(r"/\*.*?\*/", "", open(os.path.join(inc, f)).read(), flags=re.S)
+            names |= set(re.findall(r"\b(gdr_[a-z_0-9]+)\s*\(", src))
+    return sorted(names)
 
 
 def test_library_loads_and_exports_header_symbols():
@@ -27,7 +33,7 @@ def test_library_loads_and_exports_header_symbols():
     names = _declared()
     assert {"gdr_chunk_fwd", "gdr_chunk_fwd_gated", "gdr_chunk_bwd", "gdr_chunk_bwd_workspace",
             "gdr_step_decode", "gdr_chunk_fwd_workspace", "gdr_status_str",
-            "gdr_abi_version"} <= set(names)
+            "gdr_abi_version", "gdr_chunk_bwd_noalloc", "gdr_raven_fwd"} <= set(names)
     for nm in names:
         assert hasattr(lib, nm), nm
     out = subprocess.run(["nm", "-D", "--defined-only", gdr.LIB_PATH], capture_output=True,
@@ -241,8 +247,10 @@ def test_step_rejects_before_any_hip_call(kw, status):
 def test_struct_layout_matches_header(tmp_path):
     """Field offsets of the ctypes mirrors equal the C compiler's offsetof()."""
     fields = {"gdr_fwd_args": gdr.FwdArgs, "gdr_step_args": gdr.StepArgs,
-              "gdr_gate_args": gdr.GateArgs, "gdr_bwd_args": gdr.BwdArgs}
+              "gdr_gate_args": gdr.GateArgs, "gdr_bwd_args": gdr.BwdArgs,
+              "gdr_raven_args": gdr.RavenArgs}
     lines = ["#include <stdio.h>", "#include <stddef.h>", f'#include "{HEADER}"',
+             f'#include "{RAVEN_HEADER}"',
              "int main(void) {"]
     for cname, cls in fields.items():
         lines.append(f'printf("{cname} size %zu\\n", sizeof({cname}));')
@@ -435,12 +443,69 @@ def test_host_half_under_sanitizers(tmp_path):
            "-fsanitize=address,undefined", "-fno-sanitize-recover=all", "-g",
            os.path.join(ROOT, "tests", "abi_host_harness.cpp"),
            os.path.join(ROOT, "recurrent_state_memory_amd", "csrc", "gdr_api.cpp"),
+           os.path.join(ROOT, "recurrent_state_memory_amd", "csrc", "raven_api.cpp"),
            "-o", str(exe)]
     r = subprocess.run(cmd, capture_output=True, text=True)
     if r.returncode != 0 and "sanitizer" in r.stderr.lower():
         pytest.skip("sanitizer runtime not available: " + r.stderr[-200:])
     assert r.returncode == 0, r.stderr
-    env = dict(os.environ, ASAN_OPTIONS="detect_leaks=1:abort_on_error=1")
-    env.pop("LD_PRELOAD", None)
+    # the environment is passed through unchanged; ASan is told not to insist on
+    # coming first in the library list
+    env = dict(os.environ,
+               ASAN_OPTIONS="detect_leaks=1:abort_on_error=1:verify_asan_link_order=0")
     out = subprocess.run([str(exe)], capture_output=True, text=True, env=env)
     assert out.returncode == 0 and "ABI_HARNESS_OK" in out.stdout, out.stderr
+
+
+# ------------------------------------------------------------ Raven slot memory
+def _good_raven(**kw):
+    r = gdr.RavenArgs()
+    r.B, r.T, r.H, r.dk, r.dv, r.slots, r.topk, r.scale = 2, 70, 3, 128, 128, 64, 8, 0.088
+    for f in ("q", "k", "v", "z", "a", "o"):
+        setattr(r, f, FAKE)
+    for f, val in kw.items():
+        setattr(r, f, val)
+    return r
+
+
+RAVEN_CASES = [
+    (dict(q=None), gdr.GDR_ERR_NULL),
+    (dict(z=None), gdr.GDR_ERR_NULL),
+    (dict(a=None), gdr.GDR_ERR_NULL),
+    (dict(o=None), gdr.GDR_ERR_NULL),
+    (dict(T=0), gdr.GDR_ERR_SHAPE),
+    (dict(topk=0), gdr.GDR_ERR_SHAPE),
+    (dict(topk=9), gdr.GDR_ERR_UNSUPPORTED),
+    (dict(slots=128), gdr.GDR_ERR_UNSUPPORTED),
+    (dict(dk=32, dv=32), gdr.GDR_ERR_UNSUPPORTED),
+    (dict(dk=128, dv=64), gdr.GDR_ERR_UNSUPPORTED),
+    (dict(scale=float("nan")), gdr.GDR_ERR_UNSUPPORTED),
+    (dict(z=MISALIGNED), gdr.GDR_ERR_ALIGN),
+    (dict(Sk0=FAKE, Sk_out=FAKE + 64), gdr.GDR_ERR_ARG),      # partial overlap
+    (dict(Sk_out=FAKE, Sv_out=FAKE), gdr.GDR_ERR_ARG),        # the two states in one buffer
+]
+
+
+@pytest.mark.parametrize("kw,status", RAVEN_CASES)
+def test_raven_rejects_before_any_hip_call(kw, status):
+    assert gdr.call_raven_fwd(_good_raven(**kw)) == status
+
+
+def test_raven_binding_checks():
+    """Good shapes pass every check (then the CPU device is refused); each bad
+    shape or dtype is named."""
+    import torch
+    bf, f32 = torch.bfloat16, torch.float32
+    B, T, H, d, M = 2, 5, 3, 64, 64
+    good = dict(q=torch.zeros(B, T, H, d, dtype=bf), k=torch.zeros(B, T, H, d, dtype=bf),
+                v=torch.zeros(B, T, H, d, dtype=bf), z=torch.zeros(B, T, H, M, dtype=bf),
+                a=torch.zeros(B, T, H, dtype=f32))
+    with pytest.raises(ValueError, match="GPU"):
+        gdr.gdr_raven_fwd(**good, topk=8)
+    for name, val in (("k", torch.zeros(B, T, H, d)), ("z", torch.zeros(B, T, H + 1, M, dtype=bf)),
+                      ("a", torch.zeros(B, T, H, dtype=bf)), ("v", torch.zeros(B, T, 2, d, dtype=bf)),
+                      ("Sk0", torch.zeros(B, H, M, d - 1)), ("Sv0", torch.zeros(B, H, M, d, dtype=bf))):
+        a = dict(good)
+        a[name] = val
+        with pytest.raises(ValueError, match=name):
+            gdr.gdr_raven_fwd(**a, topk=8)
