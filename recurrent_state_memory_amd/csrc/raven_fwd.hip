@@ -95,11 +95,6 @@ __device__ inline unsigned route_key(unsigned u16, int slot) {
   const unsigned ord = (u16 & 0x8000u) ? (~u16 & 0xffffu) : (u16 | 0x8000u);
   return (ord << 16) | (0xffffu - (unsigned)slot);
 }
-__device__ inline float key_value(unsigned key) {
-  const unsigned ord = key >> 16;
-  const unsigned u16 = (ord & 0x8000u) ? (ord & 0x7fffu) : (~ord & 0xffffu);
-  return __uint_as_float(u16 << 16);
-}
 __device__ inline int key_slot(unsigned key) { return (int)(0xffffu - (key & 0xffffu)); }
 
 __device__ inline void ce(unsigned& a, unsigned& b) {   // a >= b after
@@ -128,18 +123,23 @@ __device__ inline void merge8(unsigned (&x)[8], int ctrl) {
   ce(x[0], x[1]); ce(x[2], x[3]); ce(x[4], x[5]); ce(x[6], x[7]);
 }
 
-__device__ inline float sigm(float z) { return 1.f / (1.f + __expf(-z)); }
+// component-wise (a select of the whole struct goes through the stack)
+__device__ inline uint4 keep_if(bool ok, const uint4& x) {
+  return uint4{ok ? x.x : 0u, ok ? x.y : 0u, ok ? x.z : 0u, ok ? x.w : 0u};
+}
+
+__device__ inline float sigm(float z) { return __builtin_amdgcn_rcpf(1.f + __expf(-z)); }
 
 template <int D>
-__global__ __launch_bounds__(NT) void raven_fwd_kernel(RavenParams p) {
+__global__ __launch_bounds__(NT) __attribute__((amdgpu_waves_per_eu(1, 1))) void raven_fwd_kernel(RavenParams p) {
   using O = Op<bf>;
   using S = Sh<D>;
   constexpr int RQ = S::RQ, RT = S::RT, RF = S::RF, RM = S::RM, RK = S::RK;
   constexpr int NCT = D / 16;       // channel tiles of Sk^T held by each wave
   constexpr int VCT = D / 64;       // value-channel tiles of Sv held by each wave
   constexpr int CW = D / 4;         // value channels per wave
-  constexpr int NPC = D / 64;       // 16-byte pieces of q (k, v) per lane per chunk
   constexpr int PPT = D / 8;        // 16-byte pieces per token row
+  constexpr int NPAIR = 16 * PPT;   // (token pair, 8-channel block) units of a chunk
   __shared__ __attribute__((aligned(16))) S sh;
 
   const int tid = threadIdx.x, w = tid >> 6, l = tid & 63, n = l & 15, g = l >> 4;
@@ -173,44 +173,63 @@ __global__ __launch_bounds__(NT) void raven_fwd_kernel(RavenParams p) {
           Sv[st][vt][j] = p.Sv0 ? p.Sv0[sb + (size_t)(16 * st + 4 * g + j) * D + CW * w + 16 * vt + n] : 0.f;
   }
 
-  // ---- raw chunk loads (registers), then into LDS
-  uint4 rq[NPC], rk[NPC], rv[NPC], rz;
+  // ---- raw chunk loads (registers), then into LDS.  Lane (tid < NPAIR) takes
+  // tokens 2tp, 2tp + 1 of channels 8cb .. 8cb + 7, so that the transposed
+  // copies are written as whole dwords (two tokens of one channel).
+  // Tokens past T load from the last token (a valid address, so that no
+  // select waits on the load here) and are zeroed when written to LDS.
+  uint4 rq[2], rk[2], rv[2], rz;
   float ra = 0.f;
+  unsigned okm = 0u;   // bit u: token 2tp + u valid; bit 2: router row valid; bit 3: rate valid
+  const int tp = tid & 15, cb = tid >> 4;
+  const int cbl = tid < NPAIR ? cb : 0;
   auto load_chunk = [&](int c) {
     const int c0 = c * L;
 #pragma unroll
-    for (int u = 0; u < NPC; ++u) {
-      const int pc = tid + NT * u, t = pc / PPT, ch = (pc % PPT) * 8;
-      const bool ok = c0 + t < T;
-      const size_t off = (size_t)(c0 + t) * tok + ch;
-      rq[u] = ok ? *(const uint4*)(qg + off) : uint4{0u, 0u, 0u, 0u};
-      rk[u] = ok ? *(const uint4*)(kg + off) : uint4{0u, 0u, 0u, 0u};
-      rv[u] = ok ? *(const uint4*)(vg + off) : uint4{0u, 0u, 0u, 0u};
+    for (int u = 0; u < 2; ++u) {
+      const int t = c0 + 2 * tp + u;
+      okm = (okm & ~(1u << u)) | ((tid < NPAIR && t < T) ? 1u << u : 0u);
+      const size_t off = (size_t)(t < T ? t : T - 1) * tok + 8 * cbl;
+      rq[u] = *(const uint4*)(qg + off);
+      rk[u] = *(const uint4*)(kg + off);
+      rv[u] = *(const uint4*)(vg + off);
     }
     {
-      const int t = tid >> 3, s8 = (tid & 7) * 8;
-      rz = c0 + t < T ? *(const uint4*)(zg + (size_t)(c0 + t) * H * M + s8) : uint4{0u, 0u, 0u, 0u};
+      const int t = c0 + (tid >> 3), s8 = (tid & 7) * 8;
+      okm = (okm & ~4u) | (t < T ? 4u : 0u);
+      rz = *(const uint4*)(zg + (size_t)(t < T ? t : T - 1) * H * M + s8);
     }
-    ra = (tid < L && c0 + tid < T) ? ag[(size_t)(c0 + tid) * H] : 0.f;
+    {
+      const int t = c0 + (tid & (L - 1));
+      okm = (okm & ~8u) | ((tid < L && t < T) ? 8u : 0u);
+      ra = ag[(size_t)(t < T ? t : T - 1) * H];
+    }
   };
   auto fill_lds = [&]() {
+    if (tid < NPAIR) {
+      const int ch = 8 * cb;
+      const bool ok0 = okm & 1u, ok1 = okm & 2u;
+      const uint4 q0 = keep_if(ok0, rq[0]), q1 = keep_if(ok1, rq[1]);
+      const uint4 ka = keep_if(ok0, rk[0]), kb = keep_if(ok1, rk[1]);
+      const uint4 va = keep_if(ok0, rv[0]), vb = keep_if(ok1, rv[1]);
+      *(uint4*)(sh.Qs + (2 * tp) * RQ + ch) = q0;
+      *(uint4*)(sh.Qs + (2 * tp + 1) * RQ + ch) = q1;
+      *(uint4*)(sh.Ks + (2 * tp) * RQ + ch) = ka;
+      *(uint4*)(sh.Ks + (2 * tp + 1) * RQ + ch) = kb;
+      const uint32_t k0[4] = {ka.x, ka.y, ka.z, ka.w};
+      const uint32_t k1[4] = {kb.x, kb.y, kb.z, kb.w};
+      const uint32_t v0[4] = {va.x, va.y, va.z, va.w};
+      const uint32_t v1[4] = {vb.x, vb.y, vb.z, vb.w};
 #pragma unroll
-    for (int u = 0; u < NPC; ++u) {
-      const int pc = tid + NT * u, t = pc / PPT, ch = (pc % PPT) * 8;
-      *(uint4*)(sh.Qs + t * RQ + ch) = rq[u];
-      *(uint4*)(sh.Ks + t * RQ + ch) = rk[u];
-      const uint32_t kw[4] = {rk[u].x, rk[u].y, rk[u].z, rk[u].w};
-      const uint32_t vw[4] = {rv[u].x, rv[u].y, rv[u].z, rv[u].w};
-#pragma unroll
-      for (int e = 0; e < 4; ++e) {
-        sh.Kt[(ch + 2 * e) * RT + t] = __builtin_bit_cast(bf, (unsigned short)(kw[e] & 0xffffu));
-        sh.Kt[(ch + 2 * e + 1) * RT + t] = __builtin_bit_cast(bf, (unsigned short)(kw[e] >> 16));
-        sh.Vt[(ch + 2 * e) * RT + t] = __builtin_bit_cast(bf, (unsigned short)(vw[e] & 0xffffu));
-        sh.Vt[(ch + 2 * e + 1) * RT + t] = __builtin_bit_cast(bf, (unsigned short)(vw[e] >> 16));
+      for (int e = 0; e < 4; ++e) {   // channels ch + 2e (low halves) and ch + 2e + 1 (high)
+        *(uint32_t*)(sh.Kt + (ch + 2 * e) * RT + 2 * tp) = (k0[e] & 0xffffu) | (k1[e] << 16);
+        *(uint32_t*)(sh.Kt + (ch + 2 * e + 1) * RT + 2 * tp) = (k0[e] >> 16) | (k1[e] & 0xffff0000u);
+        *(uint32_t*)(sh.Vt + (ch + 2 * e) * RT + 2 * tp) = (v0[e] & 0xffffu) | (v1[e] << 16);
+        *(uint32_t*)(sh.Vt + (ch + 2 * e + 1) * RT + 2 * tp) = (v0[e] >> 16) | (v1[e] & 0xffff0000u);
       }
     }
-    *(uint4*)(sh.Zs + (tid >> 3) * M + (tid & 7) * 8) = rz;
-    if (tid < L) sh.As[tid] = ra;
+    *(uint4*)(sh.Zs + (tid >> 3) * M + (tid & 7) * 8) = keep_if(okm & 4u, rz);
+    if (tid < L) sh.As[tid] = (okm & 8u) ? ra : 0.f;
   };
 
   load_chunk(0);
@@ -237,33 +256,45 @@ __global__ __launch_bounds__(NT) void raven_fwd_kernel(RavenParams p) {
       merge8(top, 0x4e);
       merge8(top, 0x141);
       unsigned thr = top[0];
-      float ssum = 0.f;
       int mine = -1;
 #pragma unroll
       for (int j = 0; j < 8; ++j) {
         if (j == K - 1) thr = top[j];
-        if (j < K) ssum += sigm(key_value(top[j]));
         if (j == g8) mine = j < K ? key_slot(top[j]) : -1;
       }
+      // sigmoid of each own slot; the selected ones' sum over the token's 8 lanes
+      float sg[8], part = 0.f;
+#pragma unroll
+      for (int e = 0; e < 8; ++e) {
+        const uint32_t bits = (e & 1 ? zw[e >> 1] >> 16 : zw[e >> 1]) & 0xffffu;
+        sg[e] = sigm(__uint_as_float(bits << 16));
+        part += own[e] >= thr ? sg[e] : 0.f;
+      }
+      part += dpp_f(part, 0xb1);
+      part += dpp_f(part, 0x4e);
+      part += dpp_f(part, 0x141);
       const float at = sh.As[t];
-      const float inv = 1.f / ssum;
+      const float inv = __builtin_amdgcn_rcpf(part);
       float lv[8];
 #pragma unroll
-      for (int e = 0; e < 8; ++e)
-        lv[e] = own[e] >= thr ? at * (sigm(key_value(own[e])) * inv) : 0.f;
+      for (int e = 0; e < 8; ++e) lv[e] = own[e] >= thr ? at * (sg[e] * inv) : 0.f;
       *(f32x4*)(sh.lam + t * RF + 8 * g8) = f32x4{lv[0], lv[1], lv[2], lv[3]};
       *(f32x4*)(sh.lam + t * RF + 8 * g8 + 4) = f32x4{lv[4], lv[5], lv[6], lv[7]};
       sh.sel[t * 8 + g8] = mine;
     }
     // ---------------- q . Sk_0 (accumulators as the B operand) and q . k
+    {
+      typename O::frag skb[D / 32];
+#pragma unroll
+      for (int ks = 0; ks < D / 32; ++ks) skb[ks] = O::from_acc(SkT[2 * ks], SkT[2 * ks + 1]);
 #pragma unroll
     for (int tt = 0; tt < 2; ++tt) {
       f32x4 acc = {0.f, 0.f, 0.f, 0.f};
 #pragma unroll
-      for (int ks = 0; ks < D / 32; ++ks)
-        O::mma(acc, load_cb<bf>(sh.Qs, RQ, 16 * tt, 32 * ks), O::from_acc(SkT[2 * ks], SkT[2 * ks + 1]));
+      for (int ks = 0; ks < D / 32; ++ks) O::mma(acc, load_cb<bf>(sh.Qs, RQ, 16 * tt, 32 * ks), skb[ks]);
 #pragma unroll
       for (int j = 0; j < 4; ++j) sh.G[(16 * tt + 4 * g + j) * RF + 16 * w + n] = acc[j];
+    }
     }
     {
       const int tt = w == 0 ? 0 : 1, st = w == 2 ? 1 : 0;   // tiles (0,0) (1,0) (1,1); wave 3: (0,1)
@@ -316,7 +347,7 @@ __global__ __launch_bounds__(NT) void raven_fwd_kernel(RavenParams p) {
         const bf ehi = (bf)e;
         eh[u] = ehi;
         el[u] = (bf)(e - (float)ehi);
-        const bf bs = (bf)(om / lc);   // used only where pend >= e^-40 (so lc >= e^-40)
+        const bf bs = (bf)(om * __builtin_amdgcn_rcpf(lc));   // used only where pend >= e^-40
         bb[u] = bs;
         sh.Bsi[t * RM + i] = bs;
       }
@@ -380,7 +411,7 @@ __global__ __launch_bounds__(NT) void raven_fwd_kernel(RavenParams p) {
       sum += dpp_f(sum, 0xb1);
       sum += dpp_f(sum, 0x4e);
       sum += dpp_f(sum, 0x141);
-      const float inv = 1.f / sum;
+      const float inv = __builtin_amdgcn_rcpf(sum);
       bf16x8 pl;
 #pragma unroll
       for (int e = 0; e < 8; ++e) {
@@ -428,14 +459,18 @@ __global__ __launch_bounds__(NT) void raven_fwd_kernel(RavenParams p) {
     }
     lds_barrier();
     // ---------------- output (old Sv in the accumulators as the B operand)
+    typename O::frag svb[2][VCT];
+#pragma unroll
+    for (int ks = 0; ks < 2; ++ks)
+#pragma unroll
+      for (int vt = 0; vt < VCT; ++vt) svb[ks][vt] = O::from_acc(Sv[2 * ks][vt], Sv[2 * ks + 1][vt]);
 #pragma unroll
     for (int tt = 0; tt < 2; ++tt) {
 #pragma unroll
       for (int vt = 0; vt < VCT; ++vt) {
         f32x4 acc = {0.f, 0.f, 0.f, 0.f};
 #pragma unroll
-        for (int ks = 0; ks < 2; ++ks)
-          O::mma(acc, load_cb<bf>(sh.PL, RM, 16 * tt, 32 * ks), O::from_acc(Sv[2 * ks][vt], Sv[2 * ks + 1][vt]));
+        for (int ks = 0; ks < 2; ++ks) O::mma(acc, load_cb<bf>(sh.PL, RM, 16 * tt, 32 * ks), svb[ks][vt]);
         O::mma(acc, load_plain<bf>(sh.Ab, RT, 16 * tt, 0), load_plain<bf>(sh.Vt, RT, CW * w + 16 * vt, 0));
 #pragma unroll
         for (int j = 0; j < 4; ++j) sh.Os[(16 * tt + 4 * g + j) * RQ + CW * w + 16 * vt + n] = (bf)acc[j];
