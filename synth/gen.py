@@ -19,7 +19,9 @@ long  1, 16, 32768, 128               128    bf16         decay + content erase
 rot   4, 16, 8192, 128 (+ decode)     64     bf16         2x2 rotation blocks
 ====  ==============================  =====  ===========  ====================
 
-The Raven slot-memory forward has its own workload (``RAVEN_WORKLOADS``:
+The partial-permutation forward has ``PERM_WORKLOADS`` (the layer shape with a
+random stack move per token and head) and ``generate_perm``.  The Raven
+slot-memory forward has its own workload (``RAVEN_WORKLOADS``:
 the layer shape B=8, H=16, T=4096, d=128 with 64 slots and top-8 routing) and
 generator (``generate_raven``).
 
@@ -95,7 +97,7 @@ class Workload:
     dv: int
     chunk: int
     io: str            # "f32" | "bf16"
-    decay: str         # "diag" | "rot2" | "dihedral" (rot2 with reflection blocks)
+    decay: str         # "diag" | "rot2" | "dihedral" (rot2 with reflection blocks) | "perm"
     content: bool      # content-aware erase
     seed: int
     rank: int = 16     # low-rank width of the erase projection
@@ -358,3 +360,54 @@ def generate_raven(wl: RavenWorkload, T: Optional[int] = None,
     a = (np.float32(-wl.a_scale) * _softplus(x)).astype(np.float32)
     return RavenInputs(wl, bf16_round(_l2_normalise(q)), bf16_round(_l2_normalise(k)),
                        bf16_round(v), bf16_round(z), a)
+
+
+# --------------------------------------------------------------------------
+# partial-permutation transitions (bounded-stack moves)
+# --------------------------------------------------------------------------
+PERM_WORKLOADS = {
+    # the layer shape with a stack move per (token, head): push (every channel one
+    # deeper, channel 0 emptied), pop (one channel up) or stay, with probability 1/3 each
+    "stack": Workload("stack", 8, 16, 4096, 128, 128, 64, "bf16", "perm", False, 7),
+}
+
+
+@dataclasses.dataclass
+class PermInputs:
+    """fp32 host arrays (q, k, v hold bf16 values) and int16 source maps."""
+    wl: Workload
+    q: np.ndarray      # [B,T,H,dk], L2-normalised per token
+    k: np.ndarray      # [B,T,H,dk], L2-normalised per token
+    v: np.ndarray      # [B,T,H,dv]
+    beta: np.ndarray   # [B,T,H]
+    w: np.ndarray      # [B,T,H]
+    src: np.ndarray    # [B,T,H,dk] int16: column j of S D_t is column src[j] of S (-1: zero)
+
+
+def stack_moves(op: np.ndarray, dk: int) -> np.ndarray:
+    """Source maps of stack moves: op 0 = push (src[j] = j - 1, src[0] = -1),
+    1 = pop (src[j] = j + 1, src[dk-1] = -1), 2 = stay (src[j] = j)."""
+    j = np.arange(dk)
+    push = np.where(j >= 1, j - 1, -1)
+    pop = np.where(j + 1 < dk, j + 1, -1)
+    stay = j
+    table = np.stack([push, pop, stay]).astype(np.int16)
+    return table[op]
+
+
+def generate_perm(wl: Workload, T: Optional[int] = None, B: Optional[int] = None) -> PermInputs:
+    """Draw order: q, k, v, beta-logit, w-logit (fp32 standard normal), then the
+    move per (b, t, h) uniform over {push, pop, stay}.  q, k L2-normalised and
+    rounded to bf16, v rounded to bf16, beta = w = sigmoid."""
+    if T is not None or B is not None:
+        wl = wl.replace(T=T if T is not None else wl.T, B=B if B is not None else wl.B)
+    rng = np.random.default_rng(wl.seed)
+    Bn, Tn, H, dk, dv = wl.B, wl.T, wl.H, wl.dk, wl.dv
+    q = rng.standard_normal((Bn, Tn, H, dk), dtype=np.float32)
+    k = rng.standard_normal((Bn, Tn, H, dk), dtype=np.float32)
+    v = rng.standard_normal((Bn, Tn, H, dv), dtype=np.float32)
+    b_logit = rng.standard_normal((Bn, Tn, H), dtype=np.float32)
+    w_logit = rng.standard_normal((Bn, Tn, H), dtype=np.float32)
+    op = rng.integers(0, 3, (Bn, Tn, H))
+    return PermInputs(wl, bf16_round(_l2_normalise(q)), bf16_round(_l2_normalise(k)),
+                      bf16_round(v), _sigmoid(b_logit), _sigmoid(w_logit), stack_moves(op, dk))
