@@ -16,7 +16,7 @@ kernel (algorithmic bytes per launch / measured launch time, against the HBM
 peak) and a CPU baseline: the fp64 oracle timed on a bounded sample of the
 same workload on this host.
 
-Other workloads (``--workload small|rot|dihedral|long|decode|raven|copy``) are for profiling
+Other workloads (``--workload small|rot|dihedral|long|decode|raven|stack|copy``) are for profiling
 and are not the reported metric; ``copy`` is a plain device copy of known size
 used to calibrate the HBM byte counters.
 """
@@ -37,6 +37,7 @@ METRIC = "tokens/sec gated-delta chunk fwd (H=16,d=128,T=4096) + % MFMA/HBM roof
 HBM_PEAK_GBS = 8000.0          # MI355X HBM3E
 MFMA_BF16_PEAK_TFS = 2500.0    # dense bf16 matrix peak
 MFMA_F32_PEAK_TFS = 157.3
+VALU_F32_PEAK_TFS = 157.3      # fp32 vector peak: 256 CUs x 128 FMA per cycle x 2 flops x 2.4 GHz
 TRAFFIC_FILE = os.path.join(ROOT, "profiles", "gdr_fwd_pipe_kernel_layer_traffic.txt")
 TRAFFIC_FILE_GATED = os.path.join(ROOT, "profiles", "gdr_fwd_pipe_kernel_layer_gated_traffic.txt")
 KERNEL_SRCS = [os.path.join(ROOT, "recurrent_state_memory_amd", "csrc", f)
@@ -264,6 +265,67 @@ def cpu_baseline_raven(wl, x, budget_s: float = 15.0):
                        f"first {T_s} of {wl.T} tokens, {secs:.1f} s")}
 
 
+def perm_bytes(wl) -> int:
+    """Bytes the partial-permutation forward must move at least once: q, k, v
+    (bf16), the int16 source maps, beta and w (fp32) in; o (bf16) and the final
+    state (fp32) out."""
+    per_th = (2 * wl.dk + wl.dv) * 2 + 2 * wl.dk + 8 + 2 * wl.dv
+    return per_th * wl.B * wl.T * wl.H + 4 * wl.dv * wl.dk * wl.B * wl.H
+
+
+def perm_flops(wl) -> float:
+    """fp32 vector flops per launch: X k, the rank-1 update and S q, 2 d_v d_k
+    each per token-head (the column selection moves data only)."""
+    return 6.0 * wl.dv * wl.dk * wl.B * wl.T * wl.H
+
+
+def _perm_closure(wl):
+    import torch
+    import recurrent_state_memory_amd as gdr
+    from synth.gen import generate_perm
+    x = generate_perm(wl)
+    bf = torch.bfloat16
+    q, k, v = (_to_dev(t, bf) for t in (x.q, x.k, x.v))
+    w, beta = _to_dev(x.w), _to_dev(x.beta)
+    src = torch.from_numpy(x.src).to("cuda")
+    o = torch.empty((wl.B, wl.T, wl.H, wl.dv), dtype=bf, device="cuda")
+    S = torch.empty((wl.B, wl.H, wl.dv, wl.dk), dtype=torch.float32, device="cuda")
+
+    def step():
+        gdr.gdr_perm_fwd(q, k, v, w, src, beta, o=o, S_out=S)
+    return step, x
+
+
+def cpu_baseline_perm(wl, x, budget_s: float = 15.0):
+    """The partial-permutation oracle on this host's cores (as ``cpu_baseline``)."""
+    import concurrent.futures as cf
+    import numpy as np
+    from threadpoolctl import threadpool_limits
+    from oracle import perm
+
+    workers = max(1, min(16, len(os.sched_getaffinity(0)), wl.B))
+
+    def run(b, T_s):
+        sl = (slice(b, b + 1), slice(0, T_s))
+        return perm.forward(x.q[sl], x.k[sl], x.v[sl], x.w[sl], x.src[sl], x.beta[sl])[0]
+
+    with threadpool_limits(limits=1), cf.ThreadPoolExecutor(max_workers=workers) as ex:
+        probe = 16
+        t0 = time.perf_counter()
+        list(ex.map(lambda b: run(b, probe), range(wl.B)))
+        per_tok = (time.perf_counter() - t0) / probe
+        T_s = int(max(32, min(wl.T, budget_s / max(per_tok, 1e-9))))
+        t0 = time.perf_counter()
+        outs = list(ex.map(lambda b: run(b, T_s), range(wl.B)))
+        secs = time.perf_counter() - t0
+    assert all(np.all(np.isfinite(o)) for o in outs)
+    return {"value": round(wl.B * T_s / secs, 2), "unit": "tokens/s", "cores": workers,
+            "kind": "oracle",
+            "sample": (f"fp64 numpy token-by-token partial-permutation oracle, {workers} worker "
+                       f"threads (BLAS single-threaded) on {_cpu_model()}, all {wl.B}x{wl.H} heads, "
+                       f"first {T_s} of {wl.T} tokens, {secs:.1f} s")}
+
+
 def _decode_closure():
     import torch
     import recurrent_state_memory_amd as gdr
@@ -381,7 +443,7 @@ def main(argv=None):
     ap.add_argument("--warmup", type=int, default=150)
     ap.add_argument("--workload", default="layer",
                     choices=["layer", "small", "rot", "dihedral", "long", "tiny", "decode", "copy",
-                             "raven"])
+                             "raven", "stack"])
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--bwd", action="store_true",
                     help="gdr_chunk_bwd: the backward (forward recompute + reverse blocks + reduction)")
@@ -452,6 +514,36 @@ def main(argv=None):
         }
         if not a.no_cpu_baseline:
             out["cpu_baseline"] = cpu_baseline_raven(wl, x)
+        print(json.dumps(out))
+        return 0
+
+    if a.workload == "stack":
+        from synth.gen import PERM_WORKLOADS
+        wl = PERM_WORKLOADS["stack"]
+        step, x = _perm_closure(wl)
+        secs, wall = _time(step, a.steps, a.warmup)
+        per = secs / a.steps
+        nbytes = perm_bytes(wl)
+        fl = perm_flops(wl)
+        out = {
+            "metric": "tokens/sec delta rule with partial-permutation transitions fwd",
+            "value": round(wl.B * wl.T / per, 1), "unit": "tokens/s", "n_gpus": 1,
+            "steps": a.steps, "warmup": a.warmup, "ms_per_step": round(per * 1e3, 4),
+            "higher_is_better": True, "scaling": "weak", "vs_baseline": None, "dtype": "f32",
+            "data": "synthetic (seeded; q,k L2-normalised, sigmoid gates, random stack moves)",
+            "config": {"workload": (f"stack: B={wl.B} H={wl.H} T={wl.T} d_k=d_v={wl.dk}, bf16 "
+                                    "q/k/v, int16 source maps (push/pop/stay), fp32 state and "
+                                    "arithmetic, token by token"),
+                       "global_batch": wl.B, "seq_len": wl.T, "parallelism": "single GPU"},
+            "roofline": {"bound": "alu", "achieved": round(fl / per / 1e12, 2),
+                         "peak": VALU_F32_PEAK_TFS, "unit": "TFLOP/s",
+                         "frac": round(fl / per / 1e12 / VALU_F32_PEAK_TFS, 4), "traffic": None},
+            "roofline_hbm": {"achieved": round(nbytes / per / 1e9, 1), "peak": HBM_PEAK_GBS,
+                             "unit": "GB/s", "frac": round(nbytes / per / 1e9 / HBM_PEAK_GBS, 4)},
+            "wall_s_timed_region": round(wall, 4),
+        }
+        if not a.no_cpu_baseline:
+            out["cpu_baseline"] = cpu_baseline_perm(wl, x)
         print(json.dumps(out))
         return 0
 

@@ -15,6 +15,8 @@ Entry points (same names as the C ABI):
 * ``gdr_step_decode`` -- one token on a batch of states, in place, returns o
 * ``gdr_raven_fwd``   -- the Raven routing slot memory (include/gdr_raven.h),
   returns (o, Sk_out, Sv_out)
+* ``gdr_perm_fwd``    -- the delta rule with partial-permutation transitions
+  (include/gdr_perm.h), returns (o, S_out)
 """
 from __future__ import annotations
 
@@ -85,6 +87,15 @@ class RavenArgs(ctypes.Structure):
     ]
 
 
+class PermArgs(ctypes.Structure):
+    """Mirror of ``gdr_perm_args`` (include/gdr_perm.h)."""
+    _fields_ = [
+        ("B", _i32), ("T", _i32), ("H", _i32), ("dk", _i32), ("dv", _i32),
+        ("q", _vp), ("k", _vp), ("v", _vp), ("src", _vp), ("beta", _vp), ("w", _vp),
+        ("S0", _vp), ("o", _vp), ("S_out", _vp),
+    ]
+
+
 class GdrError(RuntimeError):
     def __init__(self, status: int, msg: str):
         super().__init__(f"gdr status {status}: {msg}")
@@ -120,6 +131,8 @@ def load_library(path: Optional[str] = None) -> ctypes.CDLL:
     lib.gdr_step_decode.restype = ctypes.c_int
     lib.gdr_raven_fwd.argtypes = [ctypes.POINTER(RavenArgs), _vp]
     lib.gdr_raven_fwd.restype = ctypes.c_int
+    lib.gdr_perm_fwd.argtypes = [ctypes.POINTER(PermArgs), _vp]
+    lib.gdr_perm_fwd.restype = ctypes.c_int
     lib.gdr_status_str.argtypes = [ctypes.c_int]
     lib.gdr_status_str.restype = ctypes.c_char_p
     lib.gdr_abi_version.argtypes = []
@@ -219,6 +232,14 @@ def call_raven_fwd(args: RavenArgs, stream=None) -> int:
     s = stream if isinstance(stream, ctypes.c_void_p) else (
         ctypes.c_void_p(0) if stream is None else _stream(stream))
     return lib.gdr_raven_fwd(ctypes.byref(args), s)
+
+
+def call_perm_fwd(args: PermArgs, stream=None) -> int:
+    """Raw call with a filled ``PermArgs``; returns the status code."""
+    lib = load_library()
+    s = stream if isinstance(stream, ctypes.c_void_p) else (
+        ctypes.c_void_p(0) if stream is None else _stream(stream))
+    return lib.gdr_perm_fwd(ctypes.byref(args), s)
 
 
 def call_step_decode(args: StepArgs, stream=None) -> int:
@@ -504,3 +525,39 @@ def gdr_raven_fwd(q, k, v, z, a, *, topk, scale=None, Sk0=None, Sv0=None, o=None
     r.Sk0, r.Sv0, r.o, r.Sk_out, r.Sv_out = map(_ptr, (Sk0, Sv0, o, Sk_out, Sv_out))
     _check(call_raven_fwd(r, _stream(stream)))
     return o, Sk_out, Sv_out
+
+
+def gdr_perm_fwd(q, k, v, w, src, beta, *, S0=None, o=None, S_out=None, return_state=True,
+                 stream=None):
+    """Delta rule with partial-permutation transitions (see ``gdr_perm_fwd`` in
+    include/gdr_perm.h): column j of S D_t is column src[j] of S (zero for a
+    value outside [0, dk)).
+
+    q, k [B,T,H,dk], v [B,T,H,dv] bf16; w, beta fp32 [B,T,H]; src int16
+    [B,T,H,dk]; S0 fp32 [B,H,dv,dk] or None.  Returns (o [B,T,H,dv] bf16, S_out).
+    """
+    import torch
+    if q.dim() != 4 or k.dim() != 4 or v.dim() != 4:
+        raise ValueError("gdr: q, k and v must be [B,T,H,d]")
+    B, T, H, dk = q.shape
+    dv = v.shape[-1]
+    bf, f32 = torch.bfloat16, torch.float32
+    _expect(q, "q", (B, T, H, dk), bf)
+    _expect(k, "k", (B, T, H, dk), bf)
+    _expect(v, "v", (B, T, H, dv), bf)
+    _expect(src, "src", (B, T, H, dk), torch.int16)
+    _expect(w, "w", (B, T, H), f32)
+    _expect(beta, "beta", (B, T, H), f32)
+    _expect(S0, "S0", (B, H, dv, dk), f32, required=False)
+    if o is None:
+        o = torch.empty((B, T, H, dv), dtype=bf, device=q.device)
+    _expect(o, "o", (B, T, H, dv), bf)
+    if S_out is None and return_state:
+        S_out = torch.empty((B, H, dv, dk), dtype=f32, device=q.device)
+    _expect(S_out, "S_out", (B, H, dv, dk), f32, required=False)
+    a = PermArgs()
+    a.B, a.T, a.H, a.dk, a.dv = B, T, H, dk, dv
+    a.q, a.k, a.v, a.src, a.beta, a.w = map(_ptr, (q, k, v, src, beta, w))
+    a.S0, a.o, a.S_out = _ptr(S0), _ptr(o), _ptr(S_out)
+    _check(call_perm_fwd(a, _stream(stream)))
+    return o, S_out

@@ -1,0 +1,242 @@
+// perm_fwd.hip -- delta rule with partial-permutation transitions, gfx950.
+//
+// SFDA technical summary, finite-state expressivity: partial permutations as
+// the structured control realise a bounded stack.  Per token the key-axis
+// transition selects columns of the state (column j <- column src[j], or zero),
+// then the delta-rule erase and write follow:
+//
+//   X = S D_t;  S = X + beta (w v - X k) k^T;  o = S q.
+//
+// Products of such transitions are singular (a dropped channel never comes
+// back), so the split chunk form (which needs Gamma^-1) does not exist here;
+// the kernel walks the tokens in order.  Value rows evolve independently under
+// key-axis transitions, so every row runs on its own: a wave carries 8 rows
+// (8 lanes per row, d_k/8 channels per lane, fp32 in registers) and needs no
+// other wave within a chunk -- the column selection goes through the wave's own
+// LDS row buffer (a source outside [0, d_k) is mapped at staging to a column
+// that always holds 0, so the gather has no test), the two dot products through
+// DPP butterflies inside each group of 8 lanes.  Workgroups (one head, 32 value
+// rows) stage 16 tokens of k, q (as fp32), the source maps, v, beta and w in
+// LDS, with the next chunk's loads in flight; the value blocks of one head
+// share an XCD, so keys, queries and maps come from its L2 after the first
+// reader.
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+#include "perm_kernels.h"
+
+namespace gdr {
+namespace perm {
+namespace {
+
+using bf = __bf16;
+constexpr int L = 16;      // tokens per staged chunk
+constexpr int NT = 256;    // 4 waves x 8 rows = 32 value rows per workgroup
+constexpr int RPW = 8;     // rows per wave (8 lanes per row)
+constexpr int ROWS = 4 * RPW;
+
+template <int D>
+struct Sh {
+  float Kc[L * D];
+  float Qc[L * D];
+  int16_t Sc[L * D];       // source channel, or D (the zero column) where there is none
+  bf Vc[L * ROWS];
+  float Bc[L];             // beta
+  float Wc[L];             // w
+  float Rb[4][RPW][D + 4]; // per wave, per row: the row for the column selection; [D] = 0
+  bf Oc[L * ROWS];
+};
+
+__device__ inline float dpp_f(float x, int ctrl) {
+  int r;
+  const int u = __float_as_int(x);
+  if (ctrl == 0xb1) r = __builtin_amdgcn_mov_dpp(u, 0xb1, 0xf, 0xf, false);         // lane ^ 1
+  else if (ctrl == 0x4e) r = __builtin_amdgcn_mov_dpp(u, 0x4e, 0xf, 0xf, false);    // lane ^ 2
+  else r = __builtin_amdgcn_mov_dpp(u, 0x141, 0xf, 0xf, false);                     // 7 - lane in 8
+  return __int_as_float(r);
+}
+// sum over 8 aligned lanes; every lane gets the same value
+__device__ inline float row_sum(float x) {
+  x += dpp_f(x, 0xb1);
+  x += dpp_f(x, 0x4e);
+  x += dpp_f(x, 0x141);
+  return x;
+}
+
+__device__ inline float bf_lo(uint32_t u) { return __uint_as_float(u << 16); }
+__device__ inline float bf_hi(uint32_t u) { return __uint_as_float(u & 0xffff0000u); }
+__device__ inline uint32_t src_fix(uint32_t pair, int d) {   // two int16 sources -> [0, d]
+  const int a = (int)(int16_t)(pair & 0xffffu), b = (int)(int16_t)(pair >> 16);
+  const uint32_t ua = (a >= 0 && a < d) ? (uint32_t)a : (uint32_t)d;
+  const uint32_t ub = (b >= 0 && b < d) ? (uint32_t)b : (uint32_t)d;
+  return ua | (ub << 16);
+}
+
+template <int D>
+__global__ __launch_bounds__(NT) void perm_fwd_kernel(PermParams p) {
+  constexpr int CPL = D / 8;           // key channels per lane
+  constexpr int PPT = D / 8;           // 16-byte pieces per token row (bf16 / int16)
+  constexpr int NPIECE = L * PPT;      // such pieces per chunk per tensor (<= NT)
+  __shared__ __attribute__((aligned(16))) Sh<D> sh;
+
+  // value blocks of one head on one XCD (workgroup ids 8 apart)
+  const int NVB = p.DV / ROWS;
+  const int id = blockIdx.x, xcd = id & 7, vb = (id >> 3) % NVB, grp = (id >> 3) / NVB;
+  const int bh = grp * 8 + xcd;
+  if (bh >= p.B * p.H) return;
+  const int b = bh / p.H, h = bh % p.H;
+  const int T = p.T, H = p.H, DV = p.DV, v0 = vb * ROWS;
+  const int tid = threadIdx.x, w = tid >> 6, l = tid & 63, r = l >> 3, cg = l & 7;
+  const int vrow = v0 + RPW * w + r;
+  const size_t row0 = (size_t)b * T * H + h;
+  const bf* qg = static_cast<const bf*>(p.q) + row0 * D;
+  const bf* kg = static_cast<const bf*>(p.k) + row0 * D;
+  const bf* vg = static_cast<const bf*>(p.v) + row0 * DV + v0;
+  const int16_t* sg = p.src + row0 * D;
+  const float* betag = p.beta + row0;
+  const float* wg = p.w + row0;
+  bf* og = static_cast<bf*>(p.o) + row0 * DV + v0;
+  const size_t tokd = (size_t)H * D, tokv = (size_t)H * DV;
+
+  float x[CPL];
+#pragma unroll
+  for (int e = 0; e < CPL; ++e) x[e] = 0.f;
+  if (p.S0) {
+    const size_t so = ((size_t)bh * DV + vrow) * D + cg * CPL;
+#pragma unroll
+    for (int e = 0; e < CPL; e += 4) {
+      const float4 s4 = *(const float4*)(p.S0 + so + e);
+      x[e] = s4.x;
+      x[e + 1] = s4.y;
+      x[e + 2] = s4.z;
+      x[e + 3] = s4.w;
+    }
+  }
+  float* rbuf = sh.Rb[w][r];
+  if (cg == 0) rbuf[D] = 0.f;   // the zero column
+
+  // ---- chunk loads into registers (tokens past T read the last token; the
+  // token loop never reaches them), then into LDS
+  uint4 rk, rq, rs, rv;
+  float rb = 0.f;
+  const int pt = tid / PPT, pch = (tid % PPT) * 8;   // piece of k, q, src (tid < NPIECE)
+  auto load_chunk = [&](int c) {
+    const int c0 = c * L;
+    {
+      const int t = c0 + (tid < NPIECE ? pt : 0);
+      const size_t off = (size_t)(t < T ? t : T - 1) * tokd + (tid < NPIECE ? pch : 0);
+      rk = *(const uint4*)(kg + off);
+      rq = *(const uint4*)(qg + off);
+      rs = *(const uint4*)(sg + off);
+    }
+    {
+      const int t = c0 + ((tid >> 2) & (L - 1));
+      rv = *(const uint4*)(vg + (size_t)(t < T ? t : T - 1) * tokv + 8 * (tid & 3));
+    }
+    {
+      const int t = c0 + (tid & (L - 1));
+      const size_t off = (size_t)(t < T ? t : T - 1) * H;
+      rb = (tid & L) ? wg[off] : betag[off];
+    }
+  };
+  auto fill_lds = [&]() {
+    if (tid < NPIECE) {
+      float* kd = sh.Kc + pt * D + pch;
+      float* qd = sh.Qc + pt * D + pch;
+      *(float4*)kd = float4{bf_lo(rk.x), bf_hi(rk.x), bf_lo(rk.y), bf_hi(rk.y)};
+      *(float4*)(kd + 4) = float4{bf_lo(rk.z), bf_hi(rk.z), bf_lo(rk.w), bf_hi(rk.w)};
+      *(float4*)qd = float4{bf_lo(rq.x), bf_hi(rq.x), bf_lo(rq.y), bf_hi(rq.y)};
+      *(float4*)(qd + 4) = float4{bf_lo(rq.z), bf_hi(rq.z), bf_lo(rq.w), bf_hi(rq.w)};
+      *(uint4*)(sh.Sc + pt * D + pch) =
+          uint4{src_fix(rs.x, D), src_fix(rs.y, D), src_fix(rs.z, D), src_fix(rs.w, D)};
+    }
+    if (tid < 4 * L) *(uint4*)(sh.Vc + (tid >> 2) * ROWS + 8 * (tid & 3)) = rv;
+    if (tid < L) sh.Bc[tid] = rb;
+    else if (tid < 2 * L) sh.Wc[tid - L] = rb;
+  };
+
+  const int nchunks = (T + L - 1) / L;
+  load_chunk(0);
+  fill_lds();
+  if (nchunks > 1) load_chunk(1);
+  __syncthreads();
+
+  for (int c = 0; c < nchunks; ++c) {
+    const int c0 = c * L;
+    const int tn = T - c0 < L ? T - c0 : L;
+#pragma unroll 1
+    for (int t = 0; t < tn; ++t) {
+      const int base = t * D + cg * CPL;
+      // column selection through this row's LDS buffer (source D reads the zero)
+#pragma unroll
+      for (int e = 0; e < CPL; e += 4)
+        *(float4*)(rbuf + cg * CPL + e) = float4{x[e], x[e + 1], x[e + 2], x[e + 3]};
+      float xs[CPL], kf[CPL], qf[CPL];
+#pragma unroll
+      for (int e = 0; e < CPL; e += 8) {
+        const uint4 s4 = *(const uint4*)(sh.Sc + base + e);
+        const uint32_t sw[4] = {s4.x, s4.y, s4.z, s4.w};
+#pragma unroll
+        for (int u = 0; u < 8; ++u) xs[e + u] = rbuf[u & 1 ? sw[u >> 1] >> 16 : sw[u >> 1] & 0xffffu];
+      }
+#pragma unroll
+      for (int e = 0; e < CPL; e += 4) {
+        const float4 k4 = *(const float4*)(sh.Kc + base + e);
+        const float4 q4 = *(const float4*)(sh.Qc + base + e);
+        kf[e] = k4.x; kf[e + 1] = k4.y; kf[e + 2] = k4.z; kf[e + 3] = k4.w;
+        qf[e] = q4.x; qf[e + 1] = q4.y; qf[e + 2] = q4.z; qf[e + 3] = q4.w;
+      }
+      float a4[4] = {0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+      for (int e = 0; e < CPL; ++e) a4[e & 3] += xs[e] * kf[e];
+      const float y = row_sum((a4[0] + a4[1]) + (a4[2] + a4[3]));
+      const float vr = (float)sh.Vc[t * ROWS + RPW * w + r];
+      const float coef = sh.Bc[t] * (sh.Wc[t] * vr - y);   // beta (w v - X k)
+      float b4[4] = {0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+      for (int e = 0; e < CPL; ++e) {
+        x[e] = xs[e] + coef * kf[e];
+        b4[e & 3] += x[e] * qf[e];
+      }
+      const float op = row_sum((b4[0] + b4[1]) + (b4[2] + b4[3]));
+      if (cg == 0) sh.Oc[t * ROWS + RPW * w + r] = (bf)op;
+    }
+    __syncthreads();
+    if (tid < 4 * tn) {
+      const int t = tid >> 2;
+      *(uint4*)(og + (size_t)(c0 + t) * tokv + 8 * (tid & 3)) =
+          *(const uint4*)(sh.Oc + t * ROWS + 8 * (tid & 3));
+    }
+    if (c + 1 < nchunks) {
+      fill_lds();
+      if (c + 2 < nchunks) load_chunk(c + 2);
+    }
+    __syncthreads();
+  }
+
+  if (p.S_out) {
+    const size_t so = ((size_t)bh * DV + vrow) * D + cg * CPL;
+#pragma unroll
+    for (int e = 0; e < CPL; e += 4)
+      *(float4*)(p.S_out + so + e) = float4{x[e], x[e + 1], x[e + 2], x[e + 3]};
+  }
+}
+
+}  // namespace
+
+hipError_t launch_perm_fwd(const PermParams& p, hipStream_t s) {
+  const int nvb = p.DV / ROWS;   // DV is a multiple of 32
+  const int groups = (p.B * p.H + 7) / 8;
+  const dim3 grid(groups * 8 * nvb);
+  if (p.DK == 128) {
+    hipLaunchKernelGGL(perm_fwd_kernel<128>, grid, dim3(NT), 0, s, p);
+  } else if (p.DK == 64) {
+    hipLaunchKernelGGL(perm_fwd_kernel<64>, grid, dim3(NT), 0, s, p);
+  } else {
+    return hipErrorInvalidValue;
+  }
+  return hipGetLastError();
+}
+
+}  // namespace perm
+}  // namespace gdr

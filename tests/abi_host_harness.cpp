@@ -10,6 +10,8 @@
 #include "gdr_kernels.h"
 #include "gdr_raven.h"
 #include "raven_kernels.h"
+#include "gdr_perm.h"
+#include "perm_kernels.h"
 
 namespace gdr {
 static FwdParams g_fwd;
@@ -40,6 +42,15 @@ hipError_t launch_raven_fwd(const RavenParams& p, hipStream_t) {
   return hipSuccess;
 }
 }  // namespace raven
+namespace perm {
+static PermParams g_pm;
+static int g_npm = 0;
+hipError_t launch_perm_fwd(const PermParams& p, hipStream_t) {
+  g_pm = p;
+  ++g_npm;
+  return hipSuccess;
+}
+}  // namespace perm
 }  // namespace gdr
 
 static int g_fail = 0;
@@ -221,6 +232,25 @@ int main() {
     x = r; x.scale = 1.f / 0.f; CHECK(gdr_raven_fwd(&x, nullptr) == GDR_ERR_UNSUPPORTED);
     CHECK(gdr_raven_fwd(nullptr, nullptr) == GDR_ERR_NULL);
     CHECK(gdr::raven::g_nrv == 1);
+  }
+
+  // partial permutations: marshalled, and rejected before any launch
+  {
+    gdr_perm_args a;
+    std::memset(&a, 0, sizeof a);
+    a.B = 2; a.T = 50; a.H = 3; a.dk = 128; a.dv = 64;
+    a.q = fake(1); a.k = fake(2); a.v = fake(3); a.src = (const int16_t*)fake(4);
+    a.beta = (const float*)fake(5); a.w = (const float*)fake(6); a.o = fake(7);
+    a.S0 = (const float*)fake(8); a.S_out = (float*)fake(8);
+    CHECK(gdr_perm_fwd(&a, nullptr) == GDR_OK && gdr::perm::g_npm == 1);
+    const gdr::perm::PermParams& p = gdr::perm::g_pm;
+    CHECK(p.B == 2 && p.T == 50 && p.H == 3 && p.DK == 128 && p.DV == 64);
+    CHECK(p.src == a.src && p.beta == a.beta && p.w == a.w && p.o == a.o && p.S_out == a.S_out);
+    gdr_perm_args x = a; x.dv = 40; CHECK(gdr_perm_fwd(&x, nullptr) == GDR_ERR_UNSUPPORTED);
+    x = a; x.src = nullptr; CHECK(gdr_perm_fwd(&x, nullptr) == GDR_ERR_NULL);
+    x = a; x.S_out = (float*)((char*)fake(8) + 16); CHECK(gdr_perm_fwd(&x, nullptr) == GDR_ERR_ARG);
+    x = a; x.B = 0x7fffffff; x.T = 0x7fffffff; CHECK(gdr_perm_fwd(&x, nullptr) == GDR_ERR_SHAPE);
+    CHECK(gdr_perm_fwd(nullptr, nullptr) == GDR_ERR_NULL && gdr::perm::g_npm == 1);
   }
 
   for (int st = -1; st < 12; ++st) CHECK(gdr_status_str((gdr_status)st) != nullptr);

@@ -12,6 +12,7 @@ import recurrent_state_memory_amd as gdr
 ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
 HEADER = os.path.join(ROOT, "include", "gdr.h")
 RAVEN_HEADER = os.path.join(ROOT, "include", "gdr_raven.h")
+PERM_HEADER = os.path.join(ROOT, "include", "gdr_perm.h")
 
 FAKE = 0x10000          # aligned, never dereferenced: validation fails first
 MISALIGNED = 0x10004
@@ -33,7 +34,8 @@ def test_library_loads_and_exports_header_symbols():
     names = _declared()
     assert {"gdr_chunk_fwd", "gdr_chunk_fwd_gated", "gdr_chunk_bwd", "gdr_chunk_bwd_workspace",
             "gdr_step_decode", "gdr_chunk_fwd_workspace", "gdr_status_str",
-            "gdr_abi_version", "gdr_chunk_bwd_noalloc", "gdr_raven_fwd"} <= set(names)
+            "gdr_abi_version", "gdr_chunk_bwd_noalloc", "gdr_raven_fwd",
+            "gdr_perm_fwd"} <= set(names)
     for nm in names:
         assert hasattr(lib, nm), nm
     out = subprocess.run(["nm", "-D", "--defined-only", gdr.LIB_PATH], capture_output=True,
@@ -248,9 +250,9 @@ def test_struct_layout_matches_header(tmp_path):
     """Field offsets of the ctypes mirrors equal the C compiler's offsetof()."""
     fields = {"gdr_fwd_args": gdr.FwdArgs, "gdr_step_args": gdr.StepArgs,
               "gdr_gate_args": gdr.GateArgs, "gdr_bwd_args": gdr.BwdArgs,
-              "gdr_raven_args": gdr.RavenArgs}
+              "gdr_raven_args": gdr.RavenArgs, "gdr_perm_args": gdr.PermArgs}
     lines = ["#include <stdio.h>", "#include <stddef.h>", f'#include "{HEADER}"',
-             f'#include "{RAVEN_HEADER}"',
+             f'#include "{RAVEN_HEADER}"', f'#include "{PERM_HEADER}"',
              "int main(void) {"]
     for cname, cls in fields.items():
         lines.append(f'printf("{cname} size %zu\\n", sizeof({cname}));')
@@ -444,6 +446,7 @@ def test_host_half_under_sanitizers(tmp_path):
            os.path.join(ROOT, "tests", "abi_host_harness.cpp"),
            os.path.join(ROOT, "recurrent_state_memory_amd", "csrc", "gdr_api.cpp"),
            os.path.join(ROOT, "recurrent_state_memory_amd", "csrc", "raven_api.cpp"),
+           os.path.join(ROOT, "recurrent_state_memory_amd", "csrc", "perm_api.cpp"),
            "-o", str(exe)]
     r = subprocess.run(cmd, capture_output=True, text=True)
     if r.returncode != 0 and "sanitizer" in r.stderr.lower():
@@ -509,3 +512,53 @@ def test_raven_binding_checks():
         a[name] = val
         with pytest.raises(ValueError, match=name):
             gdr.gdr_raven_fwd(**a, topk=8)
+
+
+# ------------------------------------------------------------ partial permutations
+def _good_perm(**kw):
+    a = gdr.PermArgs()
+    a.B, a.T, a.H, a.dk, a.dv = 2, 70, 3, 128, 128
+    for f in ("q", "k", "v", "src", "beta", "w", "o"):
+        setattr(a, f, FAKE)
+    for f, val in kw.items():
+        setattr(a, f, val)
+    return a
+
+
+PERM_CASES = [
+    (dict(src=None), gdr.GDR_ERR_NULL),
+    (dict(beta=None), gdr.GDR_ERR_NULL),
+    (dict(o=None), gdr.GDR_ERR_NULL),
+    (dict(T=0), gdr.GDR_ERR_SHAPE),
+    (dict(dk=32), gdr.GDR_ERR_UNSUPPORTED),
+    (dict(dv=24), gdr.GDR_ERR_UNSUPPORTED),
+    (dict(dv=48), gdr.GDR_ERR_UNSUPPORTED),
+    (dict(dv=288), gdr.GDR_ERR_UNSUPPORTED),
+    (dict(src=MISALIGNED), gdr.GDR_ERR_ALIGN),
+    (dict(S0=FAKE, S_out=FAKE + 64), gdr.GDR_ERR_ARG),
+    (dict(B=1 << 20, T=1 << 12, H=1 << 8), gdr.GDR_ERR_SHAPE),
+]
+
+
+@pytest.mark.parametrize("kw,status", PERM_CASES)
+def test_perm_rejects_before_any_hip_call(kw, status):
+    assert gdr.call_perm_fwd(_good_perm(**kw)) == status
+
+
+def test_perm_binding_checks():
+    import torch
+    bf, f32 = torch.bfloat16, torch.float32
+    B, T, H, d = 2, 5, 3, 64
+    good = dict(q=torch.zeros(B, T, H, d, dtype=bf), k=torch.zeros(B, T, H, d, dtype=bf),
+                v=torch.zeros(B, T, H, d, dtype=bf), w=torch.zeros(B, T, H, dtype=f32),
+                src=torch.zeros(B, T, H, d, dtype=torch.int16), beta=torch.zeros(B, T, H, dtype=f32))
+    with pytest.raises(ValueError, match="GPU"):
+        gdr.gdr_perm_fwd(**good)
+    for name, val in (("src", torch.zeros(B, T, H, d, dtype=torch.int32)),
+                      ("src", torch.zeros(B, T, H, d - 1, dtype=torch.int16)),
+                      ("beta", torch.zeros(B, T, H, dtype=bf)), ("w", torch.zeros(B, T, 1)),
+                      ("S0", torch.zeros(B, H, d, d, dtype=bf))):
+        a = dict(good)
+        a[name] = val
+        with pytest.raises(ValueError, match=name):
+            gdr.gdr_perm_fwd(**a)
