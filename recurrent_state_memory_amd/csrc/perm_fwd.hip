@@ -16,7 +16,7 @@
 // LDS row buffer (a source outside [0, d_k) is mapped at staging to a column
 // that always holds 0, so the gather has no test), the two dot products through
 // DPP butterflies inside each group of 8 lanes.  Workgroups (one head, 32 value
-// rows) stage 16 tokens of k, q (as fp32), the source maps, v, beta and w in
+// rows) stage 16 tokens of k, q (bf16), the source maps, v, beta and w in
 // LDS, with the next chunk's loads in flight; the value blocks of one head
 // share an XCD, so keys, queries and maps come from its L2 after the first
 // reader.
@@ -37,8 +37,8 @@ constexpr int ROWS = 4 * RPW;
 
 template <int D>
 struct Sh {
-  float Kc[L * D];
-  float Qc[L * D];
+  bf Kc[L * D];
+  bf Qc[L * D];
   int16_t Sc[L * D];       // source channel, or D (the zero column) where there is none
   bf Vc[L * ROWS];
   float Bc[L];             // beta
@@ -141,12 +141,8 @@ __global__ __launch_bounds__(NT) void perm_fwd_kernel(PermParams p) {
   };
   auto fill_lds = [&]() {
     if (tid < NPIECE) {
-      float* kd = sh.Kc + pt * D + pch;
-      float* qd = sh.Qc + pt * D + pch;
-      *(float4*)kd = float4{bf_lo(rk.x), bf_hi(rk.x), bf_lo(rk.y), bf_hi(rk.y)};
-      *(float4*)(kd + 4) = float4{bf_lo(rk.z), bf_hi(rk.z), bf_lo(rk.w), bf_hi(rk.w)};
-      *(float4*)qd = float4{bf_lo(rq.x), bf_hi(rq.x), bf_lo(rq.y), bf_hi(rq.y)};
-      *(float4*)(qd + 4) = float4{bf_lo(rq.z), bf_hi(rq.z), bf_lo(rq.w), bf_hi(rq.w)};
+      *(uint4*)(sh.Kc + pt * D + pch) = rk;
+      *(uint4*)(sh.Qc + pt * D + pch) = rq;
       *(uint4*)(sh.Sc + pt * D + pch) =
           uint4{src_fix(rs.x, D), src_fix(rs.y, D), src_fix(rs.z, D), src_fix(rs.w, D)};
     }
@@ -167,24 +163,48 @@ __global__ __launch_bounds__(NT) void perm_fwd_kernel(PermParams p) {
 #pragma unroll 1
     for (int t = 0; t < tn; ++t) {
       const int base = t * D + cg * CPL;
-      // column selection through this row's LDS buffer (source D reads the zero)
-#pragma unroll
-      for (int e = 0; e < CPL; e += 4)
-        *(float4*)(rbuf + cg * CPL + e) = float4{x[e], x[e + 1], x[e + 2], x[e + 3]};
+      // column selection through this row's LDS buffer (source D reads the zero);
+      // a token whose map is the identity (the same for every row: a wave-wide
+      // vote) keeps the row in registers
       float xs[CPL], kf[CPL], qf[CPL];
+      uint32_t sw[CPL / 2];
 #pragma unroll
       for (int e = 0; e < CPL; e += 8) {
         const uint4 s4 = *(const uint4*)(sh.Sc + base + e);
-        const uint32_t sw[4] = {s4.x, s4.y, s4.z, s4.w};
+        sw[e / 2] = s4.x;
+        sw[e / 2 + 1] = s4.y;
+        sw[e / 2 + 2] = s4.z;
+        sw[e / 2 + 3] = s4.w;
+      }
+      bool ident = true;
 #pragma unroll
-        for (int u = 0; u < 8; ++u) xs[e + u] = rbuf[u & 1 ? sw[u >> 1] >> 16 : sw[u >> 1] & 0xffffu];
+      for (int u = 0; u < CPL / 2; ++u) {
+        const uint32_t want = (uint32_t)(cg * CPL + 2 * u) | ((uint32_t)(cg * CPL + 2 * u + 1) << 16);
+        ident = ident && sw[u] == want;
+      }
+      if (__all(ident)) {
+#pragma unroll
+        for (int e = 0; e < CPL; ++e) xs[e] = x[e];
+      } else {
+#pragma unroll
+        for (int e = 0; e < CPL; e += 4)
+          *(float4*)(rbuf + cg * CPL + e) = float4{x[e], x[e + 1], x[e + 2], x[e + 3]};
+#pragma unroll
+        for (int e = 0; e < CPL; ++e) xs[e] = rbuf[e & 1 ? sw[e >> 1] >> 16 : sw[e >> 1] & 0xffffu];
       }
 #pragma unroll
-      for (int e = 0; e < CPL; e += 4) {
-        const float4 k4 = *(const float4*)(sh.Kc + base + e);
-        const float4 q4 = *(const float4*)(sh.Qc + base + e);
-        kf[e] = k4.x; kf[e + 1] = k4.y; kf[e + 2] = k4.z; kf[e + 3] = k4.w;
-        qf[e] = q4.x; qf[e + 1] = q4.y; qf[e + 2] = q4.z; qf[e + 3] = q4.w;
+      for (int e = 0; e < CPL; e += 8) {
+        const uint4 k8 = *(const uint4*)(sh.Kc + base + e);
+        const uint4 q8 = *(const uint4*)(sh.Qc + base + e);
+        const uint32_t kw[4] = {k8.x, k8.y, k8.z, k8.w};
+        const uint32_t qw[4] = {q8.x, q8.y, q8.z, q8.w};
+#pragma unroll
+        for (int u = 0; u < 4; ++u) {
+          kf[e + 2 * u] = bf_lo(kw[u]);
+          kf[e + 2 * u + 1] = bf_hi(kw[u]);
+          qf[e + 2 * u] = bf_lo(qw[u]);
+          qf[e + 2 * u + 1] = bf_hi(qw[u]);
+        }
       }
       float a4[4] = {0.f, 0.f, 0.f, 0.f};
 #pragma unroll
