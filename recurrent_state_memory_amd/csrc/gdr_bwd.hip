@@ -266,7 +266,7 @@ __global__ __launch_bounds__(NT) void bwd_kernel(BwdParams p) {
           sm.Gam[r * PK + j] = gam;
           sm.Kp[r * PK + j] = gam * kk;
           sm.Qp[r * PK + j] = gam * qq;
-          sm.Kh[r * PK + j] = kk / gam;
+          sm.Kh[r * PK + j] = kk * __builtin_amdgcn_rcpf(gam);
         }
         sm.gl[j] = gam;
       }
@@ -285,7 +285,7 @@ __global__ __launch_bounds__(NT) void bwd_kernel(BwdParams p) {
           zi = ni;
           const float k0 = sm.Kp[r * PK + 2 * pr], k1 = sm.Kp[r * PK + 2 * pr + 1];
           const float q0 = sm.Qp[r * PK + 2 * pr], q1 = sm.Qp[r * PK + 2 * pr + 1];
-          const float iz = 1.f / (zr * zr + zi * zi);
+          const float iz = __builtin_amdgcn_rcpf(zr * zr + zi * zi);
           const float hr = zr * iz, hi = zi * iz;   // P^{-T} on a pair: z / |z|^2
           sm.Gam[r * PK + 2 * pr] = zr;
           sm.Gam[r * PK + 2 * pr + 1] = zi;
@@ -316,19 +316,60 @@ __global__ __launch_bounds__(NT) void bwd_kernel(BwdParams p) {
       }
     }
     lds_barrier();
-    // ------------------- T = (I + Diag(beta) N)^{-1}, and T Diag(beta) in DA
-    if (wv == 0 && l < L) {
-      float x[L];
+    // ------------------- T = (I + A)^{-1} with A = Diag(beta) N strictly lower, so
+    // A^32 = 0 and T = (I - A)(I + A^2)(I + A^4)(I + A^8)(I + A^16): four
+    // squarings and four products on the matrix cores, each wave one 16x16
+    // tile of each (DM, DDl and DR, written later in the block, hold the
+    // intermediate powers and partial products); then T Diag(beta) in DA
+    {
+      static_assert(Sm::PV == PL, "the scratch matrices share the L x L stride");
+      for (int e = tid; e < L * L; e += NT) {
+        const int r = e / L, c2 = e % L;
+        const float a = sm.beta[r] * sm.N[r * PL + c2];   // N is 0 on and above the diagonal
+        sm.DM[r * PL + c2] = a;
+        sm.T[r * PL + c2] = (r == c2 ? 1.f : 0.f) - a;
+      }
+      lds_barrier();
+      const int r0 = 16 * ti2, cc0 = 16 * tj2;
+      auto tile_load = [&](const float* m) {
+        f32x4 t;
 #pragma unroll
-      for (int i = 0; i < L; ++i) {
-        float acc = i == l ? 1.f : 0.f;
-        float dot = 0.f;
+        for (int j = 0; j < 4; ++j) t[j] = m[(r0 + 4 * g + j) * PL + cc0 + n];
+        return t;
+      };
+      auto tile_store = [&](float* m, const f32x4& t) {
 #pragma unroll
-        for (int s = 0; s < i; ++s) dot += sm.N[i * PL + s] * x[s];
-        acc -= sm.beta[i] * dot;
-        x[i] = acc;
-        sm.T[i * PL + l] = acc;
-        sm.DA[i * PL + l] = acc * sm.beta[l];
+        for (int j = 0; j < 4; ++j) m[(r0 + 4 * g + j) * PL + cc0 + n] = t[j];
+      };
+      float* Xc = sm.DM;
+      float* Xn = sm.DDl;
+      {
+        f32x4 x = {0.f, 0.f, 0.f, 0.f};
+        mm<PL, 1, PL, 1, L>(x, Xc, r0, Xc, cc0);   // A^2
+        tile_store(Xn, x);
+      }
+      lds_barrier();
+      { float* t_ = Xc; Xc = Xn; Xn = t_; }
+      float* Pc = sm.T;
+      float* Pn = sm.DR;
+#pragma unroll 1
+      for (int m = 0; m < 4; ++m) {
+        f32x4 pv = tile_load(Pc);
+        mm<PL, 1, PL, 1, L>(pv, Pc, r0, Xc, cc0);   // P (I + A^(2^(m+1)))
+        tile_store(Pn, pv);
+        if (m < 3) {
+          f32x4 x = {0.f, 0.f, 0.f, 0.f};
+          mm<PL, 1, PL, 1, L>(x, Xc, r0, Xc, cc0);   // the next power
+          tile_store(Xn, x);
+        }
+        lds_barrier();
+        { float* t_ = Pc; Pc = Pn; Pn = t_; }
+        { float* t_ = Xc; Xc = Xn; Xn = t_; }
+      }
+      // four swaps: the product is back in T
+      for (int e = tid; e < L * L; e += NT) {
+        const int r = e / L, c2 = e % L;
+        sm.DA[r * PL + c2] = sm.T[r * PL + c2] * sm.beta[c2];
       }
     }
     lds_barrier();
@@ -481,7 +522,7 @@ __global__ __launch_bounds__(NT) void bwd_kernel(BwdParams p) {
             if (r == nt - 1) dl += sm.dl_end[ch];
             if (r < nt) {
               Pq[o + ch] = gam * gq;
-              Pk[o + ch] = gam * gkp + gkh / gam;
+              Pk[o + ch] = gam * gkp + gkh * __builtin_amdgcn_rcpf(gam);
               Pl[o + ch] = dl;
             }
           } else {
@@ -498,7 +539,7 @@ __global__ __launch_bounds__(NT) void bwd_kernel(BwdParams p) {
             const float Qp0 = even ? qp : x_qp, Qp1 = even ? x_qp : qp;
             const float Kh0 = even ? kh : x_kh, Kh1 = even ? x_kh : kh;
             // dq = conj(z) dQp; dk = conj(z) dKp + conj(z) / |z|^2 dKh
-            const float iz = 1.f / (zr * zr + zi * zi);
+            const float iz = __builtin_amdgcn_rcpf(zr * zr + zi * zi);
             const float dq0 = zr * q0 + zi * q1, dq1 = zr * q1 - zi * q0;
             const float dk0 = zr * a0 + zi * a1 + iz * (zr * h0 + zi * h1);
             const float dk1 = zr * a1 - zi * a0 + iz * (zr * h1 - zi * h0);
