@@ -105,101 +105,125 @@ __device__ inline void put8(float* dst, uint4 u, bool ok) {
   }
 }
 
-// Raw inputs of block c into LDS; tokens at or past T read as zero (and as
-// the identity transition).
+// Raw inputs of one block, held in registers between their global loads and
+// their LDS stores, so that the loads of block c - 1 run under the products of
+// block c.
 template <int DK, int DECAY>
-__device__ inline void stage_block(Smem<DK>& sm, const BwdParams& p, int unit, size_t bh, int c,
-                                   int t0, int nt, int nc, int v0, int tid) {
-  constexpr int PK = Smem<DK>::PK, PV = Smem<DK>::PV;
+struct BlockRaw {
+  static constexpr int SP = TV * DK / 4 / NT;                      // state tile, 16-byte pieces
+  static constexpr int KP = L * DK / 8 / NT;                       // keys, queries
+  static constexpr int AP = DECAY == 0 ? L * DK / 4 / NT           // DIAG alpha
+                                       : (L * DK / 8 + NT - 1) / NT;   // ROT2 gamma, theta
+  float bt, wt;
+  uint4 uv, ug;
+  f32x4 s[SP];
+  uint4 kx[KP], qx[KP];
+  f32x4 ax[AP], tx[DECAY == 0 ? 1 : AP];
+};
+
+// Issues every global load of block c (16-byte pieces); rows at or past T
+// repeat the last token (masked when stored).
+template <int DK, int DECAY>
+__device__ inline void load_block(BlockRaw<DK, DECAY>& R, const BwdParams& p, int unit, size_t bh,
+                                  int c, int t0, int nt, int nc, int v0, int tid) {
+  using RW = BlockRaw<DK, DECAY>;
   const int H = p.H, DV = p.DV;
   if (tid < L) {
-    const bool ok = tid < nt;
     const size_t row = bh + (size_t)(t0 + min(tid, nt - 1)) * H;
-    const float bt = p.beta[row], wt = p.w[row];
-    sm.beta[tid] = ok ? bt : 0.f;
-    sm.w[tid] = ok ? wt : 0.f;
+    R.bt = p.beta[row];
+    R.wt = p.w[row];
   }
   // v and grad_o tiles: L rows x TV bf16 = 4 pieces of 8 per row
   static_assert(L * TV / 8 <= NT, "one piece of v and of grad_o per thread");
   if (tid < L * TV / 8) {
     const int r = tid / (TV / 8), i8 = tid % (TV / 8);
-    const bool ok = r < nt;
     const size_t src = (bh + (size_t)(t0 + min(r, nt - 1)) * H) * DV + v0 + 8 * i8;
-    const uint4 uv = *(const uint4*)((const __bf16*)p.v + src);
-    const uint4 ug = *(const uint4*)((const __bf16*)p.grad_o + src);
-    put8(sm.V + r * PV + 8 * i8, uv, ok);
-    put8(sm.DO + r * PV + 8 * i8, ug, ok);
+    R.uv = *(const uint4*)((const __bf16*)p.v + src);
+    R.ug = *(const uint4*)((const __bf16*)p.grad_o + src);
   }
-  // block-start state tile: TV rows x DK fp32
-  {
-    constexpr int PIECES = TV * DK / 4 / NT;
+  {   // block-start state tile: TV rows x DK fp32
     const float* ck = p.ckpt + ((size_t)unit * nc + c) * DV * DK;   // unit = b * H + h
-    f32x4 x[PIECES];
 #pragma unroll
-    for (int u = 0; u < PIECES; ++u) {
+    for (int u = 0; u < RW::SP; ++u) {
       const int e = tid + u * NT, i = e / (DK / 4), j4 = e % (DK / 4);
-      x[u] = *(const f32x4*)(ck + (size_t)(v0 + i) * DK + 4 * j4);
-    }
-#pragma unroll
-    for (int u = 0; u < PIECES; ++u) {
-      const int e = tid + u * NT, i = e / (DK / 4), j4 = e % (DK / 4);
-      *(f32x4*)(sm.S + i * PK + 4 * j4) = x[u];
+      R.s[u] = *(const f32x4*)(ck + (size_t)(v0 + i) * DK + 4 * j4);
     }
   }
-  // keys and queries: L rows x DK bf16
-  {
-    constexpr int PIECES = L * DK / 8 / NT;
-    uint4 kx[PIECES], qx[PIECES];
 #pragma unroll
-    for (int u = 0; u < PIECES; ++u) {
-      const int e = tid + u * NT, r = e / (DK / 8), j8 = e % (DK / 8);
-      const size_t src = (bh + (size_t)(t0 + min(r, nt - 1)) * H) * DK + 8 * j8;
-      kx[u] = *(const uint4*)((const __bf16*)p.k + src);
-      qx[u] = *(const uint4*)((const __bf16*)p.q + src);
-    }
-#pragma unroll
-    for (int u = 0; u < PIECES; ++u) {
-      const int e = tid + u * NT, r = e / (DK / 8), j8 = e % (DK / 8);
-      put8(sm.Kp + r * PK + 8 * j8, kx[u], r < nt);
-      put8(sm.Qp + r * PK + 8 * j8, qx[u], r < nt);
-    }
+  for (int u = 0; u < RW::KP; ++u) {   // keys and queries: L rows x DK bf16
+    const int e = tid + u * NT, r = e / (DK / 8), j8 = e % (DK / 8);
+    const size_t src = (bh + (size_t)(t0 + min(r, nt - 1)) * H) * DK + 8 * j8;
+    R.kx[u] = *(const uint4*)((const __bf16*)p.k + src);
+    R.qx[u] = *(const uint4*)((const __bf16*)p.q + src);
   }
-  // transitions: DIAG alpha [L x DK]; ROT2 gamma and theta [L x DK/2] each
-  if constexpr (DECAY == 0) {
-    constexpr int PIECES = L * DK / 4 / NT;
-    f32x4 ax[PIECES];
+  if constexpr (DECAY == 0) {   // alpha: L x DK
 #pragma unroll
-    for (int u = 0; u < PIECES; ++u) {
+    for (int u = 0; u < RW::AP; ++u) {
       const int e = tid + u * NT, r = e / (DK / 4), j4 = e % (DK / 4);
-      ax[u] = *(const f32x4*)(p.alpha + (bh + (size_t)(t0 + min(r, nt - 1)) * H) * DK + 4 * j4);
+      R.ax[u] = *(const f32x4*)(p.alpha + (bh + (size_t)(t0 + min(r, nt - 1)) * H) * DK + 4 * j4);
     }
+  } else {   // gamma and theta: L x DK/2 each
+    constexpr int HP = DK / 2;
 #pragma unroll
-    for (int u = 0; u < PIECES; ++u) {
+    for (int u = 0; u < RW::AP; ++u) {
+      const int e = min(tid + u * NT, L * HP / 4 - 1), r = e / (HP / 4), j4 = e % (HP / 4);
+      const size_t src = (bh + (size_t)(t0 + min(r, nt - 1)) * H) * HP + 4 * j4;
+      R.ax[u] = *(const f32x4*)(p.alpha + src);
+      R.tx[u] = *(const f32x4*)(p.theta + src);
+    }
+  }
+}
+
+// Stores block raw inputs into LDS: k into Kp, q into Qp, the transition into
+// Gam (DIAG alpha; ROT2 gamma at even, theta at odd positions); tokens at or
+// past T as zero (and as the identity transition).
+template <int DK, int DECAY>
+__device__ inline void store_block(Smem<DK>& sm, const BwdParams& p, const BlockRaw<DK, DECAY>& R,
+                                   int nt, int tid) {
+  using RW = BlockRaw<DK, DECAY>;
+  constexpr int PK = Smem<DK>::PK, PV = Smem<DK>::PV;
+  if (tid < L) {
+    const bool ok = tid < nt;
+    sm.beta[tid] = ok ? R.bt : 0.f;
+    sm.w[tid] = ok ? R.wt : 0.f;
+  }
+  if (tid < L * TV / 8) {
+    const int r = tid / (TV / 8), i8 = tid % (TV / 8);
+    const bool ok = r < nt;
+    put8(sm.V + r * PV + 8 * i8, R.uv, ok);
+    put8(sm.DO + r * PV + 8 * i8, R.ug, ok);
+  }
+#pragma unroll
+  for (int u = 0; u < RW::SP; ++u) {
+    const int e = tid + u * NT, i = e / (DK / 4), j4 = e % (DK / 4);
+    *(f32x4*)(sm.S + i * PK + 4 * j4) = R.s[u];
+  }
+#pragma unroll
+  for (int u = 0; u < RW::KP; ++u) {
+    const int e = tid + u * NT, r = e / (DK / 8), j8 = e % (DK / 8);
+    put8(sm.Kp + r * PK + 8 * j8, R.kx[u], r < nt);
+    put8(sm.Qp + r * PK + 8 * j8, R.qx[u], r < nt);
+  }
+  if constexpr (DECAY == 0) {
+#pragma unroll
+    for (int u = 0; u < RW::AP; ++u) {
       const int e = tid + u * NT, r = e / (DK / 4), j4 = e % (DK / 4);
       const bool ok = r < nt;
 #pragma unroll
-      for (int q4 = 0; q4 < 4; ++q4) sm.Gam[r * PK + 4 * j4 + q4] = ok ? ax[u][q4] : 1.f;
+      for (int q4 = 0; q4 < 4; ++q4) sm.Gam[r * PK + 4 * j4 + q4] = ok ? R.ax[u][q4] : 1.f;
     }
   } else {
-    constexpr int HP = DK / 2, PIECES = (L * HP / 4 + NT - 1) / NT;
-    f32x4 gx[PIECES], tx[PIECES];
+    constexpr int HP = DK / 2;
 #pragma unroll
-    for (int u = 0; u < PIECES; ++u) {
-      const int e = min(tid + u * NT, L * HP / 4 - 1), r = e / (HP / 4), j4 = e % (HP / 4);
-      const size_t src = (bh + (size_t)(t0 + min(r, nt - 1)) * H) * HP + 4 * j4;
-      gx[u] = *(const f32x4*)(p.alpha + src);
-      tx[u] = *(const f32x4*)(p.theta + src);
-    }
-#pragma unroll
-    for (int u = 0; u < PIECES; ++u) {
+    for (int u = 0; u < RW::AP; ++u) {
       const int e = tid + u * NT;
       if (e < L * HP / 4) {
         const int r = e / (HP / 4), j4 = e % (HP / 4);
         const bool ok = r < nt;
 #pragma unroll
         for (int q4 = 0; q4 < 4; ++q4) {
-          sm.Gam[r * PK + 2 * (4 * j4 + q4)] = ok ? gx[u][q4] : 1.f;
-          sm.Gam[r * PK + 2 * (4 * j4 + q4) + 1] = ok ? tx[u][q4] : 0.f;
+          sm.Gam[r * PK + 2 * (4 * j4 + q4)] = ok ? R.ax[u][q4] : 1.f;
+          sm.Gam[r * PK + 2 * (4 * j4 + q4) + 1] = ok ? R.tx[u][q4] : 0.f;
         }
       }
     }
@@ -246,14 +270,19 @@ __global__ __launch_bounds__(NT) void bwd_kernel(BwdParams p) {
         G[ti][c][j] = p.grad_S ? p.grad_S[((size_t)(b * H + h) * DV + row) * DK + col] : 0.f;
       }
 
+  BlockRaw<DK, DECAY> raw;
+  {
+    const int t0 = (nc - 1) * L;
+    load_block<DK, DECAY>(raw, p, unit, bh, nc - 1, t0, Tn - t0, nc, v0, tid);
+  }
   for (int c = nc - 1; c >= 0; --c) {
     const int t0 = c * L, nt = min(L, Tn - t0);
     // ---------------------------------------------------------------- loads
-    // Every global load of the block is issued before any is used (unrolled,
-    // 16-byte pieces), into LDS: k into Kp, q into Qp, the transition into
-    // Gam (DIAG alpha; ROT2 gamma at even, theta at odd positions).
-    stage_block<DK, DECAY>(sm, p, unit, bh, c, t0, nt, nc, v0, tid);
+    // this block's raw inputs (loaded during the previous block) into LDS,
+    // then the loads of the next block (c - 1, a full block) are issued
+    store_block<DK, DECAY>(sm, p, raw, nt, tid);
     lds_barrier();
+    if (c > 0) load_block<DK, DECAY>(raw, p, unit, bh, c - 1, t0 - L, L, nc, v0, tid);
     // cumulative transitions and the decayed key/query forms, in place
     if constexpr (DECAY == 0) {
       if (tid < DK) {
