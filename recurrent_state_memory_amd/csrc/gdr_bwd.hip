@@ -283,50 +283,90 @@ __global__ __launch_bounds__(NT) void bwd_kernel(BwdParams p) {
     store_block<DK, DECAY>(sm, p, raw, nt, tid);
     lds_barrier();
     if (c > 0) load_block<DK, DECAY>(raw, p, unit, bh, c - 1, t0 - L, L, nc, v0, tid);
-    // cumulative transitions and the decayed key/query forms, in place
-    if constexpr (DECAY == 0) {
-      if (tid < DK) {
-        const int j = tid;
-        float gam = 1.f;
-#pragma unroll 4
-        for (int r = 0; r < L; ++r) {
-          gam *= sm.Gam[r * PK + j];
-          const float kk = sm.Kp[r * PK + j], qq = sm.Qp[r * PK + j];
-          sm.Gam[r * PK + j] = gam;
-          sm.Kp[r * PK + j] = gam * kk;
-          sm.Qp[r * PK + j] = gam * qq;
-          sm.Kh[r * PK + j] = kk * __builtin_amdgcn_rcpf(gam);
+    // cumulative transitions and the decayed key/query forms, in place: every
+    // thread takes one token segment of one channel (ROT2: channel pair), and
+    // the products of the earlier segments come from a scan over the lanes
+    // that hold the same channel (shuffles inside the wave)
+    {
+      constexpr int NCH = DECAY == 0 ? DK : DK / 2;
+      constexpr int NSEG = NT / NCH, CW = 64 / NSEG, TPS = L / NSEG;
+      static_assert(NSEG >= 2 && CW * NSEG == 64 && TPS * NSEG == L, "prefix split");
+      const int seg = l / CW, j = wv * CW + l % CW, r0 = seg * TPS;
+      if constexpr (DECAY == 0) {
+        float a[TPS];
+        float inc = 1.f;
+#pragma unroll
+        for (int r = 0; r < TPS; ++r) {
+          a[r] = sm.Gam[(r0 + r) * PK + j];
+          inc *= a[r];
         }
-        sm.gl[j] = gam;
-      }
-    } else {
-      if (tid < DK / 2) {
-        const int pr = tid;
-        float zr = 1.f, zi = 0.f;
-#pragma unroll 4
-        for (int r = 0; r < L; ++r) {
-          const float gm = sm.Gam[r * PK + 2 * pr], th = sm.Gam[r * PK + 2 * pr + 1];
+#pragma unroll
+        for (int d = 1; d < NSEG; d *= 2) {
+          const float up = __shfl_up(inc, CW * d);
+          if (seg >= d) inc *= up;
+        }
+        const float ex = __shfl_up(inc, CW);
+        float gam = seg > 0 ? ex : 1.f;
+#pragma unroll
+        for (int r = 0; r < TPS; ++r) {
+          const int rr = r0 + r;
+          gam *= a[r];
+          const float kk = sm.Kp[rr * PK + j], qq = sm.Qp[rr * PK + j];
+          sm.Gam[rr * PK + j] = gam;
+          sm.Kp[rr * PK + j] = gam * kk;
+          sm.Qp[rr * PK + j] = gam * qq;
+          sm.Kh[rr * PK + j] = kk * __builtin_amdgcn_rcpf(gam);
+        }
+        if (seg == NSEG - 1) sm.gl[j] = gam;
+      } else {
+        const int pr = j;
+        float dr[TPS], di[TPS];
+        float ir = 1.f, ii = 0.f;
+#pragma unroll
+        for (int r = 0; r < TPS; ++r) {
+          const float gm = sm.Gam[(r0 + r) * PK + 2 * pr], th = sm.Gam[(r0 + r) * PK + 2 * pr + 1];
           float sn, cs;
           __sincosf(th, &sn, &cs);
-          const float dr = gm * cs, di = gm * sn;
-          const float nr = zr * dr - zi * di, ni = zr * di + zi * dr;
+          dr[r] = gm * cs;
+          di[r] = gm * sn;
+          const float nr = ir * dr[r] - ii * di[r], ni = ir * di[r] + ii * dr[r];
+          ir = nr;
+          ii = ni;
+        }
+#pragma unroll
+        for (int d = 1; d < NSEG; d *= 2) {
+          const float ur = __shfl_up(ir, CW * d), ui = __shfl_up(ii, CW * d);
+          if (seg >= d) {
+            const float nr = ir * ur - ii * ui, ni = ir * ui + ii * ur;
+            ir = nr;
+            ii = ni;
+          }
+        }
+        const float er = __shfl_up(ir, CW), ei = __shfl_up(ii, CW);
+        float zr = seg > 0 ? er : 1.f, zi = seg > 0 ? ei : 0.f;
+#pragma unroll
+        for (int r = 0; r < TPS; ++r) {
+          const int rr = r0 + r;
+          const float nr = zr * dr[r] - zi * di[r], ni = zr * di[r] + zi * dr[r];
           zr = nr;
           zi = ni;
-          const float k0 = sm.Kp[r * PK + 2 * pr], k1 = sm.Kp[r * PK + 2 * pr + 1];
-          const float q0 = sm.Qp[r * PK + 2 * pr], q1 = sm.Qp[r * PK + 2 * pr + 1];
+          const float k0 = sm.Kp[rr * PK + 2 * pr], k1 = sm.Kp[rr * PK + 2 * pr + 1];
+          const float q0 = sm.Qp[rr * PK + 2 * pr], q1 = sm.Qp[rr * PK + 2 * pr + 1];
           const float iz = __builtin_amdgcn_rcpf(zr * zr + zi * zi);
           const float hr = zr * iz, hi = zi * iz;   // P^{-T} on a pair: z / |z|^2
-          sm.Gam[r * PK + 2 * pr] = zr;
-          sm.Gam[r * PK + 2 * pr + 1] = zi;
-          sm.Kp[r * PK + 2 * pr] = zr * k0 - zi * k1;
-          sm.Kp[r * PK + 2 * pr + 1] = zr * k1 + zi * k0;
-          sm.Qp[r * PK + 2 * pr] = zr * q0 - zi * q1;
-          sm.Qp[r * PK + 2 * pr + 1] = zr * q1 + zi * q0;
-          sm.Kh[r * PK + 2 * pr] = hr * k0 - hi * k1;
-          sm.Kh[r * PK + 2 * pr + 1] = hr * k1 + hi * k0;
+          sm.Gam[rr * PK + 2 * pr] = zr;
+          sm.Gam[rr * PK + 2 * pr + 1] = zi;
+          sm.Kp[rr * PK + 2 * pr] = zr * k0 - zi * k1;
+          sm.Kp[rr * PK + 2 * pr + 1] = zr * k1 + zi * k0;
+          sm.Qp[rr * PK + 2 * pr] = zr * q0 - zi * q1;
+          sm.Qp[rr * PK + 2 * pr + 1] = zr * q1 + zi * q0;
+          sm.Kh[rr * PK + 2 * pr] = hr * k0 - hi * k1;
+          sm.Kh[rr * PK + 2 * pr + 1] = hr * k1 + hi * k0;
         }
-        sm.gl[2 * pr] = zr;
-        sm.gl[2 * pr + 1] = zi;
+        if (seg == NSEG - 1) {
+          sm.gl[2 * pr] = zr;
+          sm.gl[2 * pr + 1] = zi;
+        }
       }
     }
     lds_barrier();
