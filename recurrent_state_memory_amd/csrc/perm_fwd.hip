@@ -19,7 +19,11 @@
 // rows) stage 16 tokens of k, q (bf16), the source maps, v, beta and w in
 // LDS, with the next chunk's loads in flight; the value blocks of one head
 // share an XCD, so keys, queries and maps come from its L2 after the first
-// reader.
+// reader.  Staging also classifies every token's map (the same for all rows):
+// the identity and the two unit shifts of a bounded stack (push: channel j
+// takes j - 1 and channel 0 empties; pop: j takes j + 1 and the last empties)
+// then move the row in registers (one DPP move across the row's lanes), and
+// only other maps use the LDS selection.
 #include <hip/hip_runtime.h>
 #include <stdint.h>
 
@@ -35,6 +39,8 @@ constexpr int NT = 256;    // 4 waves x 8 rows = 32 value rows per workgroup
 constexpr int RPW = 8;     // rows per wave (8 lanes per row)
 constexpr int ROWS = 4 * RPW;
 
+constexpr int kGeneral = 0, kIdentity = 1, kDown = 2, kUp = 3;
+
 template <int D>
 struct Sh {
   bf Kc[L * D];
@@ -43,6 +49,7 @@ struct Sh {
   bf Vc[L * ROWS];
   float Bc[L];             // beta
   float Wc[L];             // w
+  int Kind[L];             // the token's map: kGeneral, kIdentity, kDown or kUp
   float Rb[4][RPW][D + 4]; // per wave, per row: the row for the column selection; [D] = 0
   bf Oc[L * ROWS];
 };
@@ -70,6 +77,23 @@ __device__ inline uint32_t src_fix(uint32_t pair, int d) {   // two int16 source
   const uint32_t ua = (a >= 0 && a < d) ? (uint32_t)a : (uint32_t)d;
   const uint32_t ub = (b >= 0 && b < d) ? (uint32_t)b : (uint32_t)d;
   return ua | (ub << 16);
+}
+
+// Which of the three structured maps 8 consecutive fixed sources (channels
+// j0 .. j0 + 7; D stands for "none") agree with: bit 0 identity, bit 1 down
+// (j <- j - 1), bit 2 up (j <- j + 1).
+template <int D>
+__device__ inline unsigned classify8(const uint32_t (&fx)[4], int j0) {
+  bool id = true, dn = true, up = true;
+#pragma unroll
+  for (int i = 0; i < 8; ++i) {
+    const int j = j0 + i;
+    const int sv = (int)((fx[i >> 1] >> (16 * (i & 1))) & 0xffffu);
+    id = id && sv == j;
+    dn = dn && sv == (j >= 1 ? j - 1 : D);
+    up = up && sv == (j + 1 < D ? j + 1 : D);
+  }
+  return (id ? 1u : 0u) | (dn ? 2u : 0u) | (up ? 4u : 0u);
 }
 
 template <int D>
@@ -140,11 +164,24 @@ __global__ __launch_bounds__(NT) void perm_fwd_kernel(PermParams p) {
     }
   };
   auto fill_lds = [&]() {
+    const uint32_t fx[4] = {src_fix(rs.x, D), src_fix(rs.y, D), src_fix(rs.z, D), src_fix(rs.w, D)};
+    const unsigned cls = tid < NPIECE ? classify8<D>(fx, pch) : 0u;
     if (tid < NPIECE) {
       *(uint4*)(sh.Kc + pt * D + pch) = rk;
       *(uint4*)(sh.Qc + pt * D + pch) = rq;
-      *(uint4*)(sh.Sc + pt * D + pch) =
-          uint4{src_fix(rs.x, D), src_fix(rs.y, D), src_fix(rs.z, D), src_fix(rs.w, D)};
+      *(uint4*)(sh.Sc + pt * D + pch) = uint4{fx[0], fx[1], fx[2], fx[3]};
+    }
+    {   // a token's PPT pieces sit in PPT consecutive lanes of one wave
+      static_assert(64 % PPT == 0 && NPIECE % 64 == 0, "pieces of a token in one wave");
+      const unsigned long long bi = __ballot((cls & 1u) != 0u), bd = __ballot((cls & 2u) != 0u),
+                               bu = __ballot((cls & 4u) != 0u);
+      const int sh0 = l & ~(PPT - 1);
+      const unsigned long long all = (PPT == 64 ? ~0ull : ((1ull << PPT) - 1ull)) << sh0;
+      if (tid < NPIECE && (l & (PPT - 1)) == 0) {
+        sh.Kind[pt] = (bi & all) == all ? kIdentity
+                    : (bd & all) == all ? kDown
+                    : (bu & all) == all ? kUp : kGeneral;
+      }
     }
     if (tid < 4 * L) *(uint4*)(sh.Vc + (tid >> 2) * ROWS + 8 * (tid & 3)) = rv;
     if (tid < L) sh.Bc[tid] = rb;
@@ -163,29 +200,35 @@ __global__ __launch_bounds__(NT) void perm_fwd_kernel(PermParams p) {
 #pragma unroll 1
     for (int t = 0; t < tn; ++t) {
       const int base = t * D + cg * CPL;
-      // column selection through this row's LDS buffer (source D reads the zero);
-      // a token whose map is the identity (the same for every row: a wave-wide
-      // vote) keeps the row in registers
+      // column selection: the structured maps in registers (a lane's first or
+      // last channel comes from the neighbouring lane of the same row, or is
+      // the emptied channel), any other map through this row's LDS buffer
+      // (source D reads the zero)
       float xs[CPL], kf[CPL], qf[CPL];
-      uint32_t sw[CPL / 2];
-#pragma unroll
-      for (int e = 0; e < CPL; e += 8) {
-        const uint4 s4 = *(const uint4*)(sh.Sc + base + e);
-        sw[e / 2] = s4.x;
-        sw[e / 2 + 1] = s4.y;
-        sw[e / 2 + 2] = s4.z;
-        sw[e / 2 + 3] = s4.w;
-      }
-      bool ident = true;
-#pragma unroll
-      for (int u = 0; u < CPL / 2; ++u) {
-        const uint32_t want = (uint32_t)(cg * CPL + 2 * u) | ((uint32_t)(cg * CPL + 2 * u + 1) << 16);
-        ident = ident && sw[u] == want;
-      }
-      if (__all(ident)) {
+      const int kind = __builtin_amdgcn_readfirstlane(sh.Kind[t]);
+      if (kind == kIdentity) {
 #pragma unroll
         for (int e = 0; e < CPL; ++e) xs[e] = x[e];
+      } else if (kind == kDown) {
+        const float in = __int_as_float(__builtin_amdgcn_mov_dpp(__float_as_int(x[CPL - 1]), 0x111, 0xf, 0xf, false));
+        xs[0] = cg == 0 ? 0.f : in;   // row_shr:1 -- lane l - 1 holds channels just below
+#pragma unroll
+        for (int e = 1; e < CPL; ++e) xs[e] = x[e - 1];
+      } else if (kind == kUp) {
+        const float in = __int_as_float(__builtin_amdgcn_mov_dpp(__float_as_int(x[0]), 0x101, 0xf, 0xf, false));
+        xs[CPL - 1] = cg == 7 ? 0.f : in;   // row_shl:1 -- lane l + 1 holds channels just above
+#pragma unroll
+        for (int e = 0; e < CPL - 1; ++e) xs[e] = x[e + 1];
       } else {
+        uint32_t sw[CPL / 2];
+#pragma unroll
+        for (int e = 0; e < CPL; e += 8) {
+          const uint4 s4 = *(const uint4*)(sh.Sc + base + e);
+          sw[e / 2] = s4.x;
+          sw[e / 2 + 1] = s4.y;
+          sw[e / 2 + 2] = s4.z;
+          sw[e / 2 + 3] = s4.w;
+        }
 #pragma unroll
         for (int e = 0; e < CPL; e += 4)
           *(float4*)(rbuf + cg * CPL + e) = float4{x[e], x[e + 1], x[e + 2], x[e + 3]};

@@ -7,7 +7,8 @@ the state <= 1e-4 (max |x - ref| / max |ref| per tensor).
 
 Cases: random stack moves with ragged lengths, both key widths, value widths
 32 .. 256, a start state and in place; random partial permutations and maps
-with repeated or out-of-range sources; the stack construction read back exactly
+with repeated or out-of-range sources; maps one channel away from the identity
+or a stack shift; the stack construction read back exactly
 (push = shift down then write channel 0, pop = shift up, top = channel 0); the
 workload's 128 heads on a prefix and at full size on sampled heads; a bitwise
 rerun.
@@ -85,6 +86,34 @@ def test_perm_general_maps():
     S0 = random_state(B, H, dk, dk, 9)
     check(run(x, S0, src=src), perm.forward(x.q, x.k, x.v, x.w, src, x.beta, S0),
           "perm general maps")
+
+
+@pytest.mark.parametrize("dk", [64, 128])
+def test_perm_near_structured_maps(dk):
+    """Maps one channel away from the identity, push or pop (which take the
+    register path when exact) must take the general path; an out-of-range
+    source where a shift empties a channel is still that shift."""
+    x = generate_perm(_wl(dk, T=96, seed=560 + dk))
+    rng = np.random.default_rng(561 + dk)
+    B, T, H, _ = x.src.shape
+    j = np.arange(dk)
+    push, pop = np.where(j >= 1, j - 1, -1), np.where(j + 1 < dk, j + 1, -1)
+    src = np.empty_like(x.src)
+    for b in range(B):
+        for t in range(T):
+            for h in range(H):
+                kind = rng.integers(0, 7)
+                m = [j, push, pop][kind % 3].copy()
+                if kind in (3, 4, 5):            # one channel altered
+                    c = rng.integers(0, dk)
+                    m[c] = (m[c] + rng.integers(1, dk)) % dk if rng.uniform() < 0.7 else -1
+                elif kind == 6:                   # push / pop with another "none" value
+                    m = (push if rng.uniform() < 0.5 else pop).copy()
+                    m[m < 0] = rng.choice([-7, dk, 300])
+                src[b, t, h] = m.astype(np.int16)
+    S0 = random_state(B, H, dk, dk, 11)
+    check(run(x, S0, src=src), perm.forward(x.q, x.k, x.v, x.w, src, x.beta, S0),
+          f"perm near-structured maps d{dk}")
 
 
 def test_perm_bounded_stack_exact():
