@@ -188,10 +188,11 @@ gdr_status gdr_chunk_fwd_gated(const gdr_fwd_args *a, const gdr_gate_args *g, vo
  * products, so the gradients carry the forward's rounding.
  *
  * Supported: BF16 q, k, v and grad_o; dk == dv in {64, 128}; T * H * dk <
- * 2^29; otherwise GDR_ERR_UNSUPPORTED.  Range: every 32-token block must keep
- * each key channel's (or pair's) decay product >= e^-40 (the forward has a
- * token path for such blocks, the backward does not); a head with a block
- * outside that range gets non-finite gradients.
+ * 2^29; otherwise GDR_ERR_UNSUPPORTED.  Range: every decay in [0, 1] is
+ * supported.  A head with a 32-token block whose decay product in some key
+ * channel (or pair) falls below e^-40 is redone token by token in fp32 with no
+ * division (exact for decays of 0), at a few times the cost of that head's
+ * block form.
  *
  * Layouts (fp32 gradients, same shapes as the inputs):
  *   grad_q, grad_k [B,T,H,dk]; grad_v [B,T,H,dv]; grad_alpha as alpha

@@ -157,10 +157,10 @@ gdr_status check_gated(const gdr_fwd_args* a, const gdr_gate_args* g) {
   return GDR_OK;
 }
 // Backward: the workspace holds the block-start states of the forward
-// recompute, its output o (not returned) and the per-value-tile partial sums,
-// each region 256-byte aligned.
+// recompute, its output o (not returned), the per-value-tile partial sums and
+// one range flag per (b, h, value tile), each region 256-byte aligned.
 struct BwdLayout {
-  size_t ckpt, o, part, total;
+  size_t ckpt, o, part, flag, total;
 };
 
 size_t round256(size_t x) { return (x + 255) & ~(size_t)255; }
@@ -172,7 +172,8 @@ BwdLayout bwd_layout(const gdr_bwd_args* a) {
   w.ckpt = 0;
   w.o = round256((size_t)a->B * a->H * nc * a->dv * a->dk * sizeof(float));
   w.part = w.o + round256(bth * a->dv * 2);
-  w.total = w.part + round256(gdr::bwd_part_floats(a->B, a->T, a->H, a->dk, a->dv) * sizeof(float));
+  w.flag = w.part + round256(gdr::bwd_part_floats(a->B, a->T, a->H, a->dk, a->dv) * sizeof(float));
+  w.total = w.flag + round256((size_t)a->B * a->H * (a->dv / gdr::kBwdTile) * sizeof(int));
   return w;
 }
 
@@ -303,6 +304,7 @@ gdr_status chunk_bwd_on(const gdr_bwd_args* a, void* workspace, size_t workspace
   p.grad_S0 = a->grad_S0;
   p.ckpt = (const float*)(ws + lay.ckpt);
   p.part = (float*)(ws + lay.part);
+  p.flag = (int*)(ws + lay.flag);
   e = gdr::launch_bwd(p, stream);
   return e == hipSuccess ? GDR_OK : GDR_ERR_HIP;
 }

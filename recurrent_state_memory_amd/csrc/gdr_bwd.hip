@@ -27,13 +27,16 @@
 // recompute (checkpoints).
 //
 // Range: like the forward's split form, the block form divides by the running
-// decay, so every block must keep each channel's product P_L >= e^-40; a block
-// that does not gives non-finite gradients for its head (the forward's token
-// path has no counterpart here).
+// decay, so it is exact only while each channel's product over a block stays
+// at or above e^-40.  bwd_kernel flags every (b, h, value tile) with a block
+// outside that range (strong forgetting: decays near or at zero), and
+// bwd_token_kernel then redoes the flagged ones token by token in fp32 with no
+// division, overwriting every output the block form wrote for them.
 #include <hip/hip_runtime.h>
 
 #include "gdr_kernels.h"
 #include "gdr_mfma.h"
+#include "gdr_token.h"
 
 namespace gdr {
 namespace bwd {
@@ -270,6 +273,7 @@ __global__ __launch_bounds__(NT) void bwd_kernel(BwdParams p) {
         G[ti][c][j] = p.grad_S ? p.grad_S[((size_t)(b * H + h) * DV + row) * DK + col] : 0.f;
       }
 
+  bool bad = false;   // some block's decay product left the block form's range
   BlockRaw<DK, DECAY> raw;
   {
     const int t0 = (nc - 1) * L;
@@ -317,7 +321,10 @@ __global__ __launch_bounds__(NT) void bwd_kernel(BwdParams p) {
           sm.Qp[rr * PK + j] = gam * qq;
           sm.Kh[rr * PK + j] = kk * __builtin_amdgcn_rcpf(gam);
         }
-        if (seg == NSEG - 1) sm.gl[j] = gam;
+        if (seg == NSEG - 1) {
+          sm.gl[j] = gam;
+          bad |= !(gam >= kMinChunkDecay);   // also true for NaN
+        }
       } else {
         const int pr = j;
         float dr[TPS], di[TPS];
@@ -366,6 +373,7 @@ __global__ __launch_bounds__(NT) void bwd_kernel(BwdParams p) {
         if (seg == NSEG - 1) {
           sm.gl[2 * pr] = zr;
           sm.gl[2 * pr + 1] = zi;
+          bad |= !(zr * zr + zi * zi >= kMinChunkDecay * kMinChunkDecay);
         }
       }
     }
@@ -654,6 +662,334 @@ __global__ __launch_bounds__(NT) void bwd_kernel(BwdParams p) {
           p.grad_S0[((size_t)(b * H + h) * DV + row) * DK + col] = G[ti][cc][j];
         }
   }
+  // one flag per workgroup, written whether set or not (no clearing needed)
+  __shared__ int bad_w[4];
+  const bool wbad = __ballot(bad) != 0ull;
+  if (l == 0) bad_w[wv] = wbad ? 1 : 0;
+  lds_barrier();
+  if (tid == 0) p.flag[blockIdx.x] = bad_w[0] | bad_w[1] | bad_w[2] | bad_w[3];
+}
+
+// ------------------------------------------------------------------------------
+// Token path of the backward for a flagged (b, h, value tile): the reverse mode
+// of the token recurrence itself,
+//     X = S_{t-1} D_t,  e = w_t v_t - X k_t,  S_t = X + beta_t e k_t^T,  o_t = S_t q_t,
+// per value row (rows are independent under key-axis transitions):
+//     g += dO_t q_t;            dq_t += dO_t S_t
+//     gk = g . k_t;             dbeta_t += e gk;  dw_t += beta v gk;  dv_t = w beta gk
+//     dX = g - beta gk k_t;     dk_t += beta e g - beta gk X
+//     g = dX D_t^T;             d(decay)_t from dX and S_{t-1}
+// with the sums over rows.  S_{t-1} comes from recomputing each block forward
+// from its checkpoint: once over the block keeping the state at every eighth
+// token in LDS, then per group of 8 tokens (last group first) again from that
+// state, keeping the group's 8 states in registers.  fp32 throughout and no
+// division, so decays of 0 are exact.
+//
+// Layout: a wave holds 8 rows (lanes 8c + r: row r, channels c*DK/8 ..), so a
+// row's dot products reduce over lanes 8, 16 and 32 apart and the sums over
+// rows over 8 neighbouring lanes (DPP).  The decay's partial sums go out per
+// token as dL/d(alpha) (DIAG) or dL/d(gamma), dL/d(theta) (ROT2) -- already the
+// transition's own gradients, which bwd_reduce_kernel adds up without its
+// prefix sum for flagged heads.
+
+template <int DK>
+struct TokSmem {
+  static constexpr int NG = L / 8;   // groups of 8 tokens
+  __bf16 K[L * DK], Q[L * DK];
+  float Z[L * DK];            // DIAG alpha; ROT2 (gamma cos theta, gamma sin theta) per pair
+  float V[L * TV], DO[L * TV];
+  float beta[L], w[L];
+  float sub[NG][TV * DK];     // the state before tokens 0, 8, 16, 24 of the block
+  float red[8][4][3 * DK];    // per token of a group, per wave: dq, dk, d(decay) row sums
+  float redb[8][4][2];        // dbeta, dw row sums
+};
+
+// sum over the 8 neighbouring lanes 8c .. 8c + 7; every lane gets it
+__device__ inline float sum8_rows(float x) {
+  x += __int_as_float(__builtin_amdgcn_mov_dpp(__float_as_int(x), 0xb1, 0xf, 0xf, false));    // lane ^ 1
+  x += __int_as_float(__builtin_amdgcn_mov_dpp(__float_as_int(x), 0x4e, 0xf, 0xf, false));    // lane ^ 2
+  x += __int_as_float(__builtin_amdgcn_mov_dpp(__float_as_int(x), 0x141, 0xf, 0xf, false));   // 7 - lane in 8
+  return x;
+}
+// sum over the lanes r, r + 8, ..., r + 56 (one row's channel slices)
+__device__ inline float sum_row_slices(float x) {
+  x += __shfl_xor(x, 8);
+  x += __shfl_xor(x, 16);
+  x += __shfl_xor(x, 32);
+  return x;
+}
+
+template <int DK, int DECAY>
+__global__ __launch_bounds__(NT) void bwd_token_kernel(BwdParams p) {
+  if (p.flag[blockIdx.x] == 0) return;   // uniform over the workgroup
+  using Sm = TokSmem<DK>;
+  constexpr int CPL = DK / 8;            // channels per lane
+  __shared__ __attribute__((aligned(16))) Sm sm;
+  const int tid = threadIdx.x, l = tid & 63, wv = tid >> 6;
+  const int r = l & 7, cs = l >> 3, row = 8 * wv + r, ch0 = cs * CPL;
+  const int H = p.H, Tn = p.T, DV = p.DV;
+  const int vt = blockIdx.x % p.n_vt, unit = blockIdx.x / p.n_vt;
+  const int b = unit / H, h = unit % H;
+  const int v0 = vt * TV;
+  const int nc = (Tn + L - 1) / L;
+  const size_t bh = (size_t)b * Tn * H + h;
+  const size_t BTH = (size_t)p.B * Tn * H;
+  const __bf16* q = (const __bf16*)p.q;
+  const __bf16* k = (const __bf16*)p.k;
+  const __bf16* v = (const __bf16*)p.v;
+  const __bf16* dO = (const __bf16*)p.grad_o;
+  float* Pq = p.part;
+  float* Pk = Pq + (size_t)p.n_vt * BTH * DK;
+  float* Pl = Pk + (size_t)p.n_vt * BTH * DK;
+  float* Pb = Pl + (size_t)p.n_vt * BTH * DK;
+  float* Pw = Pb + (size_t)p.n_vt * BTH;
+  const size_t srow = ((size_t)(b * H + h) * DV + v0 + row) * DK + ch0;   // this lane's state slice
+
+  float gr[CPL];   // dL/dS of this lane's row slice after the token being undone
+#pragma unroll
+  for (int e = 0; e < CPL; ++e) gr[e] = p.grad_S ? p.grad_S[srow + e] : 0.f;
+
+  // this lane's slice of X = S D_t
+  auto transition = [&](const float (&s)[CPL], float (&x)[CPL], int t) {
+    const float* z = sm.Z + t * DK + ch0;
+#pragma unroll
+    for (int e = 0; e < CPL; e += 2) {
+      if constexpr (DECAY == 0) {
+        x[e] = s[e] * z[e];
+        x[e + 1] = s[e + 1] * z[e + 1];
+      } else {   // S times the block gamma [[c, -s], [s, c]]: zr = gamma c, zi = gamma s
+        x[e] = z[e] * s[e] + z[e + 1] * s[e + 1];
+        x[e + 1] = -z[e + 1] * s[e] + z[e] * s[e + 1];
+      }
+    }
+  };
+  auto keys = [&](float (&kk)[CPL], const __bf16* src) {   // CPL bf16 as 16-byte pieces
+#pragma unroll
+    for (int e8 = 0; e8 < CPL; e8 += 8) {
+      const uint4 u4 = *(const uint4*)(src + e8);
+      const uint32_t wds[4] = {u4.x, u4.y, u4.z, u4.w};
+#pragma unroll
+      for (int j = 0; j < 4; ++j) {
+        kk[e8 + 2 * j] = __uint_as_float(wds[j] << 16);
+        kk[e8 + 2 * j + 1] = __uint_as_float(wds[j] & 0xffff0000u);
+      }
+    }
+  };
+  // one token forward: s <- S_t from s = S_{t-1}
+  auto fwd_token = [&](float (&s)[CPL], int t) {
+    float x[CPL], kk[CPL];
+    transition(s, x, t);
+    keys(kk, sm.K + t * DK + ch0);
+    float y = 0.f;
+#pragma unroll
+    for (int e = 0; e < CPL; ++e) y += x[e] * kk[e];
+    y = sum_row_slices(y);
+    const float cf = sm.beta[t] * (sm.w[t] * sm.V[t * TV + row] - y);
+#pragma unroll
+    for (int e = 0; e < CPL; ++e) s[e] = x[e] + cf * kk[e];
+  };
+
+  for (int c = nc - 1; c >= 0; --c) {
+    const int t0 = c * L, nt = min(L, Tn - t0);
+    // ------------------------------------------------ stage the block's inputs
+    for (int e = tid; e < L * DK / 8; e += NT) {
+      const int tt = e / (DK / 8), j8 = e % (DK / 8);
+      uint4 kk = {0u, 0u, 0u, 0u}, qq = kk;
+      if (tt < nt) {
+        const size_t src = (bh + (size_t)(t0 + tt) * H) * DK + 8 * j8;
+        kk = *(const uint4*)(k + src);
+        qq = *(const uint4*)(q + src);
+      }
+      *(uint4*)(sm.K + tt * DK + 8 * j8) = kk;
+      *(uint4*)(sm.Q + tt * DK + 8 * j8) = qq;
+    }
+    if constexpr (DECAY == 0) {
+      for (int e = tid; e < L * DK / 4; e += NT) {
+        const int tt = e / (DK / 4), j4 = e % (DK / 4);
+        f32x4 a = {1.f, 1.f, 1.f, 1.f};
+        if (tt < nt) a = *(const f32x4*)(p.alpha + (bh + (size_t)(t0 + tt) * H) * DK + 4 * j4);
+        *(f32x4*)(sm.Z + tt * DK + 4 * j4) = a;
+      }
+    } else {
+      for (int e = tid; e < L * DK / 2; e += NT) {
+        const int tt = e / (DK / 2), pr = e % (DK / 2);
+        float zr = 1.f, zi = 0.f;
+        if (tt < nt) {
+          const size_t src = (bh + (size_t)(t0 + tt) * H) * (DK / 2) + pr;
+          float sn, cn;
+          __sincosf(p.theta[src], &sn, &cn);
+          const float gm = p.alpha[src];
+          zr = gm * cn;
+          zi = gm * sn;
+        }
+        sm.Z[tt * DK + 2 * pr] = zr;
+        sm.Z[tt * DK + 2 * pr + 1] = zi;
+      }
+    }
+    for (int e = tid; e < L * TV; e += NT) {
+      const int tt = e / TV, i = e % TV;
+      float vv = 0.f, gg = 0.f;
+      if (tt < nt) {
+        const size_t src = (bh + (size_t)(t0 + tt) * H) * DV + v0 + i;
+        vv = (float)v[src];
+        gg = (float)dO[src];
+      }
+      sm.V[e] = vv;
+      sm.DO[e] = gg;
+    }
+    if (tid < L) {
+      const bool ok = tid < nt;
+      const size_t src = bh + (size_t)(t0 + tid) * H;
+      sm.beta[tid] = ok ? p.beta[src] : 0.f;
+      sm.w[tid] = ok ? p.w[src] : 0.f;
+    }
+    lds_barrier();
+    // ------------- forward over the block, keeping the state before every 8th token
+    {
+      float s[CPL];
+      const float* ck = p.ckpt + ((size_t)unit * nc + c) * DV * DK + (size_t)(v0 + row) * DK + ch0;
+#pragma unroll
+      for (int e = 0; e < CPL; e += 4) *(f32x4*)(s + e) = *(const f32x4*)(ck + e);
+      for (int t = 0; t < nt; ++t) {
+        if ((t & 7) == 0) {
+#pragma unroll
+          for (int e = 0; e < CPL; e += 4)
+            *(f32x4*)(sm.sub[t >> 3] + row * DK + ch0 + e) = *(const f32x4*)(s + e);
+        }
+        fwd_token(s, t);
+      }
+    }
+    // ------------------------------------ groups of 8 tokens, last group first
+    for (int grp = (nt - 1) >> 3; grp >= 0; --grp) {
+      float st[8][CPL];   // the state before each token of the group
+      {
+        float s[CPL];
+#pragma unroll
+        for (int e = 0; e < CPL; e += 4) *(f32x4*)(s + e) = *(const f32x4*)(sm.sub[grp] + row * DK + ch0 + e);
+#pragma unroll
+        for (int u = 0; u < 8; ++u) {
+#pragma unroll
+          for (int e = 0; e < CPL; ++e) st[u][e] = s[e];
+          if (u < 7 && 8 * grp + u < nt) fwd_token(s, 8 * grp + u);
+        }
+      }
+#pragma unroll
+      for (int u = 7; u >= 0; --u) {
+        const int t = 8 * grp + u;
+        if (t < nt) {
+          float x[CPL], kk[CPL], qq[CPL];
+          transition(st[u], x, t);
+          keys(kk, sm.K + t * DK + ch0);
+          keys(qq, sm.Q + t * DK + ch0);
+          float y = 0.f;
+#pragma unroll
+          for (int e = 0; e < CPL; ++e) y += x[e] * kk[e];
+          y = sum_row_slices(y);
+          const float bt = sm.beta[t], wt = sm.w[t], vr = sm.V[t * TV + row];
+          const float ev = wt * vr - y;
+          const float dor = sm.DO[t * TV + row];
+          float dq[CPL], dk[CPL], dz[CPL];
+          float gk = 0.f;
+#pragma unroll
+          for (int e = 0; e < CPL; ++e) {
+            dq[e] = dor * (x[e] + bt * ev * kk[e]);   // dO_t S_t
+            gr[e] += dor * qq[e];
+            gk += gr[e] * kk[e];
+          }
+          gk = sum_row_slices(gk);
+          const float bg = bt * gk;
+#pragma unroll
+          for (int e = 0; e < CPL; ++e) {
+            const float dx = gr[e] - bg * kk[e];
+            dk[e] = bt * ev * gr[e] - bg * x[e];
+            gr[e] = dx;   // dX for now
+          }
+          // through the transition: g = dX D^T, and the decay's gradient
+          const float* z = sm.Z + t * DK + ch0;
+#pragma unroll
+          for (int e = 0; e < CPL; e += 2) {
+            const float d0 = gr[e], d1 = gr[e + 1];
+            const float s0 = st[u][e], s1 = st[u][e + 1];
+            if constexpr (DECAY == 0) {
+              gr[e] = d0 * z[e];
+              gr[e + 1] = d1 * z[e + 1];
+              dz[e] = d0 * s0;
+              dz[e + 1] = d1 * s1;
+            } else {
+              const float zr = z[e], zi = z[e + 1];
+              gr[e] = zr * d0 - zi * d1;
+              gr[e + 1] = zi * d0 + zr * d1;
+              dz[e] = d0 * s0 + d1 * s1;       // d/d(gamma c)
+              dz[e + 1] = d0 * s1 - d1 * s0;   // d/d(gamma s)
+            }
+          }
+          // sums over the wave's 8 rows; lanes of row 0 keep them
+#pragma unroll
+          for (int e = 0; e < CPL; ++e) {
+            dq[e] = sum8_rows(dq[e]);
+            dk[e] = sum8_rows(dk[e]);
+            dz[e] = sum8_rows(dz[e]);
+          }
+          const float pb = sum8_rows(ev * gk), pw = sum8_rows(bt * vr * gk);
+          if (r == 0) {
+#pragma unroll
+            for (int e = 0; e < CPL; e += 4) {
+              *(f32x4*)(&sm.red[u][wv][ch0 + e]) = *(const f32x4*)(dq + e);
+              *(f32x4*)(&sm.red[u][wv][DK + ch0 + e]) = *(const f32x4*)(dk + e);
+              *(f32x4*)(&sm.red[u][wv][2 * DK + ch0 + e]) = *(const f32x4*)(dz + e);
+            }
+          }
+          if (l == 0) {
+            sm.redb[u][wv][0] = pb;
+            sm.redb[u][wv][1] = pw;
+          }
+          if (cs == 0) p.grad_v[(bh + (size_t)(t0 + t) * H) * DV + v0 + row] = wt * bg;
+        }
+      }
+      lds_barrier();
+      // the workgroup's sums for the group's tokens -> this tile's partials
+      for (int idx = tid; idx < 8 * 3 * DK; idx += NT) {
+        const int u = idx / (3 * DK), rem = idx % (3 * DK), qd = rem / DK, ch = rem % DK;
+        const int t = 8 * grp + u;
+        if (t >= nt) continue;
+        const float sum = sm.red[u][0][rem] + sm.red[u][1][rem] + sm.red[u][2][rem] + sm.red[u][3][rem];
+        const size_t trow = bh + (size_t)(t0 + t) * H;
+        const size_t o = ((size_t)vt * BTH + trow) * DK;
+        if (qd == 0) {
+          Pq[o + ch] = sum;
+        } else if (qd == 1) {
+          Pk[o + ch] = sum;
+        } else if constexpr (DECAY == 0) {
+          Pl[o + ch] = sum;
+        } else if ((ch & 1) == 0) {
+          // (d/d(gamma c), d/d(gamma s)) -> d/d(gamma) = dzr c + dzi s,
+          // d/d(theta) = dzi (gamma c) - dzr (gamma s)
+          const float dzi = sm.red[u][0][rem + 1] + sm.red[u][1][rem + 1] + sm.red[u][2][rem + 1] +
+                            sm.red[u][3][rem + 1];
+          const int pr = ch >> 1;
+          float sn, cn;
+          __sincosf(p.theta[trow * (DK / 2) + pr], &sn, &cn);
+          const float zr = sm.Z[t * DK + ch], zi = sm.Z[t * DK + ch + 1];
+          Pl[o + pr] = sum * cn + dzi * sn;
+          Pl[o + DK / 2 + pr] = dzi * zr - sum * zi;
+        }
+      }
+      if (tid < 16) {
+        const int u = tid >> 1, which = tid & 1, t = 8 * grp + u;
+        if (t < nt) {
+          const float sum = sm.redb[u][0][which] + sm.redb[u][1][which] + sm.redb[u][2][which] +
+                            sm.redb[u][3][which];
+          const size_t trow = bh + (size_t)(t0 + t) * H;
+          (which == 0 ? Pb : Pw)[(size_t)vt * BTH + trow] = sum;
+        }
+      }
+      lds_barrier();
+    }
+  }
+  if (p.grad_S0) {
+#pragma unroll
+    for (int e = 0; e < CPL; ++e) p.grad_S0[srow + e] = gr[e];
+  }
 }
 
 // Sums the value tiles' partials; turns the per-token log-gradients of the
@@ -676,6 +1012,8 @@ __global__ __launch_bounds__(DK) void bwd_reduce_kernel(BwdParams p) {
   const float* Pl = Pk + (size_t)nvt * BTH * DK;
   const float* Pb = Pl + (size_t)nvt * BTH * DK;
   const float* Pw = Pb + (size_t)nvt * BTH;
+  // flagged heads: the token path's partials are already the decay's gradients
+  const bool direct = p.flag[unit * nvt] != 0;
   float acc0 = 0.f, acc1 = 0.f;
   for (int r = nt - 1; r >= 0; --r) {
     const size_t row = bh + (size_t)(t0 + r) * H;
@@ -695,12 +1033,12 @@ __global__ __launch_bounds__(DK) void bwd_reduce_kernel(BwdParams p) {
     p.grad_k[row * DK + j] = sk;
     if (DECAY == 0) {
       acc0 += sl0;
-      p.grad_alpha[row * DK + j] = acc0 / p.alpha[row * DK + j];
+      p.grad_alpha[row * DK + j] = direct ? sl0 : acc0 / p.alpha[row * DK + j];
     } else if (j < DK / 2) {
       acc0 += sl0;
       acc1 += sl1;
-      p.grad_alpha[row * (DK / 2) + j] = acc0 / p.alpha[row * (DK / 2) + j];
-      p.grad_theta[row * (DK / 2) + j] = acc1;
+      p.grad_alpha[row * (DK / 2) + j] = direct ? sl0 : acc0 / p.alpha[row * (DK / 2) + j];
+      p.grad_theta[row * (DK / 2) + j] = direct ? sl1 : acc1;
     }
     if (j == 0) {
       float sb = 0.f, sw = 0.f;
@@ -721,6 +1059,10 @@ hipError_t launch_dk(const BwdParams& p0, hipStream_t s) {
   const int nc = (p.T + L - 1) / L;
   hipLaunchKernelGGL((bwd_kernel<DK, DECAY>), dim3(p.B * p.H * p.n_vt), dim3(NT), 0, s, p);
   hipError_t e = hipGetLastError();
+  if (e != hipSuccess) return e;
+  // same grid: each workgroup reads the flag bwd_kernel wrote for it
+  hipLaunchKernelGGL((bwd_token_kernel<DK, DECAY>), dim3(p.B * p.H * p.n_vt), dim3(NT), 0, s, p);
+  e = hipGetLastError();
   if (e != hipSuccess) return e;
   hipLaunchKernelGGL((bwd_reduce_kernel<DK, DECAY>), dim3(p.B * p.H * nc), dim3(DK), 0, s, p);
   return hipGetLastError();

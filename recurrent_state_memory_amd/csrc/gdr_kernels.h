@@ -66,6 +66,7 @@ struct BwdParams {
   float* grad_S0;        // or null
   const float* ckpt;
   float* part;           // partial sums, bwd_part_floats() floats
+  int* flag;             // per (b, h, value tile): a block left the block form's range
   int n_vt;              // value tiles per (b, h); set by the launcher
 };
 

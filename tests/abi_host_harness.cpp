@@ -164,8 +164,9 @@ int main() {
   w.grad_q = (float*)fake(8); w.grad_k = (float*)fake(9); w.grad_v = (float*)fake(10);
   w.grad_alpha = (float*)fake(11); w.grad_beta = (float*)fake(12); w.grad_w = (float*)fake(13);
   const size_t need = gdr_chunk_bwd_workspace(&w);
-  // 4 blocks of 32: checkpoints 2*4*4*128*128*4, o 800*128*2, partials 4*800*386*4
-  CHECK(need == (size_t)2 * 4 * 4 * 128 * 128 * 4 + 800 * 128 * 2 + (size_t)4 * 800 * 386 * 4);
+  // 4 blocks of 32: checkpoints 2*4*4*128*128*4, o 800*128*2, partials 4*800*386*4,
+  // range flags 2*4*4 ints (one 256-byte region)
+  CHECK(need == (size_t)2 * 4 * 4 * 128 * 128 * 4 + 800 * 128 * 2 + (size_t)4 * 800 * 386 * 4 + 256);
   CHECK(gdr_chunk_bwd(&w, nullptr) == GDR_ERR_WORKSPACE);
   w.workspace = fake(20); w.workspace_bytes = need - 1;
   CHECK(gdr_chunk_bwd(&w, nullptr) == GDR_ERR_WORKSPACE);
@@ -177,6 +178,8 @@ int main() {
   CHECK(gdr::g_bwd.ckpt == gdr::g_fwd.ckpt && gdr::g_bwd.grad_q == w.grad_q && gdr::g_bwd.grad_S0 == nullptr);
   CHECK((char*)gdr::g_bwd.part >= (char*)gdr::g_fwd.o + 800 * 128 * 2);
   CHECK((char*)gdr::g_bwd.part + (size_t)4 * 800 * 386 * 4 <= (char*)w.workspace + need);
+  CHECK((char*)gdr::g_bwd.flag >= (char*)gdr::g_bwd.part + (size_t)4 * 800 * 386 * 4);
+  CHECK((char*)(gdr::g_bwd.flag + 2 * 4 * 4) <= (char*)w.workspace + need);
   {
     gdr_bwd_args x = w; x.dk = x.dv = 32; CHECK(gdr_chunk_bwd(&x, nullptr) == GDR_ERR_UNSUPPORTED);
     CHECK(gdr_chunk_bwd_workspace(&x) == 0);

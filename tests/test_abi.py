@@ -199,13 +199,15 @@ def test_bwd_noalloc_rejects_before_any_hip_call():
 
 
 def test_bwd_workspace_size():
-    """Checkpoints of every 32-token block, the recompute's o and the partials."""
+    """Checkpoints of every 32-token block, the recompute's o, the partials and
+    one range flag per (b, h, 32-channel value tile)."""
     lib = gdr.load_library()
     a = _good_bwd()
     nc = (100 + 31) // 32
-    want = 2 * 4 * nc * 64 * 64 * 4 + 2 * 100 * 4 * 64 * 2 + 2 * (2 * 100 * 4) * (3 * 64 + 2) * 4
-    rounded = sum(-(-x // 256) * 256 for x in (2 * 4 * nc * 64 * 64 * 4, 2 * 100 * 4 * 64 * 2,
-                                               2 * (2 * 100 * 4) * (3 * 64 + 2) * 4))
+    parts = (2 * 4 * nc * 64 * 64 * 4, 2 * 100 * 4 * 64 * 2, 2 * (2 * 100 * 4) * (3 * 64 + 2) * 4,
+             2 * 4 * 2 * 4)
+    want = sum(parts)
+    rounded = sum(-(-x // 256) * 256 for x in parts)
     assert lib.gdr_chunk_bwd_workspace(ctypes.byref(a)) == rounded >= want
     assert lib.gdr_chunk_bwd_workspace(ctypes.byref(_good_bwd(dk=48, dv=48))) == 0
 
