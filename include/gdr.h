@@ -191,8 +191,8 @@ gdr_status gdr_chunk_fwd_gated(const gdr_fwd_args *a, const gdr_gate_args *g, vo
  * 2^29; otherwise GDR_ERR_UNSUPPORTED.  Range: every decay in [0, 1] is
  * supported.  A head with a 32-token block whose decay product in some key
  * channel (or pair) falls below e^-40 is redone token by token in fp32 with no
- * division (exact for decays of 0), at a few times the cost of that head's
- * block form.
+ * division (exact for decays of 0); such a head costs several times its block
+ * form (about 5x the whole call when every head needs it).
  *
  * Layouts (fp32 gradients, same shapes as the inputs):
  *   grad_q, grad_k [B,T,H,dk]; grad_v [B,T,H,dv]; grad_alpha as alpha
