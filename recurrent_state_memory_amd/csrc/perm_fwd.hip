@@ -16,7 +16,7 @@
 // LDS row buffer (a source outside [0, d_k) is mapped at staging to a column
 // that always holds 0, so the gather has no test), the two dot products through
 // DPP butterflies inside each group of 8 lanes.  Workgroups (one head, 32 value
-// rows) stage 16 tokens of k, q (bf16), the source maps, v, beta and w in
+// rows) stage 16 tokens of k, q (as fp32), the source maps, v, beta and w in
 // LDS, with the next chunk's loads in flight; the value blocks of one head
 // share an XCD, so keys, queries and maps come from its L2 after the first
 // reader.  Staging also classifies every token's map (the same for all rows):
@@ -41,10 +41,18 @@ constexpr int ROWS = 4 * RPW;
 
 constexpr int kGeneral = 0, kIdentity = 1, kDown = 2, kUp = 3;
 
+// Keys and queries in LDS as fp32 rows of KRS floats: the 16-channel slice of
+// lane group c starts at 20 c (d_k = 128), so the eight slices one wave reads
+// per token sit in distinct banks; 8-channel slices (d_k = 64) need no padding.
+template <int D>
+constexpr int kq_pad() { return D / 8 == 16 ? 4 : 0; }
+template <int D>
+constexpr int kq_rs() { return D + 8 * kq_pad<D>(); }
+
 template <int D>
 struct Sh {
-  bf Kc[L * D];
-  bf Qc[L * D];
+  float Kc[L * kq_rs<D>()];   // keys and queries, unpacked from bf16 at staging
+  float Qc[L * kq_rs<D>()];
   int16_t Sc[L * D];       // source channel, or D (the zero column) where there is none
   bf Vc[L * ROWS];
   float Bc[L];             // beta
@@ -167,8 +175,11 @@ __global__ __launch_bounds__(NT) void perm_fwd_kernel(PermParams p) {
     const uint32_t fx[4] = {src_fix(rs.x, D), src_fix(rs.y, D), src_fix(rs.z, D), src_fix(rs.w, D)};
     const unsigned cls = tid < NPIECE ? classify8<D>(fx, pch) : 0u;
     if (tid < NPIECE) {
-      *(uint4*)(sh.Kc + pt * D + pch) = rk;
-      *(uint4*)(sh.Qc + pt * D + pch) = rq;
+      const int kq = pt * kq_rs<D>() + pch + (pch / CPL) * kq_pad<D>();
+      *(float4*)(sh.Kc + kq) = float4{bf_lo(rk.x), bf_hi(rk.x), bf_lo(rk.y), bf_hi(rk.y)};
+      *(float4*)(sh.Kc + kq + 4) = float4{bf_lo(rk.z), bf_hi(rk.z), bf_lo(rk.w), bf_hi(rk.w)};
+      *(float4*)(sh.Qc + kq) = float4{bf_lo(rq.x), bf_hi(rq.x), bf_lo(rq.y), bf_hi(rq.y)};
+      *(float4*)(sh.Qc + kq + 4) = float4{bf_lo(rq.z), bf_hi(rq.z), bf_lo(rq.w), bf_hi(rq.w)};
       *(uint4*)(sh.Sc + pt * D + pch) = uint4{fx[0], fx[1], fx[2], fx[3]};
     }
     {   // a token's PPT pieces sit in PPT consecutive lanes of one wave
@@ -197,15 +208,28 @@ __global__ __launch_bounds__(NT) void perm_fwd_kernel(PermParams p) {
   for (int c = 0; c < nchunks; ++c) {
     const int c0 = c * L;
     const int tn = T - c0 < L ? T - c0 : L;
+    // the chunk's map kinds, 2 bits per token, in one scalar register
+    unsigned kbits = 0u;
+#pragma unroll
+    for (int i = 0; i < L; ++i) kbits |= (unsigned)__builtin_amdgcn_readfirstlane(sh.Kind[i]) << (2 * i);
 #pragma unroll 1
     for (int t = 0; t < tn; ++t) {
       const int base = t * D + cg * CPL;
+      // this token's keys, queries, value and gates first: none depends on the row
+      float xs[CPL], kf[CPL], qf[CPL];
+      const int kqb = t * kq_rs<D>() + cg * (CPL + kq_pad<D>());
+#pragma unroll
+      for (int e = 0; e < CPL; e += 4) {
+        *(float4*)(kf + e) = *(const float4*)(sh.Kc + kqb + e);
+        *(float4*)(qf + e) = *(const float4*)(sh.Qc + kqb + e);
+      }
+      const float vr = (float)sh.Vc[t * ROWS + RPW * w + r];
+      const float bt = sh.Bc[t], wt = sh.Wc[t];
       // column selection: the structured maps in registers (a lane's first or
       // last channel comes from the neighbouring lane of the same row, or is
       // the emptied channel), any other map through this row's LDS buffer
       // (source D reads the zero)
-      float xs[CPL], kf[CPL], qf[CPL];
-      const int kind = __builtin_amdgcn_readfirstlane(sh.Kind[t]);
+      const int kind = (int)((kbits >> (2 * t)) & 3u);
       if (kind == kIdentity) {
 #pragma unroll
         for (int e = 0; e < CPL; ++e) xs[e] = x[e];
@@ -235,26 +259,11 @@ __global__ __launch_bounds__(NT) void perm_fwd_kernel(PermParams p) {
 #pragma unroll
         for (int e = 0; e < CPL; ++e) xs[e] = rbuf[e & 1 ? sw[e >> 1] >> 16 : sw[e >> 1] & 0xffffu];
       }
-#pragma unroll
-      for (int e = 0; e < CPL; e += 8) {
-        const uint4 k8 = *(const uint4*)(sh.Kc + base + e);
-        const uint4 q8 = *(const uint4*)(sh.Qc + base + e);
-        const uint32_t kw[4] = {k8.x, k8.y, k8.z, k8.w};
-        const uint32_t qw[4] = {q8.x, q8.y, q8.z, q8.w};
-#pragma unroll
-        for (int u = 0; u < 4; ++u) {
-          kf[e + 2 * u] = bf_lo(kw[u]);
-          kf[e + 2 * u + 1] = bf_hi(kw[u]);
-          qf[e + 2 * u] = bf_lo(qw[u]);
-          qf[e + 2 * u + 1] = bf_hi(qw[u]);
-        }
-      }
       float a4[4] = {0.f, 0.f, 0.f, 0.f};
 #pragma unroll
       for (int e = 0; e < CPL; ++e) a4[e & 3] += xs[e] * kf[e];
       const float y = row_sum((a4[0] + a4[1]) + (a4[2] + a4[3]));
-      const float vr = (float)sh.Vc[t * ROWS + RPW * w + r];
-      const float coef = sh.Bc[t] * (sh.Wc[t] * vr - y);   // beta (w v - X k)
+      const float coef = bt * (wt * vr - y);   // beta (w v - X k)
       float b4[4] = {0.f, 0.f, 0.f, 0.f};
 #pragma unroll
       for (int e = 0; e < CPL; ++e) {
