@@ -704,11 +704,13 @@ struct TokSmem {
   float redb[8][4][2];        // dbeta, dw row sums
 };
 
-// sum over the 8 neighbouring lanes 8c .. 8c + 7; every lane gets it
+// sum over the 8 neighbouring lanes 8c .. 8c + 7; every lane gets it (no lane
+// reads outside its row, so bound_ctrl never applies; with it set the compiler
+// folds each move into the add as a DPP operand)
 __device__ inline float sum8_rows(float x) {
-  x += __int_as_float(__builtin_amdgcn_mov_dpp(__float_as_int(x), 0xb1, 0xf, 0xf, false));    // lane ^ 1
-  x += __int_as_float(__builtin_amdgcn_mov_dpp(__float_as_int(x), 0x4e, 0xf, 0xf, false));    // lane ^ 2
-  x += __int_as_float(__builtin_amdgcn_mov_dpp(__float_as_int(x), 0x141, 0xf, 0xf, false));   // 7 - lane in 8
+  x += __int_as_float(__builtin_amdgcn_update_dpp(0, __float_as_int(x), 0xb1, 0xf, 0xf, true));    // lane ^ 1
+  x += __int_as_float(__builtin_amdgcn_update_dpp(0, __float_as_int(x), 0x4e, 0xf, 0xf, true));    // lane ^ 2
+  x += __int_as_float(__builtin_amdgcn_update_dpp(0, __float_as_int(x), 0x141, 0xf, 0xf, true));   // 7 - lane in 8
   return x;
 }
 // sum over the lanes r, r + 8, ..., r + 56 (one row's channel slices)

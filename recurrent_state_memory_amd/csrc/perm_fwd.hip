@@ -62,19 +62,13 @@ struct Sh {
   bf Oc[L * ROWS];
 };
 
-__device__ inline float dpp_f(float x, int ctrl) {
-  int r;
-  const int u = __float_as_int(x);
-  if (ctrl == 0xb1) r = __builtin_amdgcn_mov_dpp(u, 0xb1, 0xf, 0xf, false);         // lane ^ 1
-  else if (ctrl == 0x4e) r = __builtin_amdgcn_mov_dpp(u, 0x4e, 0xf, 0xf, false);    // lane ^ 2
-  else r = __builtin_amdgcn_mov_dpp(u, 0x141, 0xf, 0xf, false);                     // 7 - lane in 8
-  return __int_as_float(r);
-}
-// sum over 8 aligned lanes; every lane gets the same value
+// sum over 8 aligned lanes; every lane gets the same value (no lane reads
+// outside its row, so bound_ctrl never applies; with it set the compiler folds
+// each move into the add as a DPP operand)
 __device__ inline float row_sum(float x) {
-  x += dpp_f(x, 0xb1);
-  x += dpp_f(x, 0x4e);
-  x += dpp_f(x, 0x141);
+  x += __int_as_float(__builtin_amdgcn_update_dpp(0, __float_as_int(x), 0xb1, 0xf, 0xf, true));
+  x += __int_as_float(__builtin_amdgcn_update_dpp(0, __float_as_int(x), 0x4e, 0xf, 0xf, true));
+  x += __int_as_float(__builtin_amdgcn_update_dpp(0, __float_as_int(x), 0x141, 0xf, 0xf, true));
   return x;
 }
 
