@@ -595,8 +595,14 @@ def main(argv=None):
     traffic = None
     if a.workload == "layer":
         traffic = _traffic(TRAFFIC_FILE_GATED if gated else TRAFFIC_FILE)
+    # the headline metric names the layer workload; variants name their own
+    if a.workload == "layer" and not gated:
+        metric = METRIC
+    else:
+        metric = (f"tokens/sec gated-delta chunk fwd{' (gated)' if gated else ''} "
+                  f"({wl.name}: B={wl.B},H={wl.H},d={wl.dk},T={wl.T}) + % MFMA/HBM roofline")
     out = {
-        "metric": METRIC,
+        "metric": metric,
         "value": round(value, 1),
         "unit": "tokens/s",
         "n_gpus": 1,
