@@ -19,7 +19,10 @@ L = sum(dO * o) + sum(dS_T * S_T), with respect to q, k, v, w, beta, the
 transition (alpha, or gamma and theta) and S_0.
 
 ``backward_seq`` walks the tokens backwards (the plain definition of reverse
-mode; pinned by central finite differences in the tests).  ``backward_chunk``
+mode; pinned by central finite differences in the tests).  ``backward_gated``
+adds the chain rule through the gated forward's decay activation
+exp(-a_h softplus(x)) and per-token q/k normalisation (``oracle.seq.forward_gated``;
+also pinned by finite differences).  ``backward_chunk``
 obtains the same gradients from the chunk form that a chunk-parallel kernel
 evaluates: per chunk, the WY factors are rebuilt from the chunk's start state,
 and the adjoint runs through those matrix expressions in reverse.
@@ -30,6 +33,7 @@ from typing import Optional
 
 import numpy as np
 
+from oracle import seq as _seq
 from oracle.seq import transition
 
 
@@ -291,4 +295,40 @@ def backward_chunk(q, k, v, w, alpha, beta, dO, dS_T=None, theta=None, decay="di
                     out["dtheta"][b, sl, h] = dth
                 G = dS
             out["dS0"][b, h] = G
+    return out
+
+
+def backward_gated(q_raw, k_raw, v, w, x, a, beta, dO, dS_T=None, theta=None, decay="diag",
+                   S0=None, qk_l2norm=True):
+    """Gradients of ``oracle.seq.forward_gated`` for the same scalar loss.
+
+    The forward is ``forward(l2(q_raw), l2(k_raw), v, w, exp(-a_h softplus(x)))``
+    (CARVE technical summary, section 2.3: the decay activation computed where
+    it is used), with l2(y) = y / sqrt(sum y^2 + eps) per token when
+    ``qk_l2norm``.  Its gradients are ``backward_seq``'s at the activated,
+    normalised inputs, carried back by the chain rule:
+      d decay / dx = -a_h sigmoid(x) decay,  d decay / da_h = -softplus(x) decay,
+      dL/dy = (g - u (u . g)) / n  with n = sqrt(sum y^2 + eps), u = y / n,
+        g = dL/dl2(y).
+    Returns dq, dk (of the raw inputs), dv, dw, dbeta, dx, da [H], dtheta
+    (rot2) and dS0.
+    """
+    x64, a64 = np.asarray(x, dtype=np.float64), np.asarray(a, dtype=np.float64)
+    alpha = _seq.gated_decay(x64, a64)
+    if qk_l2norm:
+        q, k = _seq.l2_normalise(q_raw), _seq.l2_normalise(k_raw)
+    else:
+        q, k = _f64(q_raw), _f64(k_raw)
+    g = backward_seq(q, k, v, w, alpha, beta, dO, dS_T, theta=theta, decay=decay, S0=S0)
+    out = {n: t for n, t in g.items() if n != "dalpha"}
+    gd = g["dalpha"] * alpha                        # dL/d(decay) times the decay
+    out["dx"] = gd * (-a64[:, None]) * _seq.sigmoid(x64)
+    out["da"] = np.sum(gd * -_seq.softplus(x64), axis=(0, 1, 3))
+    if qk_l2norm:
+        for name, raw in (("dq", q_raw), ("dk", k_raw)):
+            y = _f64(raw)
+            n = np.sqrt(np.sum(y * y, axis=-1, keepdims=True) + _seq.L2NORM_EPS)
+            u = y / n
+            gn = out[name]
+            out[name] = (gn - u * np.sum(u * gn, axis=-1, keepdims=True)) / n
     return out

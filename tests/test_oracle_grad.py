@@ -124,3 +124,72 @@ def test_chunk_backward_without_final_state_gradient():
                              theta=x["theta"], decay="rot2", chunk=4)
     for n in g1:
         assert np.max(np.abs(g1[n] - g2[n])) < 1e-11, n
+
+
+def _gated_case(decay, B=1, T=5, H=2, d=4, seed=11):
+    rng = np.random.default_rng(seed)
+    C = d if decay == "diag" else d // 2
+    x = dict(
+        q=rng.standard_normal((B, T, H, d)),
+        k=rng.standard_normal((B, T, H, d)),
+        v=rng.standard_normal((B, T, H, d)),
+        w=rng.uniform(0.2, 1.0, (B, T, H)),
+        beta=rng.uniform(0.1, 0.9, (B, T, H)),
+        x=rng.standard_normal((B, T, H, C)),
+        a=rng.uniform(0.3, 1.5, (H,)),
+        theta=None if decay == "diag" else rng.uniform(-3.0, 3.0, (B, T, H, C)),
+        S0=rng.standard_normal((B, H, d, d)) * 0.3,
+    )
+    return x, rng.standard_normal((B, T, H, d)), rng.standard_normal((B, H, d, d))
+
+
+GATED_NAMES = {"q": "dq", "k": "dk", "v": "dv", "w": "dw", "beta": "dbeta", "x": "dx", "a": "da",
+               "theta": "dtheta", "S0": "dS0"}
+
+
+@pytest.mark.parametrize("qk_l2norm", [True, False])
+@pytest.mark.parametrize("decay", ["diag", "rot2"])
+def test_backward_gated_matches_finite_differences(decay, qk_l2norm):
+    """backward_gated (chain rule through exp(-a softplus(x)) and the per-token
+    q/k normalisation) against central differences of seq.forward_gated, every
+    element of every input, the per-head scale a included."""
+    x, dO, dS = _gated_case(decay, seed=11 + qk_l2norm)
+
+    def loss(y):
+        o, S = seq.forward_gated(y["q"], y["k"], y["v"], y["w"], y["x"], y["a"], y["beta"],
+                                 theta=y["theta"], decay=decay, S0=y["S0"], qk_l2norm=qk_l2norm)
+        return float(np.sum(dO * o) + np.sum(dS * S))
+
+    g = grad.backward_gated(x["q"], x["k"], x["v"], x["w"], x["x"], x["a"], x["beta"], dO, dS,
+                            theta=x["theta"], decay=decay, S0=x["S0"], qk_l2norm=qk_l2norm)
+    assert set(g) == {n for k, n in GATED_NAMES.items() if x[k] is not None}
+    h = 1e-5
+    for name, gname in GATED_NAMES.items():
+        if x[name] is None:
+            continue
+        fd = np.empty_like(x[name])
+        for idx in np.ndindex(x[name].shape):
+            xp, xm = dict(x), dict(x)
+            xp[name], xm[name] = x[name].copy(), x[name].copy()
+            xp[name][idx] += h
+            xm[name][idx] -= h
+            fd[idx] = (loss(xp) - loss(xm)) / (2 * h)
+        err = np.max(np.abs(fd - g[gname]) / np.maximum(1.0, np.abs(fd)))
+        assert err < 1e-7, (decay, qk_l2norm, name, err)
+
+
+def test_backward_gated_without_gate_or_norm_is_backward_seq():
+    """a = 0 makes every decay 1 (and dx = 0); without normalisation the q, k, v,
+    w, beta and S0 gradients are backward_seq's with alpha = 1, and da is the
+    alpha gradient weighted by -softplus(x)."""
+    x, dO, dS = _gated_case("diag", seed=21)
+    a0 = np.zeros_like(x["a"])
+    g = grad.backward_gated(x["q"], x["k"], x["v"], x["w"], x["x"], a0, x["beta"], dO, dS,
+                            S0=x["S0"], qk_l2norm=False)
+    ones = np.ones_like(x["x"])
+    r = grad.backward_seq(x["q"], x["k"], x["v"], x["w"], ones, x["beta"], dO, dS, S0=x["S0"])
+    for n in ("dq", "dk", "dv", "dw", "dbeta", "dS0"):
+        assert np.array_equal(g[n], r[n]), n
+    assert np.all(g["dx"] == 0)
+    assert np.allclose(g["da"], np.sum(r["dalpha"] * -seq.softplus(x["x"]), axis=(0, 1, 3)),
+                       rtol=1e-14, atol=0)
