@@ -231,6 +231,35 @@ gdr_status gdr_chunk_bwd(const gdr_bwd_args *a, void *hip_stream);
  * that overlap on one GPU share the array and race.  Allocates nothing. */
 gdr_status gdr_chunk_bwd_noalloc(const gdr_bwd_args *a, void *hip_stream);
 
+/* Backward of gdr_chunk_fwd_gated: the gradients of the same loss when the
+ * decay arrives as its pre-activation (decay = exp(-a_h softplus(x))) and, with
+ * qk_l2norm, q and k are raw and normalised per token (CARVE technical summary,
+ * section 2.3: the activation computed where it is used).  It runs the plain
+ * backward on the activated, normalised inputs and carries the gradients back
+ * by the chain rule:
+ *   dL/dx = dL/d(decay) decay (-a_h) sigmoid(x),
+ *   dL/da_h = sum over batch rows, tokens and channels of
+ *             dL/d(decay) decay (-softplus(x)),
+ *   dL/dy = (g - u (u . g)) / n   (y = q or k, n = sqrt(y . y + 1e-6), u = y / n,
+ *                                  g the gradient of y / n).
+ * Arguments: a as for gdr_chunk_bwd, except that a->alpha and a->grad_alpha
+ * must be NULL (GDR_ERR_ARG otherwise); q and k are the raw inputs when
+ * g->qk_l2norm, and grad_q, grad_k are taken with respect to them.  g as for
+ * gdr_chunk_fwd_gated.  gg->grad_decay_x (fp32, decay_x's shape) and
+ * gg->grad_decay_a ([H] fp32) receive the gate gradients; theta's gradient
+ * (ROT2) goes to a->grad_theta as before.  The workspace holds the activated
+ * decay, the normalised q and k, their gradients, one fp32 per token-head, and
+ * the plain backward's workspace: at least gdr_chunk_bwd_gated_workspace bytes
+ * (0 when the arguments are invalid).  Supported as gdr_chunk_bwd. */
+typedef struct gdr_gate_grads {
+  float *grad_decay_x;  /* as decay_x: DIAG [B,T,H,dk], ROT2 [B,T,H,dk/2] */
+  float *grad_decay_a;  /* [H]                                            */
+} gdr_gate_grads;
+
+size_t gdr_chunk_bwd_gated_workspace(const gdr_bwd_args *a, const gdr_gate_args *g);
+gdr_status gdr_chunk_bwd_gated(const gdr_bwd_args *a, const gdr_gate_args *g,
+                               const gdr_gate_grads *gg, void *hip_stream);
+
 /* ------------------------------------------------------------------------ */
 /* Single-token decode step on N independent states, in place.               */
 /* ------------------------------------------------------------------------ */

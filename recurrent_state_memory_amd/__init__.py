@@ -55,6 +55,11 @@ class GateArgs(ctypes.Structure):
     _fields_ = [("decay_x", _vp), ("decay_a", _vp), ("qk_l2norm", _i32), ("reserved", _i32)]
 
 
+class GateGrads(ctypes.Structure):
+    """Mirror of ``gdr_gate_grads``."""
+    _fields_ = [("grad_decay_x", _vp), ("grad_decay_a", _vp)]
+
+
 class BwdArgs(ctypes.Structure):
     """Mirror of ``gdr_bwd_args``."""
     _fields_ = [
@@ -123,6 +128,11 @@ def load_library(path: Optional[str] = None) -> ctypes.CDLL:
     lib.gdr_chunk_bwd.restype = ctypes.c_int
     lib.gdr_chunk_bwd_noalloc.argtypes = [ctypes.POINTER(BwdArgs), _vp]
     lib.gdr_chunk_bwd_noalloc.restype = ctypes.c_int
+    lib.gdr_chunk_bwd_gated.argtypes = [ctypes.POINTER(BwdArgs), ctypes.POINTER(GateArgs),
+                                        ctypes.POINTER(GateGrads), _vp]
+    lib.gdr_chunk_bwd_gated.restype = ctypes.c_int
+    lib.gdr_chunk_bwd_gated_workspace.argtypes = [ctypes.POINTER(BwdArgs), ctypes.POINTER(GateArgs)]
+    lib.gdr_chunk_bwd_gated_workspace.restype = ctypes.c_size_t
     lib.gdr_chunk_bwd_workspace.argtypes = [ctypes.POINTER(BwdArgs)]
     lib.gdr_chunk_bwd_workspace.restype = ctypes.c_size_t
     lib.gdr_chunk_fwd_workspace.argtypes = [ctypes.POINTER(FwdArgs)]
@@ -215,6 +225,15 @@ def call_chunk_bwd(args: BwdArgs, stream=None) -> int:
     s = stream if isinstance(stream, ctypes.c_void_p) else (
         ctypes.c_void_p(0) if stream is None else _stream(stream))
     return lib.gdr_chunk_bwd(ctypes.byref(args), s)
+
+
+def call_chunk_bwd_gated(args: BwdArgs, gate: GateArgs, grads: GateGrads, stream=None) -> int:
+    """Raw call with filled ``BwdArgs``, ``GateArgs`` and ``GateGrads``; returns the
+    status code."""
+    lib = load_library()
+    s = stream if isinstance(stream, ctypes.c_void_p) else (
+        ctypes.c_void_p(0) if stream is None else _stream(stream))
+    return lib.gdr_chunk_bwd_gated(ctypes.byref(args), ctypes.byref(gate), ctypes.byref(grads), s)
 
 
 def call_chunk_bwd_noalloc(args: BwdArgs, stream=None) -> int:
@@ -439,6 +458,79 @@ def gdr_chunk_bwd(q, k, v, alpha, w, beta, grad_o, *, theta=None, S0=None, grad_
         raise ValueError(f"gdr: workspace must be a uint8 tensor of at least {need} bytes")
     a.workspace, a.workspace_bytes = _ptr(workspace), workspace.numel()
     _check(call_chunk_bwd(a, _stream(stream)))
+    return g
+
+
+def gdr_chunk_bwd_gated(q, k, v, decay_x, decay_a, w, beta, grad_o, *, theta=None,
+                        qk_l2norm=True, S0=None, grad_S=None, need_grad_S0=True,
+                        workspace=None, stream=None):
+    """Gradients of the gated forward (``gdr_chunk_bwd_gated`` in include/gdr.h).
+
+    Inputs as ``gdr_chunk_fwd_gated`` (bf16 q, k, v, raw q and k when
+    ``qk_l2norm``; bf16 decay_x [B,T,H,dk] or [B,T,H,dk/2] with ``theta``; fp32
+    decay_a [H], beta, w) plus grad_o [B,T,H,dv] bf16 and optional grad_S
+    [B,H,dv,dk] fp32.  Returns a dict of fp32 tensors: q, k (of the raw
+    inputs), v, x (decay_x), a (decay_a), beta, w, theta (rotation decay only)
+    and S0 (when ``need_grad_S0``).  The workspace
+    (``gdr_chunk_bwd_gated_workspace`` bytes) is allocated here unless a large
+    enough uint8 CUDA tensor is passed.
+    """
+    import torch
+    if q.dim() != 4 or k.dim() != 4 or v.dim() != 4:
+        raise ValueError("gdr: q, k and v must be [B,T,H,d]")
+    B, T, H, dk = q.shape
+    dv = v.shape[-1]
+    bf, f32 = torch.bfloat16, torch.float32
+    _expect(q, "q", (B, T, H, dk), bf)
+    _expect(k, "k", (B, T, H, dk), bf)
+    _expect(v, "v", (B, T, H, dv), bf)
+    rot = theta is not None
+    if rot and dk % 2:
+        raise ValueError("gdr: rotation-decay blocks need an even d_k")
+    gshape = (B, T, H, dk // 2) if rot else (B, T, H, dk)
+    _expect(decay_x, "decay_x", gshape, bf)
+    _expect(theta, "theta", gshape, f32, required=False)
+    _expect(decay_a, "decay_a", (H,), f32)
+    _expect(w, "w", (B, T, H), f32)
+    _expect(beta, "beta", (B, T, H), f32)
+    _expect(S0, "S0", (B, H, dv, dk), f32, required=False)
+    _expect(grad_o, "grad_o", (B, T, H, dv), bf)
+    _expect(grad_S, "grad_S", (B, H, dv, dk), f32, required=False)
+    dev = q.device
+    g = {"q": torch.empty((B, T, H, dk), dtype=f32, device=dev),
+         "k": torch.empty((B, T, H, dk), dtype=f32, device=dev),
+         "v": torch.empty((B, T, H, dv), dtype=f32, device=dev),
+         "x": torch.empty(gshape, dtype=f32, device=dev),
+         "a": torch.empty((H,), dtype=f32, device=dev),
+         "beta": torch.empty((B, T, H), dtype=f32, device=dev),
+         "w": torch.empty((B, T, H), dtype=f32, device=dev)}
+    if rot:
+        g["theta"] = torch.empty(gshape, dtype=f32, device=dev)
+    if need_grad_S0:
+        g["S0"] = torch.empty((B, H, dv, dk), dtype=f32, device=dev)
+    a = BwdArgs()
+    a.B, a.T, a.H, a.dk, a.dv = B, T, H, dk, dv
+    a.decay = GDR_DECAY_ROT2 if rot else GDR_DECAY_DIAG
+    a.q, a.k, a.v, a.theta = map(_ptr, (q, k, v, theta))
+    a.alpha, a.grad_alpha = None, None
+    a.beta, a.w, a.S0, a.grad_o, a.grad_S = map(_ptr, (beta, w, S0, grad_o, grad_S))
+    a.grad_q, a.grad_k, a.grad_v = _ptr(g["q"]), _ptr(g["k"]), _ptr(g["v"])
+    a.grad_theta = _ptr(g.get("theta"))
+    a.grad_beta, a.grad_w, a.grad_S0 = _ptr(g["beta"]), _ptr(g["w"]), _ptr(g.get("S0"))
+    ga = GateArgs()
+    ga.decay_x, ga.decay_a = _ptr(decay_x), _ptr(decay_a)
+    ga.qk_l2norm, ga.reserved = int(bool(qk_l2norm)), 0
+    gg = GateGrads()
+    gg.grad_decay_x, gg.grad_decay_a = _ptr(g["x"]), _ptr(g["a"])
+    need = load_library().gdr_chunk_bwd_gated_workspace(ctypes.byref(a), ctypes.byref(ga))
+    if need == 0:
+        _check(call_chunk_bwd_gated(a, ga, gg, _stream(stream)))   # reports why the arguments are invalid
+    if workspace is None:
+        workspace = torch.empty(need, dtype=torch.uint8, device=dev)
+    if workspace.dtype != torch.uint8 or workspace.numel() < need:
+        raise ValueError(f"gdr: workspace must be a uint8 tensor of at least {need} bytes")
+    a.workspace, a.workspace_bytes = _ptr(workspace), workspace.numel()
+    _check(call_chunk_bwd_gated(a, ga, gg, _stream(stream)))
     return g
 
 

@@ -21,7 +21,7 @@ ROOT = os.path.dirname(HERE)
 BUILD = os.path.join(ROOT, "_build")
 LIB = os.path.join(HERE, "libgdr.so")
 
-SOURCES = ["gdr_api.cpp", "gdr_fwd.hip", "gdr_fwd_pipe.hip", "gdr_step.hip", "gdr_bwd.hip", "gdr_noalloc.hip",
+SOURCES = ["gdr_api.cpp", "gdr_fwd.hip", "gdr_fwd_pipe.hip", "gdr_step.hip", "gdr_bwd.hip", "gdr_gate_bwd.hip", "gdr_noalloc.hip",
            "raven_api.cpp", "raven_fwd.hip", "perm_api.cpp", "perm_fwd.hip"]
 
 HIPCC = os.environ.get("HIPCC", shutil.which("hipcc") or "/opt/rocm/bin/hipcc")

@@ -311,6 +311,132 @@ gdr_status chunk_bwd_on(const gdr_bwd_args* a, void* workspace, size_t workspace
 
 }  // namespace gdr
 
+// ---------------------------------------------------------------- gated backward
+namespace {
+
+// Workspace of gdr_chunk_bwd_gated: the activated decay and its gradient, the
+// normalised q, k and their gradients (qk_l2norm), one fp32 per token-head
+// (its part of dL/da_h), then the plain backward's own workspace.
+struct GateLayout {
+  size_t alpha, galpha, qn, kn, gqn, gkn, ga, inner, inner_bytes, total;
+};
+
+alignas(16) const float kPlaceholder[4] = {0.f, 0.f, 0.f, 0.f};
+
+// The plain backward's arguments for a gated call: the activated decay and its
+// gradient in the workspace (placeholders until the workspace is known).
+gdr_bwd_args inner_args(const gdr_bwd_args* a) {
+  gdr_bwd_args t = *a;
+  t.alpha = kPlaceholder;
+  t.grad_alpha = const_cast<float*>(kPlaceholder);
+  t.workspace = nullptr;
+  t.workspace_bytes = 0;
+  return t;
+}
+
+// Everything but the workspace; gg may be NULL for the size query.
+gdr_status check_gated_bwd(const gdr_bwd_args* a, const gdr_gate_args* g, const gdr_gate_grads* gg,
+                           bool need_grads) {
+  if (!a || !g) return GDR_ERR_NULL;
+  if (a->alpha || a->grad_alpha) return GDR_ERR_ARG;
+  if (g->reserved != 0) return GDR_ERR_ARG;
+  if (!g->decay_x || !g->decay_a) return GDR_ERR_NULL;
+  if (need_grads && (!gg || !gg->grad_decay_x || !gg->grad_decay_a)) return GDR_ERR_NULL;
+  if ((reinterpret_cast<uintptr_t>(g->decay_x) & 1u) != 0) return GDR_ERR_ALIGN;
+  if ((reinterpret_cast<uintptr_t>(g->decay_a) & 3u) != 0) return GDR_ERR_ALIGN;
+  if (gg && ((reinterpret_cast<uintptr_t>(gg->grad_decay_x) & 3u) != 0 ||
+             (reinterpret_cast<uintptr_t>(gg->grad_decay_a) & 3u) != 0))
+    return GDR_ERR_ALIGN;
+  const gdr_bwd_args t = inner_args(a);
+  return check_bwd_args(&t);
+}
+
+GateLayout gate_layout(const gdr_bwd_args* a, bool norm) {
+  const size_t rows = (size_t)a->B * a->T * a->H;
+  const size_t C = a->decay == GDR_DECAY_ROT2 ? a->dk / 2 : a->dk;
+  const gdr_bwd_args t = inner_args(a);
+  GateLayout w{};
+  size_t o = 0;
+  w.alpha = o;
+  o += round256(rows * C * sizeof(float));
+  w.galpha = o;
+  o += round256(rows * C * sizeof(float));
+  if (norm) {
+    w.qn = o;
+    o += round256(rows * a->dk * 2);
+    w.kn = o;
+    o += round256(rows * a->dk * 2);
+    w.gqn = o;
+    o += round256(rows * a->dk * sizeof(float));
+    w.gkn = o;
+    o += round256(rows * a->dk * sizeof(float));
+  }
+  w.ga = o;
+  o += round256(rows * sizeof(float));
+  w.inner = o;
+  w.inner_bytes = bwd_layout(&t).total;
+  w.total = o + w.inner_bytes;
+  return w;
+}
+
+}  // namespace
+
+extern "C" {
+
+size_t gdr_chunk_bwd_gated_workspace(const gdr_bwd_args* a, const gdr_gate_args* g) {
+  if (check_gated_bwd(a, g, nullptr, false) != GDR_OK) return 0;
+  return gate_layout(a, g->qk_l2norm != 0).total;
+}
+
+gdr_status gdr_chunk_bwd_gated(const gdr_bwd_args* a, const gdr_gate_args* g,
+                               const gdr_gate_grads* gg, void* hip_stream) {
+  const gdr_status st = check_gated_bwd(a, g, gg, true);
+  if (st != GDR_OK) return st;
+  const bool norm = g->qk_l2norm != 0;
+  const GateLayout lay = gate_layout(a, norm);
+  if (!a->workspace || a->workspace_bytes < lay.total) return GDR_ERR_WORKSPACE;
+  if (!aligned16(a->workspace)) return GDR_ERR_ALIGN;
+  const hipStream_t stream = (hipStream_t)hip_stream;
+  char* ws = (char*)a->workspace;
+  gdr::GateBwdParams p{};
+  p.B = a->B;
+  p.T = a->T;
+  p.H = a->H;
+  p.DK = a->dk;
+  p.C = a->decay == GDR_DECAY_ROT2 ? a->dk / 2 : a->dk;
+  p.norm = norm ? 1 : 0;
+  p.x = g->decay_x;
+  p.a = g->decay_a;
+  p.q_raw = a->q;
+  p.k_raw = a->k;
+  p.alpha = (float*)(ws + lay.alpha);
+  p.q_n = norm ? ws + lay.qn : nullptr;
+  p.k_n = norm ? ws + lay.kn : nullptr;
+  p.grad_alpha = (const float*)(ws + lay.galpha);
+  p.grad_qn = norm ? (const float*)(ws + lay.gqn) : nullptr;
+  p.grad_kn = norm ? (const float*)(ws + lay.gkn) : nullptr;
+  p.grad_x = gg->grad_decay_x;
+  p.grad_q = a->grad_q;
+  p.grad_k = a->grad_k;
+  p.ga_rows = (float*)(ws + lay.ga);
+  p.grad_a = gg->grad_decay_a;
+  if (gdr::launch_gate_prep(p, stream) != hipSuccess) return GDR_ERR_HIP;
+  gdr_bwd_args t = *a;
+  t.alpha = p.alpha;
+  t.grad_alpha = (float*)(ws + lay.galpha);
+  if (norm) {
+    t.q = p.q_n;
+    t.k = p.k_n;
+    t.grad_q = (float*)(ws + lay.gqn);
+    t.grad_k = (float*)(ws + lay.gkn);
+  }
+  const gdr_status sb = gdr::chunk_bwd_on(&t, ws + lay.inner, lay.inner_bytes, stream);
+  if (sb != GDR_OK) return sb;
+  return gdr::launch_gate_chain(p, stream) == hipSuccess ? GDR_OK : GDR_ERR_HIP;
+}
+
+}  // extern "C"
+
 extern "C" {
 
 gdr_status gdr_step_decode(const gdr_step_args* a, void* hip_stream) {

@@ -1,0 +1,151 @@
+// gdr_gate_bwd.hip -- the gated forward's decay activation and q/k
+// normalisation around the plain backward, gfx950.
+//
+// The gated forward (CARVE technical summary, section 2.3: the decay
+// activation computed where it is used) runs the recurrence on
+//     decay = exp(-a_h softplus(x)),   q / n(q),  k / n(k),   n(y) = sqrt(y . y + 1e-6).
+// Its gradients are the plain backward's at those activated, normalised
+// inputs, carried back by the chain rule:
+//     dL/dx   = dL/d(decay) * decay * (-a_h) * sigmoid(x)
+//     dL/da_h = sum over (b, t, channels) of dL/d(decay) * decay * (-softplus(x))
+//     dL/dy   = (g - u (u . g)) / n(y),   u = y / n(y),  g = dL/d(y / n(y)).
+// gate_prep_kernel forms the decay (fp32) and the normalised q, k (bf16) for
+// the plain backward; gate_chain_kernel applies the chain rule; the per-head
+// scale's gradient is summed over rows in a fixed order by gate_a_kernel.
+// One wave per token-head row; the row's dot products reduce over the wave.
+#include <hip/hip_runtime.h>
+
+#include "gdr_kernels.h"
+
+namespace gdr {
+namespace gate {
+namespace {
+
+constexpr float kEps = 1e-6f;   // as the forward's normalisation
+constexpr int kRows = 4;        // rows (waves) per workgroup
+
+__device__ inline float bf2f(const void* p, size_t i) { return (float)((const __bf16*)p)[i]; }
+
+__device__ inline float wave_sum(float v) {
+#pragma unroll
+  for (int off = 32; off >= 1; off >>= 1) v += __shfl_xor(v, off);
+  return v;
+}
+
+// log(1 + e^x) without overflow, and without losing small values
+__device__ inline float softplus(float x) { return fmaxf(x, 0.f) + log1pf(expf(-fabsf(x))); }
+
+// Per-lane part of y . y over a row of DK bf16 values (lane l holds l, l + 64, ...).
+template <int DK>
+__device__ inline float row_sumsq(const void* y, size_t base, int l) {
+  float s = 0.f;
+#pragma unroll
+  for (int i = l; i < DK; i += 64) {
+    const float v = bf2f(y, base + i);
+    s += v * v;
+  }
+  return s;
+}
+
+template <int DK>
+__global__ __launch_bounds__(64 * kRows) void gate_prep_kernel(GateBwdParams p) {
+  const int l = threadIdx.x & 63;
+  const size_t rows = (size_t)p.B * p.T * p.H;
+  const size_t row = (size_t)blockIdx.x * kRows + (threadIdx.x >> 6);
+  if (row >= rows) return;   // whole waves leave together
+  const int h = (int)(row % p.H);
+  const float a = p.a[h];
+  for (int j = l; j < p.C; j += 64) {
+    const size_t i = row * p.C + j;
+    p.alpha[i] = expf(-a * softplus(bf2f(p.x, i)));
+  }
+  if (p.norm) {
+#pragma unroll
+    for (int which = 0; which < 2; ++which) {
+      const void* y = which ? p.k_raw : p.q_raw;
+      __bf16* yn = (__bf16*)(which ? p.k_n : p.q_n);
+      const size_t base = row * DK;
+      const float inv = 1.f / sqrtf(wave_sum(row_sumsq<DK>(y, base, l)) + kEps);
+#pragma unroll
+      for (int i = l; i < DK; i += 64) yn[base + i] = (__bf16)(bf2f(y, base + i) * inv);
+    }
+  }
+}
+
+template <int DK>
+__global__ __launch_bounds__(64 * kRows) void gate_chain_kernel(GateBwdParams p) {
+  const int l = threadIdx.x & 63;
+  const size_t rows = (size_t)p.B * p.T * p.H;
+  const size_t row = (size_t)blockIdx.x * kRows + (threadIdx.x >> 6);
+  if (row >= rows) return;
+  const int h = (int)(row % p.H);
+  const float a = p.a[h];
+  float ga = 0.f;
+  for (int j = l; j < p.C; j += 64) {
+    const size_t i = row * p.C + j;
+    const float x = bf2f(p.x, i);
+    const float gd = p.grad_alpha[i] * p.alpha[i];   // dL/d(decay) * decay
+    p.grad_x[i] = gd * (-a) * (1.f / (1.f + expf(-x)));
+    ga -= gd * softplus(x);
+  }
+  ga = wave_sum(ga);
+  if (l == 0) p.ga_rows[row] = ga;
+  if (p.norm) {
+#pragma unroll
+    for (int which = 0; which < 2; ++which) {
+      const void* y = which ? p.k_raw : p.q_raw;
+      const float* gn = which ? p.grad_kn : p.grad_qn;
+      float* gy = which ? p.grad_k : p.grad_q;
+      const size_t base = row * DK;
+      const float inv = 1.f / sqrtf(wave_sum(row_sumsq<DK>(y, base, l)) + kEps);
+      float ug = 0.f;
+#pragma unroll
+      for (int i = l; i < DK; i += 64) ug += bf2f(y, base + i) * inv * gn[base + i];
+      ug = wave_sum(ug);
+#pragma unroll
+      for (int i = l; i < DK; i += 64) gy[base + i] = (gn[base + i] - bf2f(y, base + i) * inv * ug) * inv;
+    }
+  }
+}
+
+// dL/da_h: the rows of head h (every H-th row), summed in a fixed order.
+__global__ __launch_bounds__(256) void gate_a_kernel(GateBwdParams p) {
+  __shared__ float part[256];
+  const int h = blockIdx.x, tid = threadIdx.x;
+  const size_t n = (size_t)p.B * p.T;   // rows of one head
+  float s = 0.f;
+  for (size_t i = tid; i < n; i += 256) s += p.ga_rows[i * p.H + h];
+  part[tid] = s;
+  __syncthreads();
+  for (int w = 128; w >= 1; w >>= 1) {
+    if (tid < w) part[tid] += part[tid + w];
+    __syncthreads();
+  }
+  if (tid == 0) p.grad_a[h] = part[0];
+}
+
+}  // namespace
+}  // namespace gate
+
+hipError_t launch_gate_prep(const GateBwdParams& p, hipStream_t s) {
+  const size_t rows = (size_t)p.B * p.T * p.H;
+  const dim3 grid((unsigned)((rows + gate::kRows - 1) / gate::kRows));
+  if (p.DK == 128) hipLaunchKernelGGL(gate::gate_prep_kernel<128>, grid, dim3(64 * gate::kRows), 0, s, p);
+  else if (p.DK == 64) hipLaunchKernelGGL(gate::gate_prep_kernel<64>, grid, dim3(64 * gate::kRows), 0, s, p);
+  else return hipErrorInvalidValue;
+  return hipGetLastError();
+}
+
+hipError_t launch_gate_chain(const GateBwdParams& p, hipStream_t s) {
+  const size_t rows = (size_t)p.B * p.T * p.H;
+  const dim3 grid((unsigned)((rows + gate::kRows - 1) / gate::kRows));
+  if (p.DK == 128) hipLaunchKernelGGL(gate::gate_chain_kernel<128>, grid, dim3(64 * gate::kRows), 0, s, p);
+  else if (p.DK == 64) hipLaunchKernelGGL(gate::gate_chain_kernel<64>, grid, dim3(64 * gate::kRows), 0, s, p);
+  else return hipErrorInvalidValue;
+  hipError_t e = hipGetLastError();
+  if (e != hipSuccess) return e;
+  hipLaunchKernelGGL(gate::gate_a_kernel, dim3(p.H), dim3(256), 0, s, p);
+  return hipGetLastError();
+}
+
+}  // namespace gdr

@@ -91,6 +91,31 @@ bool fwd_pipe_supported(const FwdParams& p);
 hipError_t launch_fwd_pipe(const FwdParams& p, hipStream_t stream);
 hipError_t launch_step(const StepParams& p, hipStream_t stream);
 hipError_t launch_bwd(const BwdParams& p, hipStream_t stream);
+
+// The gated forward's activation and normalisation around the plain backward
+// (gdr_gate_bwd.hip): rows are token-heads (b, t, h), C = DK (per-channel
+// decay) or DK / 2 (2x2 blocks) decay channels per row.
+struct GateBwdParams {
+  int B, T, H, DK, C;
+  int norm;                 // q and k normalised per token
+  const void* x;            // bf16 decay pre-activation [B,T,H,C]
+  const float* a;           // [H]
+  const void* q_raw;        // bf16 [B,T,H,DK]
+  const void* k_raw;
+  float* alpha;             // prep: exp(-a softplus(x)) [B,T,H,C]
+  void* q_n;                // prep (norm): bf16 l2-normalised q, k
+  void* k_n;
+  const float* grad_alpha;  // from the plain backward
+  const float* grad_qn;     // from the plain backward (norm)
+  const float* grad_kn;
+  float* grad_x;            // [B,T,H,C]
+  float* grad_q;            // raw-input gradients (norm)
+  float* grad_k;
+  float* ga_rows;           // per row: its contribution to dL/da_h
+  float* grad_a;            // [H]
+};
+hipError_t launch_gate_prep(const GateBwdParams& p, hipStream_t stream);
+hipError_t launch_gate_chain(const GateBwdParams& p, hipStream_t stream);
 // block length of the backward (and of the forward's checkpoints) and the
 // value-tile width of the backward kernel
 constexpr int kBwdBlock = 32;

@@ -33,6 +33,18 @@ hipError_t launch_bwd(const BwdParams& p, hipStream_t) {
   ++g_nbwd;
   return hipSuccess;
 }
+static GateBwdParams g_gate;
+static int g_ngprep = 0, g_ngchain = 0;
+hipError_t launch_gate_prep(const GateBwdParams& p, hipStream_t) {
+  g_gate = p;
+  ++g_ngprep;
+  return hipSuccess;
+}
+hipError_t launch_gate_chain(const GateBwdParams& p, hipStream_t) {
+  g_gate = p;
+  ++g_ngchain;
+  return hipSuccess;
+}
 namespace raven {
 static RavenParams g_rv;
 static int g_nrv = 0;
@@ -193,6 +205,50 @@ int main() {
     x = w; x.T = 0; CHECK(gdr_chunk_bwd(&x, nullptr) == GDR_ERR_SHAPE);
     x = w; x.B = 0x7fffffff; x.T = 0x7fffffff; CHECK(gdr_chunk_bwd(&x, nullptr) == GDR_ERR_SHAPE);
     CHECK(gdr_chunk_bwd(nullptr, nullptr) == GDR_ERR_NULL && gdr_chunk_bwd_workspace(nullptr) == 0);
+  }
+
+  // gated backward: activation and normalisation around the plain backward
+  {
+    gdr_bwd_args gb = w;
+    gb.alpha = nullptr;
+    gb.grad_alpha = nullptr;
+    gb.workspace = nullptr;
+    gb.workspace_bytes = 0;
+    gdr_gate_args ga;
+    std::memset(&ga, 0, sizeof ga);
+    ga.decay_x = fake(30); ga.decay_a = (const float*)fake(31); ga.qk_l2norm = 1;
+    gdr_gate_grads gg;
+    gg.grad_decay_x = (float*)fake(32); gg.grad_decay_a = (float*)fake(33);
+    const size_t gneed = gdr_chunk_bwd_gated_workspace(&gb, &ga);
+    // decay and its gradient 800*128*4 each, q/k normalised 800*128*2 each and
+    // their gradients 800*128*4 each, 800 row sums, then the plain backward's
+    const size_t gown = 2 * (size_t)800 * 128 * 4 + 2 * 800 * 128 * 2 + 2 * (size_t)800 * 128 * 4 + 3328;
+    CHECK(gneed == gown + need);
+    CHECK(gdr_chunk_bwd_gated(&gb, &ga, &gg, nullptr) == GDR_ERR_WORKSPACE);
+    gb.workspace = fake(20); gb.workspace_bytes = gneed - 1;
+    CHECK(gdr_chunk_bwd_gated(&gb, &ga, &gg, nullptr) == GDR_ERR_WORKSPACE);
+    gb.workspace_bytes = gneed;
+    const int nb = gdr::g_nbwd;
+    CHECK(gdr_chunk_bwd_gated(&gb, &ga, &gg, nullptr) == GDR_OK);
+    CHECK(gdr::g_ngprep == 1 && gdr::g_ngchain == 1 && gdr::g_nbwd == nb + 1);
+    CHECK(gdr::g_gate.norm == 1 && gdr::g_gate.C == 128 && gdr::g_gate.grad_q == w.grad_q);
+    CHECK(gdr::g_bwd.grad_q != w.grad_q && gdr::g_bwd.q == gdr::g_gate.q_n);
+    CHECK((const float*)gdr::g_bwd.grad_alpha == gdr::g_gate.grad_alpha && gdr::g_gate.alpha != nullptr);
+    CHECK((char*)gdr::g_gate.ga_rows + 800 * 4 <= (char*)gdr::g_bwd.ckpt);
+    CHECK((char*)gdr::g_bwd.flag + 2 * 4 * 4 * 4 <= (char*)gb.workspace + gneed);
+    gdr_bwd_args x = gb;
+    x.alpha = (const float*)fake(4); CHECK(gdr_chunk_bwd_gated(&x, &ga, &gg, nullptr) == GDR_ERR_ARG);
+    x = gb; x.grad_alpha = (float*)fake(11); CHECK(gdr_chunk_bwd_gated(&x, &ga, &gg, nullptr) == GDR_ERR_ARG);
+    CHECK(gdr_chunk_bwd_gated(&gb, &ga, nullptr, nullptr) == GDR_ERR_NULL);
+    CHECK(gdr_chunk_bwd_gated(&gb, nullptr, &gg, nullptr) == GDR_ERR_NULL);
+    gdr_gate_args gx = ga; gx.reserved = 1; CHECK(gdr_chunk_bwd_gated(&gb, &gx, &gg, nullptr) == GDR_ERR_ARG);
+    gx = ga; gx.decay_a = (const float*)((char*)fake(31) + 2);
+    CHECK(gdr_chunk_bwd_gated(&gb, &gx, &gg, nullptr) == GDR_ERR_ALIGN);
+    gx = ga; gx.qk_l2norm = 0;
+    CHECK(gdr_chunk_bwd_gated_workspace(&gb, &gx) == 2 * (size_t)800 * 128 * 4 + 3328 + need);
+    gb.workspace_bytes = gdr_chunk_bwd_gated_workspace(&gb, &gx);
+    CHECK(gdr_chunk_bwd_gated(&gb, &gx, &gg, nullptr) == GDR_OK && gdr::g_bwd.grad_q == w.grad_q);
+    CHECK(gdr_chunk_bwd_gated_workspace(nullptr, &ga) == 0);
   }
 
   // decode

@@ -35,7 +35,7 @@ def test_library_loads_and_exports_header_symbols():
     assert {"gdr_chunk_fwd", "gdr_chunk_fwd_gated", "gdr_chunk_bwd", "gdr_chunk_bwd_workspace",
             "gdr_step_decode", "gdr_chunk_fwd_workspace", "gdr_status_str",
             "gdr_abi_version", "gdr_chunk_bwd_noalloc", "gdr_raven_fwd",
-            "gdr_perm_fwd"} <= set(names)
+            "gdr_perm_fwd", "gdr_chunk_bwd_gated", "gdr_chunk_bwd_gated_workspace"} <= set(names)
     for nm in names:
         assert hasattr(lib, nm), nm
     out = subprocess.run(["nm", "-D", "--defined-only", gdr.LIB_PATH], capture_output=True,
