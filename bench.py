@@ -201,6 +201,42 @@ def _bwd_closure(wl):
     return step, x
 
 
+def _bwd_gated_closure(wl):
+    """gdr_chunk_bwd_gated on the gated forward's raw draws (bf16 decay
+    pre-activation, raw q and k normalised per token) with a seeded bf16 grad_o
+    and an fp32 grad_S; the workspace is allocated once, outside the timed
+    region."""
+    import ctypes
+    import numpy as np
+    import torch
+    import recurrent_state_memory_amd as gdr
+    from synth.gen import bf16_round, generate_gated
+    x = generate_gated(wl)
+    bf = torch.bfloat16
+    q, k, v, xx = (_to_dev(t, bf) for t in (x.q, x.k, x.v, x.x))
+    a_h, theta, beta, w = map(_to_dev, (x.a, x.theta, x.beta, x.w))
+    rng = np.random.default_rng(wl.seed + 1)
+    dO = _to_dev(bf16_round(rng.standard_normal(x.v.shape, dtype=np.float32)), bf)
+    dS = _to_dev((rng.standard_normal((wl.B, wl.H, wl.dv, wl.dk)) / 8).astype(np.float32))
+    a = gdr.BwdArgs()
+    a.B, a.T, a.H, a.dk, a.dv = wl.B, wl.T, wl.H, wl.dk, wl.dv
+    a.decay = gdr.GDR_DECAY_ROT2 if theta is not None else gdr.GDR_DECAY_DIAG
+    for f in ("q", "k", "v", "beta", "w", "grad_o", "grad_q", "grad_k", "grad_v",
+              "grad_beta", "grad_w"):
+        setattr(a, f, 1 << 20)
+    if theta is not None:
+        a.theta = a.grad_theta = 1 << 20
+    g = gdr.GateArgs()
+    g.decay_x, g.decay_a, g.qk_l2norm, g.reserved = 1 << 20, 1 << 20, 1, 0
+    need = gdr.load_library().gdr_chunk_bwd_gated_workspace(ctypes.byref(a), ctypes.byref(g))
+    ws = torch.empty(need, dtype=torch.uint8, device="cuda")
+
+    def step():
+        return gdr.gdr_chunk_bwd_gated(q, k, v, xx, a_h, w, beta, dO, theta=theta,
+                                       qk_l2norm=True, grad_S=dS, workspace=ws)
+    return step, x
+
+
 def raven_bytes(wl) -> int:
     """Bytes the Raven slot-memory forward must move at least once: q, k, v and
     the router logits (bf16), the decay rate (fp32) in; o (bf16) out; the final
@@ -448,7 +484,8 @@ def main(argv=None):
     ap.add_argument("--bwd", action="store_true",
                     help="gdr_chunk_bwd: the backward (forward recompute + reverse blocks + reduction)")
     ap.add_argument("--gated", action="store_true",
-                    help="gdr_chunk_fwd_gated: bf16 decay pre-activation, q/k normalised in the kernel")
+                    help="gdr_chunk_fwd_gated: bf16 decay pre-activation, q/k normalised in the "
+                         "kernel (with --bwd: gdr_chunk_bwd_gated)")
     a = ap.parse_args(argv)
     if a.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) != 1:
         print("bench.py measures one GPU only: the forward runs independent (b, h) units "
@@ -553,21 +590,27 @@ def main(argv=None):
             print("--bwd runs the bf16 plain-erase workloads with d in {64, 128} "
                   "(no reflection blocks)", file=sys.stderr)
             return 2
-        step, x = _bwd_closure(wl)
+        step, x = _bwd_gated_closure(wl) if a.gated else _bwd_closure(wl)
         secs, wall = _time(step, a.steps, a.warmup)
         per = secs / a.steps
         fl = bwd_flops(wl)
         out = {
-            "metric": "tokens/sec gated-delta chunk bwd (recompute + backward + reduction)",
+            "metric": ("tokens/sec gated-delta chunk bwd, gated (activation and q/k normalisation "
+                       "+ recompute + backward + reduction + chain rule)" if a.gated else
+                       "tokens/sec gated-delta chunk bwd (recompute + backward + reduction)"),
             "value": round(wl.B * wl.T / per, 1), "unit": "tokens/s", "n_gpus": 1,
             "steps": a.steps, "warmup": a.warmup, "ms_per_step": round(per * 1e3, 4),
             "higher_is_better": True, "scaling": "weak", "vs_baseline": None, "dtype": "f32",
-            "data": "synthetic (seeded; the forward's inputs, bf16 grad_o, fp32 grad_S)",
+            "data": ("synthetic (seeded; the gated forward's raw draws, bf16 grad_o, fp32 grad_S)"
+                     if a.gated else
+                     "synthetic (seeded; the forward's inputs, bf16 grad_o, fp32 grad_S)"),
             "config": {"workload": (f"{wl.name}: B={wl.B} H={wl.H} T={wl.T} d_k=d_v={wl.dk}, "
                                     f"{'2x2 rotation-decay' if wl.decay == 'rot2' else 'per-channel decay'}, "
                                     "gradients of q,k,v,decay,beta,w,S0 in fp32"),
                        "global_batch": wl.B, "seq_len": wl.T, "parallelism": "single GPU"},
-            "roofline_scope": "whole gdr_chunk_bwd call (3 kernels); per-kernel times in profiles/",
+            "roofline_scope": ("whole gdr_chunk_bwd_gated call (7 kernels); flops of the backward "
+                               "kernel only" if a.gated else
+                               "whole gdr_chunk_bwd call (4 kernels); per-kernel times in profiles/"),
             "roofline": {"bound": "mfma", "achieved": round(fl / per / 1e12, 2),
                          "peak": MFMA_F32_PEAK_TFS, "unit": "TFLOP/s",
                          "frac": round(fl / per / 1e12 / MFMA_F32_PEAK_TFS, 4), "traffic": None},
