@@ -700,6 +700,7 @@ struct TokSmem {
   float V[L * TV], DO[L * TV];
   float beta[L], w[L];
   float sub[NG][TV * DK];     // the state before tokens 0, 8, 16, 24 of the block
+  float ev[L][TV];            // per token and row: e = w v - X k, from the first forward pass
   float red[8][4][3 * DK];    // per token of a group, per wave: dq, dk, d(decay) row sums
   float redb[8][4][2];        // dbeta, dw row sums
 };
@@ -777,16 +778,25 @@ __global__ __launch_bounds__(NT) void bwd_token_kernel(BwdParams p) {
       }
     }
   };
-  // one token forward: s <- S_t from s = S_{t-1}
-  auto fwd_token = [&](float (&s)[CPL], int t) {
+  // one token forward: s <- S_t from s = S_{t-1}; the first pass over a block
+  // forms e = w v - X k with a row dot product and keeps it, the later passes
+  // (the group recomputes) read it back, so only the first has the serial
+  // cross-lane reduction
+  auto fwd_token = [&](float (&s)[CPL], int t, bool first) {
     float x[CPL], kk[CPL];
     transition(s, x, t);
     keys(kk, sm.K + t * DK + ch0);
-    float y = 0.f;
+    float ev;
+    if (first) {
+      float y = 0.f;
 #pragma unroll
-    for (int e = 0; e < CPL; ++e) y += x[e] * kk[e];
-    y = sum_row_slices(y);
-    const float cf = sm.beta[t] * (sm.w[t] * sm.V[t * TV + row] - y);
+      for (int e = 0; e < CPL; ++e) y += x[e] * kk[e];
+      ev = sm.w[t] * sm.V[t * TV + row] - sum_row_slices(y);
+      if (cs == 0) sm.ev[t][row] = ev;
+    } else {
+      ev = sm.ev[t][row];
+    }
+    const float cf = sm.beta[t] * ev;
 #pragma unroll
     for (int e = 0; e < CPL; ++e) s[e] = x[e] + cf * kk[e];
   };
@@ -858,7 +868,7 @@ __global__ __launch_bounds__(NT) void bwd_token_kernel(BwdParams p) {
           for (int e = 0; e < CPL; e += 4)
             *(f32x4*)(sm.sub[t >> 3] + row * DK + ch0 + e) = *(const f32x4*)(s + e);
         }
-        fwd_token(s, t);
+        fwd_token(s, t, true);
       }
     }
     // ------------------------------------ groups of 8 tokens, last group first
@@ -872,7 +882,7 @@ __global__ __launch_bounds__(NT) void bwd_token_kernel(BwdParams p) {
         for (int u = 0; u < 8; ++u) {
 #pragma unroll
           for (int e = 0; e < CPL; ++e) st[u][e] = s[e];
-          if (u < 7 && 8 * grp + u < nt) fwd_token(s, 8 * grp + u);
+          if (u < 7 && 8 * grp + u < nt) fwd_token(s, 8 * grp + u, false);
         }
       }
 #pragma unroll
@@ -883,12 +893,8 @@ __global__ __launch_bounds__(NT) void bwd_token_kernel(BwdParams p) {
           transition(st[u], x, t);
           keys(kk, sm.K + t * DK + ch0);
           keys(qq, sm.Q + t * DK + ch0);
-          float y = 0.f;
-#pragma unroll
-          for (int e = 0; e < CPL; ++e) y += x[e] * kk[e];
-          y = sum_row_slices(y);
           const float bt = sm.beta[t], wt = sm.w[t], vr = sm.V[t * TV + row];
-          const float ev = wt * vr - y;
+          const float ev = sm.ev[t][row];   // w v - X k
           const float dor = sm.DO[t * TV + row];
           float dq[CPL], dk[CPL], dz[CPL];
           float gk = 0.f;
