@@ -433,7 +433,7 @@ __global__ __launch_bounds__(TV / 16 * 64) void gdr_fwd_kernel(FwdParams p) {
 
     if (token_path) {
       // ---------------------------------------------------------- token path
-      token_steps<DK, DECAY, T>(
+      token_steps<DK, DECAY, false, T>(
           Sacc, (const float*)sKhKm, sKp, sQp, RSK,
           [&](int t) { return (float)sV[t * RSV + 16 * wv + n]; }, sBeta, sBW,
           min(L, Tn - c0), [&](int t, float ov) {

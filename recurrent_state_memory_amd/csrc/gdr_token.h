@@ -66,18 +66,28 @@ __device__ inline float sum_over_g(float x) {
 //   vval(t): value of row n of this wave at token t, as float
 //   beta[t], bw[t]: erase strength and beta * w
 // emit(t, o) is called on every lane with o = o_t[n] (the same on all four g).
-template <int DK, int DECAY, typename T, typename Val, typename Emit>
+//
+// FULL unrolls the loops over the accumulator tiles completely, so the tiles
+// are addressed statically (a partial unroll indexes them at run time, a mode
+// switch per access: a strong-decay forward takes 17-26 % longer that way);
+// scheduling barriers keep each tile's loads in its own iteration.  The full
+// unroll raises the register count of the whole kernel, which slowed the
+// per-channel-decay pipelined kernel's matrix-core pass by 2.5 %, so callers
+// choose it per kernel.
+template <int DK, int DECAY, bool FULL = false, typename T, typename Val, typename Emit>
 __device__ inline void token_steps(f32x4 (&Sacc)[DK / 16], const float* tr, const T* kr,
                                    const T* qr, int ldk, Val vval,
                                    const float* beta, const float* bw, int ntok, Emit emit) {
   constexpr int NCT = DK / 16;
+  constexpr int UNR = FULL ? NCT : 4;
   const int g = (threadIdx.x & 63) >> 4;
   for (int t = 0; t < ntok; ++t) {
     const float* a = tr + t * DK + 4 * g;
     const T* kp = kr + t * ldk + 4 * g;
     float part = 0.f;
-#pragma unroll 4   // a full unroll spills in the 128-VGPR launches
+#pragma unroll UNR
     for (int ct = 0; ct < NCT; ++ct) {
+      if constexpr (FULL) __builtin_amdgcn_sched_barrier(0);
       const f32x4 z = *(const f32x4*)(a + 16 * ct);
       if constexpr (DECAY == 0) {
 #pragma unroll
@@ -106,8 +116,9 @@ __device__ inline void token_steps(f32x4 (&Sacc)[DK / 16], const float* tr, cons
     const float d = bw[t] * vn - beta[t] * y;   // beta (w v - y)
     const T* qp = qr + t * ldk + 4 * g;
     float op = 0.f;
-#pragma unroll 4   // a full unroll spills in the 128-VGPR launches
+#pragma unroll UNR
     for (int ct = 0; ct < NCT; ++ct) {
+      if constexpr (FULL) __builtin_amdgcn_sched_barrier(0);
       const f32x4 k4 = load4_f32<T>(kp + 16 * ct);
       const f32x4 q4 = load4_f32<T>(qp + 16 * ct);
 #pragma unroll
