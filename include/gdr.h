@@ -250,7 +250,9 @@ gdr_status gdr_chunk_bwd_noalloc(const gdr_bwd_args *a, void *hip_stream);
  * (ROT2) goes to a->grad_theta as before.  The workspace holds the activated
  * decay, the normalised q and k, their gradients, one fp32 per token-head, and
  * the plain backward's workspace: at least gdr_chunk_bwd_gated_workspace bytes
- * (0 when the arguments are invalid).  Supported as gdr_chunk_bwd. */
+ * (0 when the arguments are invalid).  decay_x, decay_a and the gate
+ * gradients must be 4-byte aligned (GDR_ERR_ALIGN otherwise).  Supported as
+ * gdr_chunk_bwd. */
 typedef struct gdr_gate_grads {
   float *grad_decay_x;  /* as decay_x: DIAG [B,T,H,dk], ROT2 [B,T,H,dk/2] */
   float *grad_decay_a;  /* [H]                                            */

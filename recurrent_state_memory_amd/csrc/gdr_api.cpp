@@ -342,7 +342,7 @@ gdr_status check_gated_bwd(const gdr_bwd_args* a, const gdr_gate_args* g, const 
   if (g->reserved != 0) return GDR_ERR_ARG;
   if (!g->decay_x || !g->decay_a) return GDR_ERR_NULL;
   if (need_grads && (!gg || !gg->grad_decay_x || !gg->grad_decay_a)) return GDR_ERR_NULL;
-  if ((reinterpret_cast<uintptr_t>(g->decay_x) & 1u) != 0) return GDR_ERR_ALIGN;
+  if ((reinterpret_cast<uintptr_t>(g->decay_x) & 3u) != 0) return GDR_ERR_ALIGN;   // read in pairs
   if ((reinterpret_cast<uintptr_t>(g->decay_a) & 3u) != 0) return GDR_ERR_ALIGN;
   if (gg && ((reinterpret_cast<uintptr_t>(gg->grad_decay_x) & 3u) != 0 ||
              (reinterpret_cast<uintptr_t>(gg->grad_decay_a) & 3u) != 0))

@@ -47,6 +47,10 @@ __device__ inline float row_sumsq(const void* y, size_t base, int l) {
   return s;
 }
 
+// bf16 pair <-> two floats
+__device__ inline float bf_lo(uint32_t u) { return __uint_as_float(u << 16); }
+__device__ inline float bf_hi(uint32_t u) { return __uint_as_float(u & 0xffff0000u); }
+
 template <int DK>
 __global__ __launch_bounds__(64 * kRows) void gate_prep_kernel(GateBwdParams p) {
   const int l = threadIdx.x & 63;
@@ -55,9 +59,15 @@ __global__ __launch_bounds__(64 * kRows) void gate_prep_kernel(GateBwdParams p) 
   if (row >= rows) return;   // whole waves leave together
   const int h = (int)(row % p.H);
   const float a = p.a[h];
-  for (int j = l; j < p.C; j += 64) {
-    const size_t i = row * p.C + j;
-    p.alpha[i] = expf(-a * softplus(bf2f(p.x, i)));
+  if (p.C == 128) {   // two neighbouring channels per lane: 4-byte loads, 8-byte stores
+    const size_t i = row * 128 + 2 * l;
+    const uint32_t u = *(const uint32_t*)((const __bf16*)p.x + i);
+    *(float2*)(p.alpha + i) = float2{expf(-a * softplus(bf_lo(u))), expf(-a * softplus(bf_hi(u)))};
+  } else {
+    for (int j = l; j < p.C; j += 64) {
+      const size_t i = row * p.C + j;
+      p.alpha[i] = expf(-a * softplus(bf2f(p.x, i)));
+    }
   }
   if (p.norm) {
 #pragma unroll
@@ -65,9 +75,18 @@ __global__ __launch_bounds__(64 * kRows) void gate_prep_kernel(GateBwdParams p) 
       const void* y = which ? p.k_raw : p.q_raw;
       __bf16* yn = (__bf16*)(which ? p.k_n : p.q_n);
       const size_t base = row * DK;
-      const float inv = 1.f / sqrtf(wave_sum(row_sumsq<DK>(y, base, l)) + kEps);
+      if constexpr (DK == 128) {   // channels 2l, 2l + 1
+        const uint32_t u = *(const uint32_t*)((const __bf16*)y + base + 2 * l);
+        const float y0 = bf_lo(u), y1 = bf_hi(u);
+        const float inv = 1.f / sqrtf(wave_sum(y0 * y0 + y1 * y1) + kEps);
+        const __bf16 n0 = (__bf16)(y0 * inv), n1 = (__bf16)(y1 * inv);
+        *(uint32_t*)(yn + base + 2 * l) =
+            (uint32_t)__builtin_bit_cast(uint16_t, n0) | ((uint32_t)__builtin_bit_cast(uint16_t, n1) << 16);
+      } else {
+        const float inv = 1.f / sqrtf(wave_sum(row_sumsq<DK>(y, base, l)) + kEps);
 #pragma unroll
-      for (int i = l; i < DK; i += 64) yn[base + i] = (__bf16)(bf2f(y, base + i) * inv);
+        for (int i = l; i < DK; i += 64) yn[base + i] = (__bf16)(bf2f(y, base + i) * inv);
+      }
     }
   }
 }

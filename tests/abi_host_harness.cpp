@@ -244,6 +244,8 @@ int main() {
     gdr_gate_args gx = ga; gx.reserved = 1; CHECK(gdr_chunk_bwd_gated(&gb, &gx, &gg, nullptr) == GDR_ERR_ARG);
     gx = ga; gx.decay_a = (const float*)((char*)fake(31) + 2);
     CHECK(gdr_chunk_bwd_gated(&gb, &gx, &gg, nullptr) == GDR_ERR_ALIGN);
+    gx = ga; gx.decay_x = (const char*)fake(30) + 2;
+    CHECK(gdr_chunk_bwd_gated(&gb, &gx, &gg, nullptr) == GDR_ERR_ALIGN);
     gx = ga; gx.qk_l2norm = 0;
     CHECK(gdr_chunk_bwd_gated_workspace(&gb, &gx) == 2 * (size_t)800 * 128 * 4 + 3328 + need);
     gb.workspace_bytes = gdr_chunk_bwd_gated_workspace(&gb, &gx);
