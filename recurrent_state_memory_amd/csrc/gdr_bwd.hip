@@ -63,29 +63,39 @@ struct Smem {
 __device__ inline float bf2f(const __bf16* p, size_t i) { return (float)p[i]; }
 
 // acc += A B over K, 16x16 output tile at rows r0, columns c0, with
-// A(r, k) = a[r * ARS + k * ACS] and B(k, c) = b[k * BRS + c * BCS].  Row
-// strides are multiples of 4 floats and the matrices 16-byte aligned, so an
-// operand contiguous along k is read as two 16-byte pieces.  fp32 operands:
-// bf16 ones (one 16x16x32 product per step) measured 16 % faster on the layer
-// shape but raise the gradients' error from ~1e-7 to ~4e-3 where the block
-// start state is exact.
+// A(r, k) = a[r * ARS + k * ACS] and B(k, c) = b[k * BRS + c * BCS].  fp32
+// operands: bf16 ones (one 16x16x32 product per step) measured 16 % faster on
+// the layer shape but raise the gradients' error from ~1e-7 to ~4e-3 where the
+// block start state is exact.
+//
+// Operand slot s of a lane in group g (lane = 16 g + n) holds contraction index
+// k0 + 4g + (s & 3) + 16 (s >> 2); any bijection works if both operands use it.
+// This one puts the lanes of groups g and g + 1, which a 4-byte LDS read serves
+// in the same cycle, on rows 4 apart: with every row stride here 4 mod 32
+// floats that is 16 banks apart, so the strided (transposed) operand reads are
+// free of bank conflicts (rows 8 apart, as in the plain order, share banks).
+// An operand contiguous along k is read as two 16-byte pieces, at 4g and 16 + 4g.
 template <int ARS, int ACS, int BRS, int BCS, int K>
 __device__ inline void mm(f32x4& acc, const float* a, int r0, const float* b, int c0) {
+  static_assert(ACS == 1 || ACS % 32 == 4, "strided A rows must be 4 mod 32 floats apart");
+  static_assert(BRS == 1 || BRS % 32 == 4, "strided B rows must be 4 mod 32 floats apart");
   const int l = lane_id(), n = l & 15, g = l >> 4;
 #pragma unroll
   for (int k0 = 0; k0 < K; k0 += 32) {
     f32x8 fa, fb;
-    if constexpr (ACS == 1) {   // contiguous along k: two 16-byte reads
-      fa = F::load8(a + (r0 + n) * ARS + k0 + 8 * g);
+    if constexpr (ACS == 1) {
+      const float* p = a + (r0 + n) * ARS + k0 + 4 * g;
+      fa = F::join(*(const f32x4*)p, *(const f32x4*)(p + 16));
     } else {
 #pragma unroll
-      for (int s = 0; s < 8; ++s) fa[s] = a[(r0 + n) * ARS + (k0 + 8 * g + s) * ACS];
+      for (int s = 0; s < 8; ++s) fa[s] = a[(r0 + n) * ARS + (k0 + 4 * g + (s & 3) + 16 * (s >> 2)) * ACS];
     }
     if constexpr (BRS == 1) {
-      fb = F::load8(b + (c0 + n) * BCS + k0 + 8 * g);
+      const float* p = b + (c0 + n) * BCS + k0 + 4 * g;
+      fb = F::join(*(const f32x4*)p, *(const f32x4*)(p + 16));
     } else {
 #pragma unroll
-      for (int s = 0; s < 8; ++s) fb[s] = b[(k0 + 8 * g + s) * BRS + (c0 + n) * BCS];
+      for (int s = 0; s < 8; ++s) fb[s] = b[(k0 + 4 * g + (s & 3) + 16 * (s >> 2)) * BRS + (c0 + n) * BCS];
     }
     F::mma(acc, fa, fb);
   }
