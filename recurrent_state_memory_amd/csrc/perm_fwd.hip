@@ -210,7 +210,7 @@ __global__ __launch_bounds__(NT) void perm_fwd_kernel(PermParams p) {
     for (int t = 0; t < tn; ++t) {
       const int base = t * D + cg * CPL;
       // this token's keys, queries, value and gates first: none depends on the row
-      float xs[CPL], kf[CPL], qf[CPL];
+      float kf[CPL], qf[CPL];
       const int kqb = t * kq_rs<D>() + cg * (CPL + kq_pad<D>());
 #pragma unroll
       for (int e = 0; e < CPL; e += 4) {
@@ -219,25 +219,60 @@ __global__ __launch_bounds__(NT) void perm_fwd_kernel(PermParams p) {
       }
       const float vr = (float)sh.Vc[t * ROWS + RPW * w + r];
       const float bt = sh.Bc[t], wt = sh.Wc[t];
-      // column selection: the structured maps in registers (a lane's first or
-      // last channel comes from the neighbouring lane of the same row, or is
-      // the emptied channel), any other map through this row's LDS buffer
-      // (source D reads the zero)
+      // Each kind of map runs the whole token on its own: the row is read in
+      // its selected order and updated in place (a shift writes channel e
+      // from channel e -+ 1, highest first for the push), so the four paths
+      // leave the row in the same registers and need no merge moves.
+      //   y = (S D) . k;  S D + beta (w v - y) k^T;  o = S . q
+      float op;
       const int kind = (int)((kbits >> (2 * t)) & 3u);
       if (kind == kIdentity) {
+        float a4[4] = {0.f, 0.f, 0.f, 0.f};
 #pragma unroll
-        for (int e = 0; e < CPL; ++e) xs[e] = x[e];
-      } else if (kind == kDown) {
+        for (int e = 0; e < CPL; ++e) a4[e & 3] += x[e] * kf[e];
+        const float coef = bt * (wt * vr - row_sum((a4[0] + a4[1]) + (a4[2] + a4[3])));
+        float b4[4] = {0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+        for (int e = 0; e < CPL; ++e) {
+          x[e] += coef * kf[e];
+          b4[e & 3] += x[e] * qf[e];
+        }
+        op = row_sum((b4[0] + b4[1]) + (b4[2] + b4[3]));
+      } else if (kind == kDown) {   // channel e takes e - 1; channel 0 empties
+        // row_shr:1 -- lane l - 1 holds the channels just below
         const float in = __int_as_float(__builtin_amdgcn_mov_dpp(__float_as_int(x[CPL - 1]), 0x111, 0xf, 0xf, false));
-        xs[0] = cg == 0 ? 0.f : in;   // row_shr:1 -- lane l - 1 holds channels just below
+        const float x0 = cg == 0 ? 0.f : in;
+        float a4[4] = {x0 * kf[0], 0.f, 0.f, 0.f};
 #pragma unroll
-        for (int e = 1; e < CPL; ++e) xs[e] = x[e - 1];
-      } else if (kind == kUp) {
+        for (int e = 1; e < CPL; ++e) a4[e & 3] += x[e - 1] * kf[e];
+        const float coef = bt * (wt * vr - row_sum((a4[0] + a4[1]) + (a4[2] + a4[3])));
+        float b4[4] = {0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+        for (int e = CPL - 1; e >= 1; --e) {
+          x[e] = x[e - 1] + coef * kf[e];
+          b4[e & 3] += x[e] * qf[e];
+        }
+        x[0] = x0 + coef * kf[0];
+        b4[0] += x[0] * qf[0];
+        op = row_sum((b4[0] + b4[1]) + (b4[2] + b4[3]));
+      } else if (kind == kUp) {   // channel e takes e + 1; the last channel empties
+        // row_shl:1 -- lane l + 1 holds the channels just above
         const float in = __int_as_float(__builtin_amdgcn_mov_dpp(__float_as_int(x[0]), 0x101, 0xf, 0xf, false));
-        xs[CPL - 1] = cg == 7 ? 0.f : in;   // row_shl:1 -- lane l + 1 holds channels just above
+        const float xl = cg == 7 ? 0.f : in;
+        float a4[4] = {0.f, 0.f, 0.f, xl * kf[CPL - 1]};
 #pragma unroll
-        for (int e = 0; e < CPL - 1; ++e) xs[e] = x[e + 1];
-      } else {
+        for (int e = 0; e < CPL - 1; ++e) a4[e & 3] += x[e + 1] * kf[e];
+        const float coef = bt * (wt * vr - row_sum((a4[0] + a4[1]) + (a4[2] + a4[3])));
+        float b4[4] = {0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+        for (int e = 0; e < CPL - 1; ++e) {
+          x[e] = x[e + 1] + coef * kf[e];
+          b4[e & 3] += x[e] * qf[e];
+        }
+        x[CPL - 1] = xl + coef * kf[CPL - 1];
+        b4[3] += x[CPL - 1] * qf[CPL - 1];
+        op = row_sum((b4[0] + b4[1]) + (b4[2] + b4[3]));
+      } else {   // any other map: through this row's LDS buffer (source D reads the zero)
         uint32_t sw[CPL / 2];
 #pragma unroll
         for (int e = 0; e < CPL; e += 8) {
@@ -251,20 +286,19 @@ __global__ __launch_bounds__(NT) void perm_fwd_kernel(PermParams p) {
         for (int e = 0; e < CPL; e += 4)
           *(float4*)(rbuf + cg * CPL + e) = float4{x[e], x[e + 1], x[e + 2], x[e + 3]};
 #pragma unroll
-        for (int e = 0; e < CPL; ++e) xs[e] = rbuf[e & 1 ? sw[e >> 1] >> 16 : sw[e >> 1] & 0xffffu];
-      }
-      float a4[4] = {0.f, 0.f, 0.f, 0.f};
+        for (int e = 0; e < CPL; ++e) x[e] = rbuf[e & 1 ? sw[e >> 1] >> 16 : sw[e >> 1] & 0xffffu];
+        float a4[4] = {0.f, 0.f, 0.f, 0.f};
 #pragma unroll
-      for (int e = 0; e < CPL; ++e) a4[e & 3] += xs[e] * kf[e];
-      const float y = row_sum((a4[0] + a4[1]) + (a4[2] + a4[3]));
-      const float coef = bt * (wt * vr - y);   // beta (w v - X k)
-      float b4[4] = {0.f, 0.f, 0.f, 0.f};
+        for (int e = 0; e < CPL; ++e) a4[e & 3] += x[e] * kf[e];
+        const float coef = bt * (wt * vr - row_sum((a4[0] + a4[1]) + (a4[2] + a4[3])));
+        float b4[4] = {0.f, 0.f, 0.f, 0.f};
 #pragma unroll
-      for (int e = 0; e < CPL; ++e) {
-        x[e] = xs[e] + coef * kf[e];
-        b4[e & 3] += x[e] * qf[e];
+        for (int e = 0; e < CPL; ++e) {
+          x[e] += coef * kf[e];
+          b4[e & 3] += x[e] * qf[e];
+        }
+        op = row_sum((b4[0] + b4[1]) + (b4[2] + b4[3]));
       }
-      const float op = row_sum((b4[0] + b4[1]) + (b4[2] + b4[3]));
       if (cg == 0) sh.Oc[t * ROWS + RPW * w + r] = (bf)op;
     }
     __syncthreads();
