@@ -411,6 +411,32 @@ def test_bwd_binding_checks():
             gdr.gdr_chunk_bwd(**a)
 
 
+def test_bwd_gated_binding_checks():
+    """gdr_chunk_bwd_gated: good shapes pass every check (then the CPU device is
+    refused); each bad argument is named, the rotation form included."""
+    import torch
+    bf = torch.bfloat16
+    B, T, H, d = 2, 5, 3, 8
+    good = dict(q=torch.zeros(B, T, H, d, dtype=bf), k=torch.zeros(B, T, H, d, dtype=bf),
+                v=torch.zeros(B, T, H, d, dtype=bf), decay_x=torch.zeros(B, T, H, d, dtype=bf),
+                decay_a=torch.ones(H), w=torch.zeros(B, T, H), beta=torch.zeros(B, T, H),
+                grad_o=torch.zeros(B, T, H, d, dtype=bf))
+    with pytest.raises(ValueError, match="GPU"):
+        gdr.gdr_chunk_bwd_gated(**good)
+    for name, val in (("decay_x", torch.zeros(B, T, H, d)), ("decay_a", torch.ones(H + 1)),
+                      ("grad_o", torch.zeros(B, T, H, d)), ("k", torch.zeros(B, T, H, d)),
+                      ("w", torch.zeros(B, T)), ("grad_S", torch.zeros(B, H, d, 4)),
+                      ("S0", torch.zeros(B, H, d, d, dtype=bf))):
+        a = dict(good)
+        a[name] = val
+        with pytest.raises(ValueError, match=name):
+            gdr.gdr_chunk_bwd_gated(**a)
+    a = dict(good, decay_x=torch.zeros(B, T, H, d // 2, dtype=bf),
+             theta=torch.zeros(B, T, H, d))   # theta must match the pair-wise decay
+    with pytest.raises(ValueError, match="theta"):
+        gdr.gdr_chunk_bwd_gated(**a)
+
+
 def test_decode_binding_checks():
     import torch
     bf, f32 = torch.bfloat16, torch.float32
