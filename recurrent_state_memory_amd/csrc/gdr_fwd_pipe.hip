@@ -1448,8 +1448,13 @@ hipError_t launch_fwd_pipe(const FwdParams& p, hipStream_t s) {
     return rot ? pipe::launch<64, 16, 1, true>(p, s) : pipe::launch<64, 16, 0, true>(p, s);
   }
   if (p.gmode != 0) return launch_fwd_gated(p, s);
-  if (p.ckpt != nullptr) {   // the backward's forward recompute
-    if (p.DK == 128) return rot ? pipe::launch<128, 32, 1, false, 0, true>(p, s) : pipe::launch<128, 32, 0, false, 0, true>(p, s);
+  if (p.ckpt != nullptr) {   // the backward's forward recompute (tiles as in the plain launch)
+    if (p.DK == 128) {
+      if ((long)p.B * p.H * 2 >= 192) {
+        return rot ? pipe::launch<128, 64, 1, false, 0, true>(p, s) : pipe::launch<128, 64, 0, false, 0, true>(p, s);
+      }
+      return rot ? pipe::launch<128, 32, 1, false, 0, true>(p, s) : pipe::launch<128, 32, 0, false, 0, true>(p, s);
+    }
     if (p.DK == 64) return rot ? pipe::launch<64, 32, 1, false, 0, true>(p, s) : pipe::launch<64, 32, 0, false, 0, true>(p, s);
     return hipErrorInvalidValue;
   }
