@@ -59,6 +59,31 @@ __global__ __launch_bounds__(64 * kRows) void gate_prep_kernel(GateBwdParams p) 
   if (row >= rows) return;   // whole waves leave together
   const int h = (int)(row % p.H);
   const float a = p.a[h];
+  if (DK == 128 && p.C == 128) {
+    // two neighbouring channels per lane; every load is issued before the
+    // first store (stores could alias the inputs as far as the compiler
+    // knows, so loads after a store would wait for one more round trip)
+    const size_t i = row * 128 + 2 * l;
+    const uint32_t ux = *(const uint32_t*)((const __bf16*)p.x + i);
+    uint32_t uq = 0u, uk = 0u;
+    if (p.norm) {
+      uq = *(const uint32_t*)((const __bf16*)p.q_raw + i);
+      uk = *(const uint32_t*)((const __bf16*)p.k_raw + i);
+    }
+    *(float2*)(p.alpha + i) = float2{expf(-a * softplus(bf_lo(ux))), expf(-a * softplus(bf_hi(ux)))};
+    if (p.norm) {
+#pragma unroll
+      for (int which = 0; which < 2; ++which) {
+        const uint32_t u = which ? uk : uq;
+        const float y0 = bf_lo(u), y1 = bf_hi(u);
+        const float inv = 1.f / sqrtf(wave_sum(y0 * y0 + y1 * y1) + kEps);
+        const __bf16 n0 = (__bf16)(y0 * inv), n1 = (__bf16)(y1 * inv);
+        *(uint32_t*)((__bf16*)(which ? p.k_n : p.q_n) + i) =
+            (uint32_t)__builtin_bit_cast(uint16_t, n0) | ((uint32_t)__builtin_bit_cast(uint16_t, n1) << 16);
+      }
+    }
+    return;
+  }
   if (p.C == 128) {   // two neighbouring channels per lane: 4-byte loads, 8-byte stores
     const size_t i = row * 128 + 2 * l;
     const uint32_t u = *(const uint32_t*)((const __bf16*)p.x + i);
@@ -99,6 +124,39 @@ __global__ __launch_bounds__(64 * kRows) void gate_chain_kernel(GateBwdParams p)
   if (row >= rows) return;
   const int h = (int)(row % p.H);
   const float a = p.a[h];
+  if (DK == 128 && p.C == 128) {
+    // channels 2l, 2l + 1; every load issued before the first store, as in
+    // gate_prep_kernel
+    const size_t i = row * 128 + 2 * l;
+    const uint32_t ux = *(const uint32_t*)((const __bf16*)p.x + i);
+    const float2 gal = *(const float2*)(p.grad_alpha + i), al = *(const float2*)(p.alpha + i);
+    uint32_t uy[2] = {0u, 0u};
+    float2 gn[2] = {};
+    if (p.norm) {
+      uy[0] = *(const uint32_t*)((const __bf16*)p.q_raw + i);
+      uy[1] = *(const uint32_t*)((const __bf16*)p.k_raw + i);
+      gn[0] = *(const float2*)(p.grad_qn + i);
+      gn[1] = *(const float2*)(p.grad_kn + i);
+    }
+    const float x0 = bf_lo(ux), x1 = bf_hi(ux);
+    const float gd0 = gal.x * al.x, gd1 = gal.y * al.y;   // dL/d(decay) * decay
+    // grad_decay_x is only 4-byte aligned: two 4-byte stores
+    p.grad_x[i] = gd0 * (-a) * (1.f / (1.f + expf(-x0)));
+    p.grad_x[i + 1] = gd1 * (-a) * (1.f / (1.f + expf(-x1)));
+    const float ga = wave_sum(-(gd0 * softplus(x0) + gd1 * softplus(x1)));
+    if (l == 0) p.ga_rows[row] = ga;
+    if (p.norm) {
+#pragma unroll
+      for (int which = 0; which < 2; ++which) {
+        const float y0 = bf_lo(uy[which]), y1 = bf_hi(uy[which]);
+        const float inv = 1.f / sqrtf(wave_sum(y0 * y0 + y1 * y1) + kEps);
+        const float u0 = y0 * inv, u1 = y1 * inv;
+        const float ug = wave_sum(u0 * gn[which].x + u1 * gn[which].y);
+        *(float2*)((which ? p.grad_k : p.grad_q) + i) = float2{(gn[which].x - u0 * ug) * inv, (gn[which].y - u1 * ug) * inv};
+      }
+    }
+    return;
+  }
   float ga = 0.f;
   for (int j = l; j < p.C; j += 64) {
     const size_t i = row * p.C + j;
