@@ -1024,7 +1024,7 @@ __global__ __launch_bounds__(DK) void bwd_reduce_kernel(BwdParams p) {
   const int j = threadIdx.x;
   const size_t bh = (size_t)b * Tn * H + h;
   const size_t BTH = (size_t)p.B * Tn * H;
-  const int nvt = p.n_vt;
+  constexpr int nvt = DK / TV;   // value tiles (d_v = d_k here; the launcher checks it)
   const float* Pq = p.part;
   const float* Pk = Pq + (size_t)nvt * BTH * DK;
   const float* Pl = Pk + (size_t)nvt * BTH * DK;
@@ -1032,40 +1032,64 @@ __global__ __launch_bounds__(DK) void bwd_reduce_kernel(BwdParams p) {
   const float* Pw = Pb + (size_t)nvt * BTH;
   // flagged heads: the token path's partials are already the decay's gradients
   const bool direct = p.flag[unit * nvt] != 0;
+  // Rows go in groups of RG, last first; a group's loads are all issued before
+  // its stores (the outputs may alias the partials as far as the compiler
+  // knows, so a load after a store would wait for it).
+  constexpr int RG = 4;
   float acc0 = 0.f, acc1 = 0.f;
-  for (int r = nt - 1; r >= 0; --r) {
-    const size_t row = bh + (size_t)(t0 + r) * H;
-    float sq = 0.f, sk = 0.f, sl0 = 0.f, sl1 = 0.f;
-    for (int t = 0; t < nvt; ++t) {
-      const size_t o = ((size_t)t * BTH + row) * DK;
-      sq += Pq[o + j];
-      sk += Pk[o + j];
-      if (DECAY == 0) {
-        sl0 += Pl[o + j];
-      } else if (j < DK / 2) {
-        sl0 += Pl[o + j];
-        sl1 += Pl[o + DK / 2 + j];
-      }
-    }
-    p.grad_q[row * DK + j] = sq;
-    p.grad_k[row * DK + j] = sk;
-    if (DECAY == 0) {
-      acc0 += sl0;
-      p.grad_alpha[row * DK + j] = direct ? sl0 : acc0 / p.alpha[row * DK + j];
-    } else if (j < DK / 2) {
-      acc0 += sl0;
-      acc1 += sl1;
-      p.grad_alpha[row * (DK / 2) + j] = direct ? sl0 : acc0 / p.alpha[row * (DK / 2) + j];
-      p.grad_theta[row * (DK / 2) + j] = direct ? sl1 : acc1;
-    }
-    if (j == 0) {
-      float sb = 0.f, sw = 0.f;
+  for (int r0 = nt - 1; r0 >= 0; r0 -= RG) {
+    float sq[RG], sk[RG], sl0[RG], sl1[RG], al[RG], sb[RG], sw[RG];
+#pragma unroll
+    for (int u = 0; u < RG; ++u) {
+      sq[u] = sk[u] = sl0[u] = sl1[u] = sb[u] = sw[u] = 0.f;
+      al[u] = 1.f;
+      const int r = r0 - u;
+      if (r < 0) continue;
+      const size_t row = bh + (size_t)(t0 + r) * H;
+#pragma unroll
       for (int t = 0; t < nvt; ++t) {
-        sb += Pb[(size_t)t * BTH + row];
-        sw += Pw[(size_t)t * BTH + row];
+        const size_t o = ((size_t)t * BTH + row) * DK;
+        sq[u] += Pq[o + j];
+        sk[u] += Pk[o + j];
+        if (DECAY == 0) {
+          sl0[u] += Pl[o + j];
+        } else if (j < DK / 2) {
+          sl0[u] += Pl[o + j];
+          sl1[u] += Pl[o + DK / 2 + j];
+        }
       }
-      p.grad_beta[row] = sb;
-      p.grad_w[row] = sw;
+      if (!direct) {
+        if (DECAY == 0) al[u] = p.alpha[row * DK + j];
+        else if (j < DK / 2) al[u] = p.alpha[row * (DK / 2) + j];
+      }
+      if (j == 0) {
+#pragma unroll
+        for (int t = 0; t < nvt; ++t) {
+          sb[u] += Pb[(size_t)t * BTH + row];
+          sw[u] += Pw[(size_t)t * BTH + row];
+        }
+      }
+    }
+#pragma unroll
+    for (int u = 0; u < RG; ++u) {
+      const int r = r0 - u;
+      if (r < 0) continue;
+      const size_t row = bh + (size_t)(t0 + r) * H;
+      p.grad_q[row * DK + j] = sq[u];
+      p.grad_k[row * DK + j] = sk[u];
+      if (DECAY == 0) {
+        acc0 += sl0[u];
+        p.grad_alpha[row * DK + j] = direct ? sl0[u] : acc0 / al[u];
+      } else if (j < DK / 2) {
+        acc0 += sl0[u];
+        acc1 += sl1[u];
+        p.grad_alpha[row * (DK / 2) + j] = direct ? sl0[u] : acc0 / al[u];
+        p.grad_theta[row * (DK / 2) + j] = direct ? sl1[u] : acc1;
+      }
+      if (j == 0) {
+        p.grad_beta[row] = sb[u];
+        p.grad_w[row] = sw[u];
+      }
     }
   }
 }
